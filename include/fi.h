@@ -1,0 +1,198 @@
+/*
+ * fi.h -- C-ABI of the MI355X exact autoregressive long-convolution library.
+ *
+ * What it computes.  Flash Inference (arXiv 2410.12982), summary page,
+ * "Aufgabendefinition" and "LCSM-spezifische Definition": for every layer l,
+ * batch row b and channel c, the mixer output at position n (1-based) is
+ *
+ *     y^l_n[b,c] = sum_{s=1..n} h^l[c][n-s] * x^l_s[b,c]
+ *
+ * where x^l_s is the layer's input at position s, which only becomes known
+ * after position s-1 has been produced ("unlock y_{i+1}" in Algorithm 1).
+ * The filters h^l are data independent and known ahead.
+ *
+ * How.  "Kachelung-Strategie (Algorithmus 1)" and "Schicht-uebergreifende
+ * Parallelisierung (Algorithmus 3)": after position n the library adds the
+ * contribution of inputs [n-U+1, n] to outputs [n+1, n+U], U = largest power
+ * of two dividing n ("gray block"), for all layers in one batched launch; the
+ * own-position term h^l[c][0] * x^l_n ("red cell") is added when position n is
+ * produced.  A gray block is computed either directly or through an FFT of
+ * length 2U against a cached filter spectrum ("Technische Innovationen",
+ * "FFT-Vorberechnung" and "Zirkulaere Faltungs-Trick"), chosen per block size
+ * ("Hybrid" in "Vergleichsmethoden"; selection by profiling per shape and
+ * block size, rebuttal page).
+ *
+ * Conventions shared by every call.
+ *  - Positions are 1-based; the context starts at position 0 (nothing
+ *    produced).  L, the maximum number of positions, must be a power of two
+ *    (so no gray block runs past L).
+ *  - All device buffers are caller-owned plain device pointers (for example
+ *    torch tensors' data pointers), fp32, row-major, densely packed.
+ *  - All calls are ordered on the stream bound at fi_init and return without
+ *    waiting for the device unless stated; outputs are valid once that stream
+ *    has been synchronised.
+ *  - Any HIP error poisons the context: that call and every later call except
+ *    fi_destroy/fi_last_error/fi_position return FI_ESTATE (the failing call
+ *    itself returns FI_EDEVICE).  fi_last_error() describes the first failure.
+ *  - A context is not thread safe; use one context per stream.
+ */
+#ifndef FI_H
+#define FI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fi_ctx fi_ctx; /* opaque, owned by the library */
+
+typedef enum fi_status {
+    FI_OK = 0,
+    FI_EINVAL = -1,  /* bad argument (shape, null pointer, L not a power of two) */
+    FI_ENOMEM = -2,  /* device memory could not be allocated / workspace too small */
+    FI_EDEVICE = -3, /* a HIP call failed (the context is now poisoned) */
+    FI_ERANGE = -4,  /* stepping past position L */
+    FI_ESTATE = -5   /* context poisoned, or call not valid in the current mode */
+} fi_status;
+
+/* Map between layers: x^{l+1}_n = map(y^l_n).  Feedback: x^0_{n+1} = fb(y^{M-1}_n).
+ * (The pages' synthetic model puts a block after each mixer and a sampler at
+ * the end, "LCSM-Inferenz-Algorithmus"; the elementwise tanh stands in for both.)
+ * FI_MAP_EXTERNAL: the caller runs its own block between layers with
+ * fi_layer_red() / fi_tiles(). */
+enum { FI_MAP_TANH = 0, FI_MAP_IDENTITY = 1, FI_MAP_EXTERNAL = 2 };
+enum { FI_FEEDBACK_TANH = 0, FI_FEEDBACK_IDENTITY = 1 };
+
+/* How gray blocks are computed. AUTO: per block size, the faster path as timed
+ * on the device at fi_init; DIRECT/FFT force one path where it exists (direct
+ * blocks exist for U <= 128, FFT blocks for U >= 4). */
+enum { FI_TAU_AUTO = 0, FI_TAU_DIRECT = 1, FI_TAU_FFT = 2 };
+enum { FI_PATH_NONE = 0, FI_PATH_DIRECT = 1, FI_PATH_FFT = 2 };
+
+typedef struct fi_options {
+    int map;               /* FI_MAP_*; default FI_MAP_TANH */
+    int feedback;          /* FI_FEEDBACK_*; default FI_FEEDBACK_TANH */
+    int tau_mode;          /* FI_TAU_*; default FI_TAU_AUTO */
+    int tau_split;         /* -1: per-class choice (AUTO calibrates); q >= 0: classes
+                              with U = 2^q' >= 2^q use FFT, smaller ones DIRECT */
+    int record;            /* 1: keep every layer's mixer output y^l_n (tests) */
+    int use_graphs;        /* 1 (default): fi_generate replays captured hipGraphs */
+    int block_graph_log2;  /* k: a block graph replays the 2^k - 1 positions between
+                              multiples of 2^k (default 6; 0 disables) */
+    int filters_on_device; /* 1: the filters pointer given to fi_init is device memory */
+    int reserved[8];       /* must be zero */
+} fi_options;
+
+/* Fill *opt with the defaults listed above. */
+void fi_default_options(fi_options *opt);
+
+/* Library version string, e.g. "fi 0.1 gfx950". */
+const char *fi_version(void);
+
+/* Device bytes fi_init needs for this shape and options (0 on bad arguments).
+ * The workspace holds the filters, the per-layer activation rows (inputs for
+ * positions <= n, pending sums for positions > n: the pages' activation reuse,
+ * "Speicheroptimierung"), the cached filter spectra and scratch. */
+size_t fi_workspace_bytes(int layers, int batch, int channels, int64_t L,
+                          const fi_options *opt);
+
+/* Create a context.
+ *   layers M >= 1, batch B >= 1, channels D >= 1, L = 2^P with 1 <= L <= 2^24.
+ *   filters: fp32 [M][D][L] (layer-major, channel rows of L taps h[0..L-1]),
+ *            host memory unless opt->filters_on_device; copied, the caller keeps
+ *            ownership and may free it when fi_init returns.
+ *   opt:     NULL for defaults.
+ *   workspace: device buffer of at least fi_workspace_bytes() bytes, 256-byte
+ *            aligned, owned by the caller and untouched by it while the context
+ *            lives; or NULL to let the library allocate (and free) its own.
+ *   stream:  hipStream_t the context runs on (NULL = default stream).
+ * Computes the filter spectra and, for FI_TAU_AUTO, times both block paths
+ * per block size on the device; synchronises the stream before returning.
+ * Returns FI_EINVAL / FI_ENOMEM / FI_EDEVICE on failure (*out is then NULL). */
+fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L,
+                  const float *filters, const fi_options *opt, void *workspace,
+                  void *stream);
+
+/* Release the context (and its own allocations).  Safe on NULL. */
+fi_status fi_destroy(fi_ctx *ctx);
+
+/* Back to position 0 with all activations cleared; filters, spectra and the
+ * block-path table are kept. */
+fi_status fi_reset(fi_ctx *ctx);
+
+/* Produce the next position n = fi_position()+1 (Algorithm 2 for one i).
+ *   x_t: device fp32 [B][D], the layer-0 input x^0_n; NULL = feedback
+ *        (x^0_n = fb(y^{M-1}_{n-1}); at n = 1 the value given by fi_set_input).
+ *   y_t: device fp32 [B][D] receiving the last layer's mixer output
+ *        y^{M-1}_n (before the map), or NULL.
+ * Runs the red cells of all layers in order, then the gray blocks of all
+ * layers after n.  FI_ERANGE when the position is already L.
+ * Not valid in FI_MAP_EXTERNAL mode (FI_ESTATE). */
+fi_status fi_step(fi_ctx *ctx, const float *x_t, float *y_t);
+
+/* Set the layer-0 input used by the next feedback step when no previous
+ * output exists (position 0), device fp32 [B][D]. */
+fi_status fi_set_input(fi_ctx *ctx, const float *x0);
+
+/* Teacher-forced prompt: equivalent to P calls fi_step(x + (i-1)*B*D, y ...)
+ * for i = 1..P (the invariant the tests check).
+ *   x: device fp32 [P][B][D]; y: device fp32 [P][B][D] or NULL.
+ * The prompt's positions are processed in place (position advances by P). */
+fi_status fi_prefill(fi_ctx *ctx, const float *x, int64_t P, float *y);
+
+/* Free-running generation of `steps` positions with internal feedback, with
+ * one hipGraph per block-size class plus block graphs (use_graphs = 1).
+ *   y: device fp32 [steps][B][D] receiving y^{M-1}_n for each position, or NULL.
+ * FI_ERANGE if position + steps > L (nothing is run). */
+fi_status fi_generate(fi_ctx *ctx, int64_t steps, float *y);
+
+/* Positions produced so far (0..L). */
+int64_t fi_position(const fi_ctx *ctx);
+
+/* Human-readable description of the first failure, or "" . */
+const char *fi_last_error(const fi_ctx *ctx);
+
+/* Schedule of step n (1 <= n <= L): *q = log2 of the gray-block edge after n
+ * (or -1 for n = L, which has no gray block); *path = FI_PATH_* used for it. */
+fi_status fi_debug_schedule(const fi_ctx *ctx, int64_t n, int *q, int *path);
+
+/* Block-path table: for q = 0..P-1 writes path[q] (FI_PATH_*) and, when
+ * calibration ran, the measured microseconds per launch of the direct and FFT
+ * paths (negative where a path does not exist or was not timed).  Arrays hold
+ * at least P entries; any pointer may be NULL. */
+fi_status fi_tau_table(const fi_ctx *ctx, int *path, double *us_direct, double *us_fft);
+
+/* Copy positions 1..count of one layer's rows into dst (device fp32,
+ * [B][D][count]):  what = 0: the layer inputs x^l_s (valid for s <= position);
+ * what = 1: the mixer outputs y^l_s (needs record = 1). */
+fi_status fi_history(const fi_ctx *ctx, int layer, int what, int64_t count, float *dst);
+
+/* Device wall-clock stamps (100 MHz counter ticks) written when each position
+ * finished: dst (host int64 [count]) receives the stamps of positions
+ * first..first+count-1.  Synchronises the stream. */
+fi_status fi_stamps(fi_ctx *ctx, int64_t first, int64_t count, int64_t *dst);
+
+/* External-block mode (FI_MAP_EXTERNAL).  For the current position
+ * n = fi_position()+1 the caller, for l = 0..M-1 in order, supplies the
+ * layer's mixer input q (device [B][D]) and receives its mixer output
+ *     y^l_n = (pending sum at n) + h^l[c][0] * q
+ * (the red cell of Algorithm 2), then calls fi_tiles() to run all layers'
+ * gray blocks after n and advance to n.  y may alias nothing else. */
+fi_status fi_layer_red(fi_ctx *ctx, int layer, const float *q, float *y);
+fi_status fi_tiles(fi_ctx *ctx);
+
+/* GPU Lazy baseline ("Vergleichsmethoden", Lazy: each position computes its
+ * full sum on demand, O(n) per position, all layers' sums in parallel):
+ * same semantics as fi_step / fi_generate (internal feedback) on a context
+ * that has not run any tiled step since fi_init/fi_reset (FI_ESTATE
+ * otherwise; likewise tiled calls after Lazy calls until fi_reset). */
+fi_status fi_lazy_step(fi_ctx *ctx, const float *x_t, float *y_t);
+fi_status fi_lazy_generate(fi_ctx *ctx, int64_t steps, float *y);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FI_H */

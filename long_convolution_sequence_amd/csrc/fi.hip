@@ -1,0 +1,712 @@
+// Host side of the library: context, workspace layout, the relaxed schedule,
+// per-block-size path table (device-timed), graph capture and the C-ABI.
+//
+// Flash Inference (arXiv 2410.12982), summary page, "Kachelung-Strategie",
+// "LCSM-Inferenz-Algorithmus", "Schicht-uebergreifende Parallelisierung",
+// "Implementierungsdetails" (graphs per token, filter DFT precomputation,
+// per-size preconfiguration) and the rebuttal page (per-shape, per-size
+// selection of the fastest block implementation by profiling).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/fi.h"
+#include "fi_kernels.h"
+
+using namespace fi;
+
+namespace {
+
+constexpr int kMaxDirectLog = 7;   // direct gray blocks exist for U <= 128
+constexpr int kMinFftLog = 2;      // FFT gray blocks exist for U >= 4
+constexpr int kMaxLdsFftLog = 14;  // largest transform held in one workgroup's LDS
+constexpr int kMaxLayers = 64;
+constexpr int kMaxP = 24;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int ilog2_exact(int64_t L) {
+    if (L < 1 || (L & (L - 1)) != 0) return -1;
+    int p = 0;
+    while ((int64_t(1) << p) < L) ++p;
+    return p;
+}
+
+int ctz64(int64_t n) {
+    int q = 0;
+    while (((n >> q) & 1) == 0) ++q;
+    return q;
+}
+
+struct Layout {
+    size_t filt = 0, buf = 0, rec = 0, twid = 0, xin = 0, ylast = 0, stamps = 0, state = 0;
+    size_t spec[kMaxP] = {0};
+    size_t total = 0;
+    int logNT = 0;
+};
+
+bool fft_exists(int q, int P) { return q >= kMinFftLog && q <= kMaxLdsFftLog && q <= P - 1; }
+bool direct_exists(int q) { return q <= kMaxDirectLog; }
+
+bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &lay) {
+    const int P = ilog2_exact(L);
+    if (M < 1 || M > kMaxLayers || B < 1 || D < 1 || P < 0 || P > kMaxP) return false;
+    if ((int64_t)B * D > (int64_t(1) << 24)) return false;
+    // every block size must have a path: above the direct range only FFT blocks exist
+    if (P - 1 > kMaxLdsFftLog) return false;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o2 = off;
+        off = align_up(off + bytes, 256);
+        return o2;
+    };
+    const size_t rowsMD = (size_t)M * D, rowsMBD = (size_t)M * B * D;
+    lay.filt = take(rowsMD * L * sizeof(float));
+    lay.buf = take(rowsMBD * L * sizeof(float));
+    lay.rec = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
+    for (int q = 0; q < P; ++q) {
+        lay.spec[q] = fft_exists(q, P) ? take(rowsMD * (size_t(1) << q) * 8) : 0;  // U/2 float4
+    }
+    const int nmax_log = std::min(P - 1, kMaxLdsFftLog);
+    lay.logNT = std::max(2, nmax_log + 1);
+    lay.twid = take((size_t(1) << lay.logNT) * sizeof(float2));
+    lay.xin = take((size_t)2 * B * D * sizeof(float));
+    lay.ylast = take((size_t)L * B * D * sizeof(float));
+    lay.stamps = take((size_t)(L + 1) * sizeof(long long));
+    lay.state = take(sizeof(State));
+    lay.total = off;
+    return true;
+}
+
+}  // namespace
+
+struct fi_ctx {
+    int M = 0, B = 0, D = 0, P = 0;
+    int64_t L = 0;
+    fi_options opt{};
+    hipStream_t stream = nullptr;
+    hipStream_t cap = nullptr;  // private stream used only for graph capture
+    bool own_ws = false;
+    char *ws = nullptr;
+    Layout lay;
+    Dev dev{};
+    float4 *spec[kMaxP] = {nullptr};
+    int path[kMaxP] = {0};
+    double us_direct[kMaxP], us_fft[kMaxP];
+    int64_t pos = 0;
+    int mode = 0;  // 0 fresh, 1 tiled, 2 lazy
+    bool poisoned = false;
+    std::string err;
+    hipGraphExec_t gclass[kMaxP + 1] = {nullptr};
+    hipGraphExec_t gblock = nullptr;
+    int block_log = 0;
+};
+
+namespace {
+
+fi_status fail(fi_ctx *c, fi_status s, const std::string &msg) {
+    if (c && c->err.empty()) c->err = msg;
+    if (c && s == FI_EDEVICE) c->poisoned = true;
+    return s;
+}
+
+#define HIPCK(ctx, call)                                                                     \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail((ctx), FI_EDEVICE,                                                   \
+                        std::string(#call) + ": " + hipGetErrorString(e_));                  \
+    } while (0)
+
+// ---- kernel dispatch over compile-time block sizes -------------------------
+
+int direct_ch(int M, int U) { return std::max(1, 256 / (M * U)); }
+size_t direct_lds(int M, int CH, int U) { return (size_t)M * CH * (4 * U + 1) * sizeof(float); }
+
+template <int U, bool CHAIN>
+hipError_t launch_direct_u(fi_ctx *c, hipStream_t s, const float *xext, float *yext, int advance) {
+    const int CH = direct_ch(c->M, U);
+    const int grid = (c->B * c->D + CH - 1) / CH;
+    hipLaunchKernelGGL((k_step_direct<U, CHAIN>), dim3(grid), dim3(256), direct_lds(c->M, CH, U), s,
+                       c->dev, CH, xext, yext, advance);
+    return hipGetLastError();
+}
+
+template <int U, bool CHAIN>
+hipError_t allow_direct_lds_u(fi_ctx *c) {
+    const size_t bytes = direct_lds(c->M, direct_ch(c->M, U), U);
+    return hipFuncSetAttribute((const void *)k_step_direct<U, CHAIN>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <bool CHAIN>
+hipError_t allow_direct_lds(fi_ctx *c) {
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = allow_direct_lds_u<1, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<2, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<4, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<8, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<16, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<32, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<64, CHAIN>(c);
+    if (e == hipSuccess) e = allow_direct_lds_u<128, CHAIN>(c);
+    return e;
+}
+
+template <bool CHAIN>
+hipError_t launch_direct(fi_ctx *c, int q, hipStream_t s, const float *xext, float *yext, int advance) {
+    switch (q) {
+        case 0: return launch_direct_u<1, CHAIN>(c, s, xext, yext, advance);
+        case 1: return launch_direct_u<2, CHAIN>(c, s, xext, yext, advance);
+        case 2: return launch_direct_u<4, CHAIN>(c, s, xext, yext, advance);
+        case 3: return launch_direct_u<8, CHAIN>(c, s, xext, yext, advance);
+        case 4: return launch_direct_u<16, CHAIN>(c, s, xext, yext, advance);
+        case 5: return launch_direct_u<32, CHAIN>(c, s, xext, yext, advance);
+        case 6: return launch_direct_u<64, CHAIN>(c, s, xext, yext, advance);
+        case 7: return launch_direct_u<128, CHAIN>(c, s, xext, yext, advance);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int LOGN>
+hipError_t launch_fft_n(fi_ctx *c, hipStream_t s, int advance) {
+    using S = FftShape<LOGN>;
+    const long long tiles = (long long)c->M * c->B * c->D;
+    const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
+    hipLaunchKernelGGL((k_fft_tile<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev,
+                       (const float4 *)c->spec[LOGN], advance);
+    return hipGetLastError();
+}
+
+template <int LOGN>
+hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s) {
+    using S = FftShape<LOGN>;
+    const long long rows = (long long)c->M * c->D;
+    const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
+    hipLaunchKernelGGL((k_spectrum<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev,
+                       c->spec[LOGN], 0LL);
+    return hipGetLastError();
+}
+
+hipError_t launch_fft(fi_ctx *c, int q, hipStream_t s, int advance) {
+    switch (q) {
+        case 2: return launch_fft_n<2>(c, s, advance);
+        case 3: return launch_fft_n<3>(c, s, advance);
+        case 4: return launch_fft_n<4>(c, s, advance);
+        case 5: return launch_fft_n<5>(c, s, advance);
+        case 6: return launch_fft_n<6>(c, s, advance);
+        case 7: return launch_fft_n<7>(c, s, advance);
+        case 8: return launch_fft_n<8>(c, s, advance);
+        case 9: return launch_fft_n<9>(c, s, advance);
+        case 10: return launch_fft_n<10>(c, s, advance);
+        case 11: return launch_fft_n<11>(c, s, advance);
+        case 12: return launch_fft_n<12>(c, s, advance);
+        case 13: return launch_fft_n<13>(c, s, advance);
+        case 14: return launch_fft_n<14>(c, s, advance);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
+    switch (q) {
+        case 2: return launch_spectrum_n<2>(c, s);
+        case 3: return launch_spectrum_n<3>(c, s);
+        case 4: return launch_spectrum_n<4>(c, s);
+        case 5: return launch_spectrum_n<5>(c, s);
+        case 6: return launch_spectrum_n<6>(c, s);
+        case 7: return launch_spectrum_n<7>(c, s);
+        case 8: return launch_spectrum_n<8>(c, s);
+        case 9: return launch_spectrum_n<9>(c, s);
+        case 10: return launch_spectrum_n<10>(c, s);
+        case 11: return launch_spectrum_n<11>(c, s);
+        case 12: return launch_spectrum_n<12>(c, s);
+        case 13: return launch_spectrum_n<13>(c, s);
+        case 14: return launch_spectrum_n<14>(c, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_red(fi_ctx *c, hipStream_t s, const float *xext, float *yext, int advance) {
+    const int n = c->B * c->D;
+    hipLaunchKernelGGL(k_red, dim3((n + 255) / 256), dim3(256), 0, s, c->dev, xext, yext, advance);
+    return hipGetLastError();
+}
+
+// All kernels of one position of class q (q == P: the last position, red cells only).
+hipError_t launch_position(fi_ctx *c, int q, hipStream_t s, const float *xext, float *yext, int advance) {
+    if (q >= c->P) return launch_red(c, s, xext, yext, advance);
+    if (c->path[q] == FI_PATH_DIRECT) return launch_direct<true>(c, q, s, xext, yext, advance);
+    hipError_t e = launch_red(c, s, xext, yext, 0);
+    if (e != hipSuccess) return e;
+    return launch_fft(c, q, s, advance);
+}
+
+// Gray blocks only (external-block mode): the layer inputs at n are in place.
+hipError_t launch_tiles(fi_ctx *c, int q, hipStream_t s) {
+    if (q >= c->P) {
+        hipLaunchKernelGGL(k_finish, dim3(1), dim3(64), 0, s, c->dev);
+        return hipGetLastError();
+    }
+    if (c->path[q] == FI_PATH_DIRECT) return launch_direct<false>(c, q, s, nullptr, nullptr, 1);
+    return launch_fft(c, q, s, 1);
+}
+
+int class_of(const fi_ctx *c, int64_t n) { return n < c->L ? ctz64(n) : c->P; }
+
+fi_status check_usable(fi_ctx *c) {
+    if (!c) return FI_EINVAL;
+    if (c->poisoned) return FI_ESTATE;
+    return FI_OK;
+}
+
+fi_status set_state_pos(fi_ctx *c, int64_t pos) {
+    State st{};
+    st.pos = pos;
+    HIPCK(c, hipMemcpyAsync(c->dev.st, &st, sizeof(State), hipMemcpyHostToDevice, c->stream));
+    HIPCK(c, hipStreamSynchronize(c->stream));
+    return FI_OK;
+}
+
+fi_status clear_state(fi_ctx *c) {
+    const size_t rowsMBD = (size_t)c->M * c->B * c->D;
+    HIPCK(c, hipMemsetAsync(c->dev.buf, 0, rowsMBD * c->L * sizeof(float), c->stream));
+    if (c->dev.rec) HIPCK(c, hipMemsetAsync(c->dev.rec, 0, rowsMBD * c->L * sizeof(float), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.xin, 0, 2 * (size_t)c->B * c->D * sizeof(float), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.ylast, 0, (size_t)c->L * c->B * c->D * sizeof(float), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.stamps, 0, (size_t)(c->L + 1) * sizeof(long long), c->stream));
+    fi_status s = set_state_pos(c, 0);
+    if (s != FI_OK) return s;
+    c->pos = 0;
+    c->mode = 0;
+    return FI_OK;
+}
+
+// Time both gray-block paths of class q at the real shape, n = 2^q, without
+// publishing positions.  Protocol: 2 warm-up launches, then the mean of 4
+// batches of 8 launches (the pages use 2 warm-ups and the mean of 4 runs).
+fi_status time_class(fi_ctx *c, int q, double &us_direct, double &us_fft) {
+    us_direct = us_fft = -1.0;
+    fi_status st = set_state_pos(c, (int64_t(1) << q) - 1);
+    if (st != FI_OK) return st;
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    for (int which = 0; which < 2; ++which) {
+        const bool direct = which == 0;
+        if (direct && !direct_exists(q)) continue;
+        if (!direct && !fft_exists(q, c->P)) continue;
+        auto run = [&]() -> hipError_t {
+            if (direct) return launch_direct<true>(c, q, c->stream, nullptr, nullptr, 0);
+            hipError_t e = launch_red(c, c->stream, nullptr, nullptr, 0);
+            return e != hipSuccess ? e : launch_fft(c, q, c->stream, 0);
+        };
+        for (int w = 0; w < 2; ++w) HIPCK(c, run());
+        double total = 0.0;
+        for (int rep = 0; rep < 4; ++rep) {
+            HIPCK(c, hipEventRecord(a, c->stream));
+            for (int k = 0; k < 8; ++k) HIPCK(c, run());
+            HIPCK(c, hipEventRecord(b, c->stream));
+            HIPCK(c, hipEventSynchronize(b));
+            float ms = 0.f;
+            HIPCK(c, hipEventElapsedTime(&ms, a, b));
+            total += ms * 1000.0 / 8.0;
+        }
+        (direct ? us_direct : us_fft) = total / 4.0;
+    }
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    return FI_OK;
+}
+
+fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<int> &classes) {
+    hipGraph_t g = nullptr;
+    HIPCK(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal));
+    hipError_t err = hipSuccess;
+    for (int q : classes) {
+        err = launch_position(c, q, c->cap, nullptr, nullptr, 1);
+        if (err != hipSuccess) break;
+    }
+    hipError_t e2 = hipStreamEndCapture(c->cap, &g);
+    if (err != hipSuccess) return fail(c, FI_EDEVICE, std::string("capture: ") + hipGetErrorString(err));
+    if (e2 != hipSuccess) return fail(c, FI_EDEVICE, std::string("end capture: ") + hipGetErrorString(e2));
+    hipError_t e3 = hipGraphInstantiate(out, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e3 != hipSuccess) return fail(c, FI_EDEVICE, std::string("instantiate: ") + hipGetErrorString(e3));
+    return FI_OK;
+}
+
+fi_status build_graphs(fi_ctx *c) {
+    for (int q = 0; q <= c->P; ++q) {
+        fi_status s = capture(c, &c->gclass[q], {q});
+        if (s != FI_OK) return s;
+    }
+    const int k = c->opt.block_graph_log2;
+    if (k >= 1 && k < c->P) {
+        std::vector<int> cls;
+        for (int64_t j = 1; j < (int64_t(1) << k); ++j) cls.push_back(ctz64(j));
+        fi_status s = capture(c, &c->gblock, cls);
+        if (s != FI_OK) return s;
+        c->block_log = k;
+    }
+    return FI_OK;
+}
+
+void destroy_graphs(fi_ctx *c) {
+    for (auto &g : c->gclass)
+        if (g) {
+            (void)hipGraphExecDestroy(g);
+            g = nullptr;
+        }
+    if (c->gblock) (void)hipGraphExecDestroy(c->gblock);
+    c->gblock = nullptr;
+}
+
+fi_status enter_mode(fi_ctx *c, int mode) {
+    if (c->mode != 0 && c->mode != mode)
+        return fail(c, FI_ESTATE, "tiled and Lazy calls cannot be mixed without fi_reset");
+    c->mode = mode;
+    return FI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void fi_default_options(fi_options *o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->map = FI_MAP_TANH;
+    o->feedback = FI_FEEDBACK_TANH;
+    o->tau_mode = FI_TAU_AUTO;
+    o->tau_split = -1;
+    o->record = 0;
+    o->use_graphs = 1;
+    o->block_graph_log2 = 6;
+    o->filters_on_device = 0;
+}
+
+const char *fi_version(void) { return "fi 0.1 gfx950"; }
+
+size_t fi_workspace_bytes(int layers, int batch, int channels, int64_t L, const fi_options *opt) {
+    fi_options o;
+    if (opt)
+        o = *opt;
+    else
+        fi_default_options(&o);
+    Layout lay;
+    if (!make_layout(layers, batch, channels, L, o, lay)) return 0;
+    return lay.total;
+}
+
+fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, const float *filters,
+                  const fi_options *opt, void *workspace, void *stream) {
+    if (!out) return FI_EINVAL;
+    *out = nullptr;
+    if (!filters) return FI_EINVAL;
+    fi_options o;
+    if (opt)
+        o = *opt;
+    else
+        fi_default_options(&o);
+    if (o.map < FI_MAP_TANH || o.map > FI_MAP_EXTERNAL) return FI_EINVAL;
+    if (o.feedback < FI_FEEDBACK_TANH || o.feedback > FI_FEEDBACK_IDENTITY) return FI_EINVAL;
+    if (o.tau_mode < FI_TAU_AUTO || o.tau_mode > FI_TAU_FFT) return FI_EINVAL;
+    if ((uintptr_t)workspace % 256 != 0) return FI_EINVAL;
+    Layout lay;
+    if (!make_layout(layers, batch, channels, L, o, lay)) return FI_EINVAL;
+
+    fi_ctx *c = new fi_ctx();
+    c->M = layers;
+    c->B = batch;
+    c->D = channels;
+    c->L = L;
+    c->P = ilog2_exact(L);
+    c->opt = o;
+    c->lay = lay;
+    c->stream = (hipStream_t)stream;
+    for (int q = 0; q < kMaxP; ++q) c->us_direct[q] = c->us_fft[q] = -1.0;
+
+    auto bail = [&](fi_status s) {
+        fi_destroy(c);
+        return s;
+    };
+    if (workspace) {
+        c->ws = (char *)workspace;
+    } else {
+        if (hipMalloc((void **)&c->ws, lay.total) != hipSuccess) {
+            (void)hipGetLastError();
+            c->ws = nullptr;
+            return bail(FI_ENOMEM);
+        }
+        c->own_ws = true;
+    }
+    if (hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess) return bail(FI_EDEVICE);
+
+    Dev &d = c->dev;
+    d.filt = (const float *)(c->ws + lay.filt);
+    d.buf = (float *)(c->ws + lay.buf);
+    d.rec = o.record ? (float *)(c->ws + lay.rec) : nullptr;
+    d.xin = (float *)(c->ws + lay.xin);
+    d.ylast = (float *)(c->ws + lay.ylast);
+    d.st = (State *)(c->ws + lay.state);
+    d.stamps = (long long *)(c->ws + lay.stamps);
+    d.twid = (const float2 *)(c->ws + lay.twid);
+    d.M = layers;
+    d.B = batch;
+    d.D = channels;
+    d.L = L;
+    d.logNT = lay.logNT;
+    d.map = o.map == FI_MAP_IDENTITY ? 1 : (o.map == FI_MAP_EXTERNAL ? 2 : 0);
+    d.fb = o.feedback == FI_FEEDBACK_IDENTITY ? 1 : 0;
+    for (int q = 0; q < c->P; ++q)
+        c->spec[q] = fft_exists(q, c->P) ? (float4 *)(c->ws + lay.spec[q]) : nullptr;
+
+    // filters
+    const size_t fbytes = (size_t)layers * channels * L * sizeof(float);
+    if (hipMemcpyAsync((void *)d.filt, filters, fbytes,
+                       o.filters_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                       c->stream) != hipSuccess)
+        return bail(fail(c, FI_EDEVICE, "filter copy failed"));
+    // twiddle table, fp64 on the host
+    {
+        const size_t nt = size_t(1) << lay.logNT;
+        std::vector<float2> tw(nt);
+        for (size_t k = 0; k < nt; ++k) {
+            const double a = -2.0 * 3.14159265358979323846 * (double)k / (double)nt;
+            tw[k] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+        if (hipMemcpyAsync((void *)d.twid, tw.data(), nt * sizeof(float2), hipMemcpyHostToDevice,
+                           c->stream) != hipSuccess ||
+            hipStreamSynchronize(c->stream) != hipSuccess)
+            return bail(fail(c, FI_EDEVICE, "twiddle copy failed"));
+    }
+    // the direct kernels size their LDS at launch (up to 131 KB for 64 layers)
+    if (allow_direct_lds<true>(c) != hipSuccess || allow_direct_lds<false>(c) != hipSuccess)
+        return bail(fail(c, FI_EDEVICE, "direct kernel LDS attribute"));
+    if (clear_state(c) != FI_OK) return bail(FI_EDEVICE);
+
+    // spectra of every class an FFT block may serve
+    for (int q = 0; q < c->P; ++q) {
+        if (!c->spec[q]) continue;
+        if (launch_spectrum(c, q, c->stream) != hipSuccess) return bail(fail(c, FI_EDEVICE, "spectrum launch"));
+    }
+
+    // path table
+    for (int q = 0; q < c->P; ++q) {
+        const bool de = direct_exists(q), fe = fft_exists(q, c->P);
+        int pth = de ? FI_PATH_DIRECT : FI_PATH_FFT;
+        if (o.tau_mode == FI_TAU_DIRECT) pth = de ? FI_PATH_DIRECT : FI_PATH_FFT;
+        else if (o.tau_mode == FI_TAU_FFT) pth = fe ? FI_PATH_FFT : FI_PATH_DIRECT;
+        else if (o.tau_split >= 0) pth = (q >= o.tau_split && fe) || !de ? FI_PATH_FFT : FI_PATH_DIRECT;
+        c->path[q] = pth;
+    }
+    if (o.tau_mode == FI_TAU_AUTO && o.tau_split < 0) {
+        for (int q = 0; q < c->P; ++q) {
+            if (!(direct_exists(q) && fft_exists(q, c->P))) continue;
+            double ud, uf;
+            if (time_class(c, q, ud, uf) != FI_OK) return bail(FI_EDEVICE);
+            c->us_direct[q] = ud;
+            c->us_fft[q] = uf;
+            c->path[q] = (uf >= 0 && uf < ud) ? FI_PATH_FFT : FI_PATH_DIRECT;
+        }
+        if (clear_state(c) != FI_OK) return bail(FI_EDEVICE);
+    }
+    if (o.use_graphs && o.map != FI_MAP_EXTERNAL) {
+        if (build_graphs(c) != FI_OK) return bail(FI_EDEVICE);
+    }
+    if (hipStreamSynchronize(c->stream) != hipSuccess) return bail(fail(c, FI_EDEVICE, "init sync"));
+    *out = c;
+    return FI_OK;
+}
+
+fi_status fi_destroy(fi_ctx *c) {
+    if (!c) return FI_OK;
+    if (c->ws) (void)hipStreamSynchronize(c->stream);
+    destroy_graphs(c);
+    if (c->cap) (void)hipStreamDestroy(c->cap);
+    if (c->own_ws && c->ws) (void)hipFree(c->ws);
+    delete c;
+    return FI_OK;
+}
+
+fi_status fi_reset(fi_ctx *c) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    return clear_state(c);
+}
+
+int64_t fi_position(const fi_ctx *c) { return c ? c->pos : -1; }
+
+const char *fi_last_error(const fi_ctx *c) { return c ? c->err.c_str() : "null context"; }
+
+fi_status fi_set_input(fi_ctx *c, const float *x0) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (!x0) return FI_EINVAL;
+    // position n reads xin[n & 1]; the next position is pos + 1
+    float *dst = c->dev.xin + (size_t)((c->pos + 1) & 1) * c->B * c->D;
+    HIPCK(c, hipMemcpyAsync(dst, x0, (size_t)c->B * c->D * sizeof(float), hipMemcpyDeviceToDevice,
+                            c->stream));
+    return FI_OK;
+}
+
+fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_step in external-block mode");
+    if (c->pos >= c->L) return FI_ERANGE;
+    if ((s = enter_mode(c, 1)) != FI_OK) return s;
+    const int64_t n = c->pos + 1;
+    HIPCK(c, launch_position(c, class_of(c, n), c->stream, x_t, y_t, 1));
+    c->pos = n;
+    return FI_OK;
+}
+
+fi_status fi_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (!x || P < 0) return FI_EINVAL;
+    if (c->pos + P > c->L) return FI_ERANGE;
+    const size_t BD = (size_t)c->B * c->D;
+    for (int64_t i = 0; i < P; ++i) {
+        s = fi_step(c, x + i * BD, y ? y + i * BD : nullptr);
+        if (s != FI_OK) return s;
+    }
+    return FI_OK;
+}
+
+fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_generate in external-block mode");
+    if (steps < 0) return FI_EINVAL;
+    if (c->pos + steps > c->L) return FI_ERANGE;
+    if ((s = enter_mode(c, 1)) != FI_OK) return s;
+    const int64_t pos0 = c->pos, end = c->pos + steps;
+    const int64_t bsize = c->block_log ? (int64_t(1) << c->block_log) : 0;
+    const bool graphs = c->opt.use_graphs != 0;
+    while (c->pos < end) {
+        const int64_t n = c->pos + 1;
+        if (graphs && bsize && ((n - 1) & (bsize - 1)) == 0 && n + bsize - 2 <= end) {
+            HIPCK(c, hipGraphLaunch(c->gblock, c->stream));
+            c->pos += bsize - 1;
+            continue;
+        }
+        const int q = class_of(c, n);
+        if (graphs)
+            HIPCK(c, hipGraphLaunch(c->gclass[q], c->stream));
+        else
+            HIPCK(c, launch_position(c, q, c->stream, nullptr, nullptr, 1));
+        c->pos = n;
+    }
+    if (y && steps > 0) {
+        const size_t BD = (size_t)c->B * c->D;
+        HIPCK(c, hipMemcpyAsync(y, c->dev.ylast + pos0 * BD, steps * BD * sizeof(float),
+                                hipMemcpyDeviceToDevice, c->stream));
+    }
+    return FI_OK;
+}
+
+fi_status fi_debug_schedule(const fi_ctx *c, int64_t n, int *q, int *path) {
+    if (!c || n < 1 || n > c->L) return FI_EINVAL;
+    const int cls = n < c->L ? ctz64(n) : -1;
+    if (q) *q = cls;
+    if (path) *path = cls < 0 ? FI_PATH_NONE : c->path[cls];
+    return FI_OK;
+}
+
+fi_status fi_tau_table(const fi_ctx *c, int *path, double *us_direct, double *us_fft) {
+    if (!c) return FI_EINVAL;
+    for (int q = 0; q < c->P; ++q) {
+        if (path) path[q] = c->path[q];
+        if (us_direct) us_direct[q] = c->us_direct[q];
+        if (us_fft) us_fft[q] = c->us_fft[q];
+    }
+    return FI_OK;
+}
+
+fi_status fi_history(const fi_ctx *cc, int layer, int what, int64_t count, float *dst) {
+    fi_ctx *c = const_cast<fi_ctx *>(cc);
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (layer < 0 || layer >= c->M || count < 0 || count > c->L || !dst || what < 0 || what > 1)
+        return FI_EINVAL;
+    if (what == 1 && !c->dev.rec) return fail(c, FI_ESTATE, "outputs are recorded only with record = 1");
+    if (count == 0) return FI_OK;
+    const float *src = (what == 0 ? c->dev.buf : c->dev.rec) + (size_t)layer * c->B * c->D * c->L;
+    HIPCK(c, hipMemcpy2DAsync(dst, count * sizeof(float), src, c->L * sizeof(float), count * sizeof(float),
+                              (size_t)c->B * c->D, hipMemcpyDeviceToDevice, c->stream));
+    return FI_OK;
+}
+
+fi_status fi_stamps(fi_ctx *c, int64_t first, int64_t count, int64_t *dst) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (first < 0 || count < 0 || first + count > c->L + 1 || (!dst && count)) return FI_EINVAL;
+    HIPCK(c, hipStreamSynchronize(c->stream));
+    if (count) HIPCK(c, hipMemcpy(dst, c->dev.stamps + first, count * sizeof(long long), hipMemcpyDeviceToHost));
+    return FI_OK;
+}
+
+fi_status fi_layer_red(fi_ctx *c, int layer, const float *q, float *y) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map != FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_layer_red needs FI_MAP_EXTERNAL");
+    if (layer < 0 || layer >= c->M || !q || !y) return FI_EINVAL;
+    if (c->pos >= c->L) return FI_ERANGE;
+    if ((s = enter_mode(c, 1)) != FI_OK) return s;
+    const int n = c->B * c->D;
+    hipLaunchKernelGGL(k_red_layer, dim3((n + 255) / 256), dim3(256), 0, c->stream, c->dev, layer, q, y);
+    HIPCK(c, hipGetLastError());
+    return FI_OK;
+}
+
+fi_status fi_tiles(fi_ctx *c) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map != FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_tiles needs FI_MAP_EXTERNAL");
+    if (c->pos >= c->L) return FI_ERANGE;
+    const int64_t n = c->pos + 1;
+    HIPCK(c, launch_tiles(c, class_of(c, n), c->stream));
+    c->pos = n;
+    return FI_OK;
+}
+
+fi_status fi_lazy_step(fi_ctx *c, const float *x_t, float *y_t) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
+    if (c->pos >= c->L) return FI_ERANGE;
+    if ((s = enter_mode(c, 2)) != FI_OK) return s;
+    const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
+    hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev);
+    HIPCK(c, hipGetLastError());
+    HIPCK(c, launch_red(c, c->stream, x_t, y_t, 1));
+    c->pos += 1;
+    return FI_OK;
+}
+
+fi_status fi_lazy_generate(fi_ctx *c, int64_t steps, float *y) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (steps < 0) return FI_EINVAL;
+    if (c->pos + steps > c->L) return FI_ERANGE;
+    const int64_t pos0 = c->pos;
+    for (int64_t i = 0; i < steps; ++i) {
+        s = fi_lazy_step(c, nullptr, nullptr);
+        if (s != FI_OK) return s;
+    }
+    if (y && steps > 0) {
+        const size_t BD = (size_t)c->B * c->D;
+        HIPCK(c, hipMemcpyAsync(y, c->dev.ylast + pos0 * BD, steps * BD * sizeof(float),
+                                hipMemcpyDeviceToDevice, c->stream));
+    }
+    return FI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+"""Thin Python binding of the C-ABI in ``include/fi.h`` (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library ``libfi.so``.  torch is used for device memory (workspace, inputs,
+outputs) and for the current HIP stream.  There is no fallback: if the
+library is missing or no GPU is present, construction raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfi.so")
+
+FI_OK, FI_EINVAL, FI_ENOMEM, FI_EDEVICE, FI_ERANGE, FI_ESTATE = 0, -1, -2, -3, -4, -5
+MAP_TANH, MAP_IDENTITY, MAP_EXTERNAL = 0, 1, 2
+FEEDBACK_TANH, FEEDBACK_IDENTITY = 0, 1
+TAU_AUTO, TAU_DIRECT, TAU_FFT = 0, 1, 2
+PATH_NONE, PATH_DIRECT, PATH_FFT = 0, 1, 2
+_STATUS = {0: "FI_OK", -1: "FI_EINVAL", -2: "FI_ENOMEM", -3: "FI_EDEVICE", -4: "FI_ERANGE",
+           -5: "FI_ESTATE"}
+
+
+class FiError(RuntimeError):
+    def __init__(self, status, msg=""):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("map", ctypes.c_int), ("feedback", ctypes.c_int), ("tau_mode", ctypes.c_int),
+                ("tau_split", ctypes.c_int), ("record", ctypes.c_int), ("use_graphs", ctypes.c_int),
+                ("block_graph_log2", ctypes.c_int), ("filters_on_device", ctypes.c_int),
+                ("reserved", ctypes.c_int * 8)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libfi.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FiError(FI_ESTATE, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    try:
+        import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    OP = ctypes.POINTER(Options)
+    sig = {
+        "fi_default_options": (None, [OP]),
+        "fi_version": (ctypes.c_char_p, []),
+        "fi_workspace_bytes": (S, [I, I, I, I64, OP]),
+        "fi_init": (I, [ctypes.POINTER(P), I, I, I, I64, P, OP, P, P]),
+        "fi_destroy": (I, [P]),
+        "fi_reset": (I, [P]),
+        "fi_step": (I, [P, P, P]),
+        "fi_set_input": (I, [P, P]),
+        "fi_prefill": (I, [P, P, I64, P]),
+        "fi_generate": (I, [P, I64, P]),
+        "fi_position": (I64, [P]),
+        "fi_last_error": (ctypes.c_char_p, [P]),
+        "fi_debug_schedule": (I, [P, I64, ctypes.POINTER(I), ctypes.POINTER(I)]),
+        "fi_tau_table": (I, [P, P, P, P]),
+        "fi_history": (I, [P, I, I, I64, P]),
+        "fi_stamps": (I, [P, I64, I64, P]),
+        "fi_layer_red": (I, [P, I, P, P]),
+        "fi_tiles": (I, [P]),
+        "fi_lazy_step": (I, [P, P, P]),
+        "fi_lazy_generate": (I, [P, I64, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def default_options() -> Options:
+    o = Options()
+    load_library().fi_default_options(ctypes.byref(o))
+    return o
+
+
+def workspace_bytes(M, B, D, L, opt: Options | None = None) -> int:
+    return int(load_library().fi_workspace_bytes(M, B, D, L, ctypes.byref(opt) if opt else None))
+
+
+def _dptr(t):
+    """Device pointer of a CUDA tensor (or None)."""
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "expected a contiguous device tensor"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Context:
+    """One fi_ctx bound to the current torch stream.
+
+    filters: fp32 [M][D][L], a CUDA tensor (copied device to device) or a
+    numpy array (copied from host).  Keyword options map to ``fi_options``.
+    """
+
+    def __init__(self, filters, batch, *, map=MAP_TANH, feedback=FEEDBACK_TANH, tau_mode=TAU_AUTO,
+                 tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, device=None):
+        import torch
+        if not torch.cuda.is_available():
+            raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
+        lib = load_library()
+        self._torch = torch
+        self.device = torch.device(device or "cuda")
+        opt = default_options()
+        opt.map, opt.feedback, opt.tau_mode, opt.tau_split = map, feedback, tau_mode, tau_split
+        opt.record, opt.use_graphs, opt.block_graph_log2 = int(record), int(use_graphs), block_graph_log2
+        if isinstance(filters, np.ndarray):
+            f = np.ascontiguousarray(filters, dtype=np.float32)
+            fptr = f.ctypes.data_as(ctypes.c_void_p)
+            opt.filters_on_device = 0
+            keep = f
+        else:
+            keep = filters.to(self.device, torch.float32).contiguous()
+            fptr = ctypes.c_void_p(keep.data_ptr())
+            opt.filters_on_device = 1
+        M, D, L = (int(s) for s in filters.shape)
+        self.M, self.B, self.D, self.L = M, int(batch), D, L
+        self.P = L.bit_length() - 1
+        nbytes = lib.fi_workspace_bytes(M, self.B, D, L, ctypes.byref(opt))
+        if nbytes == 0:
+            raise FiError(FI_EINVAL, f"unsupported shape M={M} B={batch} D={D} L={L}")
+        self.workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        st = lib.fi_init(ctypes.byref(h), M, self.B, D, L, fptr, ctypes.byref(opt),
+                         ctypes.c_void_p(self.workspace.data_ptr()),
+                         ctypes.c_void_p(self.stream.cuda_stream))
+        del keep
+        if st != FI_OK:
+            raise FiError(st, "fi_init failed")
+        self._h = h
+        self._lib = lib
+        self.options = opt
+
+    # -- helpers ------------------------------------------------------------
+    def _check(self, st):
+        if st != FI_OK:
+            msg = self._lib.fi_last_error(self._h)
+            raise FiError(st, msg.decode() if msg else "")
+
+    def _bd(self, lead=()):
+        return self._torch.empty(tuple(lead) + (self.B, self.D), dtype=self._torch.float32,
+                                 device=self.device)
+
+    # -- API ----------------------------------------------------------------
+    @property
+    def position(self) -> int:
+        return int(self._lib.fi_position(self._h))
+
+    def set_input(self, x0):
+        self._check(self._lib.fi_set_input(self._h, _dptr(x0)))
+
+    def step(self, x=None, y=None):
+        """One position; x: [B][D] device tensor or None (feedback). Returns y [B][D]."""
+        y = self._bd() if y is None else y
+        self._check(self._lib.fi_step(self._h, _dptr(x), _dptr(y)))
+        return y
+
+    def prefill(self, x, y=None, want_y=True):
+        P = int(x.shape[0])
+        if want_y and y is None:
+            y = self._bd((P,))
+        self._check(self._lib.fi_prefill(self._h, _dptr(x), P, _dptr(y)))
+        return y
+
+    def generate(self, steps, y=None, want_y=True):
+        if want_y and y is None:
+            y = self._bd((steps,))
+        self._check(self._lib.fi_generate(self._h, int(steps), _dptr(y)))
+        return y
+
+    def lazy_step(self, x=None, y=None):
+        y = self._bd() if y is None else y
+        self._check(self._lib.fi_lazy_step(self._h, _dptr(x), _dptr(y)))
+        return y
+
+    def lazy_generate(self, steps, y=None, want_y=True):
+        if want_y and y is None:
+            y = self._bd((steps,))
+        self._check(self._lib.fi_lazy_generate(self._h, int(steps), _dptr(y)))
+        return y
+
+    def layer_red(self, layer, q, y=None):
+        y = self._bd() if y is None else y
+        self._check(self._lib.fi_layer_red(self._h, int(layer), _dptr(q), _dptr(y)))
+        return y
+
+    def tiles(self):
+        self._check(self._lib.fi_tiles(self._h))
+
+    def history(self, layer, what, count=None):
+        """[B][D][count] device tensor: what=0 layer inputs x, what=1 recorded outputs y."""
+        count = self.position if count is None else count
+        dst = self._torch.empty((self.B, self.D, max(count, 1)), dtype=self._torch.float32,
+                                device=self.device)[..., :count]
+        dst = dst.contiguous()
+        self._check(self._lib.fi_history(self._h, int(layer), int(what), int(count), _dptr(dst)))
+        return dst
+
+    def stamps(self, first, count):
+        out = np.zeros(count, dtype=np.int64)
+        self._check(self._lib.fi_stamps(self._h, int(first), int(count),
+                                        out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def tau_table(self):
+        P = max(self.P, 1)
+        path = (ctypes.c_int * P)()
+        ud = (ctypes.c_double * P)()
+        uf = (ctypes.c_double * P)()
+        self._check(self._lib.fi_tau_table(self._h, path, ud, uf))
+        return [(q, path[q], ud[q], uf[q]) for q in range(self.P)]
+
+    def schedule(self, n):
+        q, pth = ctypes.c_int(), ctypes.c_int()
+        self._check(self._lib.fi_debug_schedule(self._h, int(n), ctypes.byref(q), ctypes.byref(pth)))
+        return q.value, pth.value
+
+    def reset(self):
+        self._check(self._lib.fi_reset(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.fi_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()

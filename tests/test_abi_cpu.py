@@ -1,0 +1,83 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/fi.h, and validates arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_convolution_sequence_amd import fi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fi.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fi_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fi.LIB_PATH):
+        pytest.fail("libfi.so missing: run __graft_entry__.build() first")
+    return fi.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fi.h but not exported"
+
+
+def test_default_options(lib):
+    o = fi.default_options()
+    assert (o.map, o.feedback, o.tau_mode, o.tau_split) == (fi.MAP_TANH, fi.FEEDBACK_TANH, fi.TAU_AUTO, -1)
+    assert (o.record, o.use_graphs, o.block_graph_log2, o.filters_on_device) == (0, 1, 6, 0)
+    assert lib.fi_version().decode().startswith("fi ")
+
+
+def test_workspace_bytes_shapes(lib):
+    o = fi.default_options()
+    small = fi.workspace_bytes(1, 1, 4, 1024, o)
+    # filters + activations + spectra (~8L bytes per row) + history of outputs
+    assert small >= 4 * 1024 * 4 * 2 + 4 * 8 * 1024 * 0.9
+    o.record = 1
+    assert fi.workspace_bytes(1, 1, 4, 1024, o) >= small + 4 * 1024 * 4
+    # the 18-layer B=4 D=768 L=2^15 stack fits easily in one 288 GB device
+    big = fi.workspace_bytes(18, 4, 768, 32768, None)
+    assert 5e9 < big < 40e9
+
+
+@pytest.mark.parametrize("M,B,D,L", [(0, 1, 1, 8), (1, 0, 1, 8), (1, 1, 0, 8), (1, 1, 1, 1000),
+                                     (1, 1, 1, 0), (65, 1, 1, 8), (1, 1, 1, -4)])
+def test_workspace_bytes_rejects_bad_shapes(lib, M, B, D, L):
+    assert fi.workspace_bytes(M, B, D, L, None) == 0
+
+
+def test_init_rejects_bad_arguments_without_a_device(lib):
+    h = ctypes.c_void_p()
+    f = (ctypes.c_float * 16)()
+    # non-power-of-two L
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 12, f, None, None, None) == fi.FI_EINVAL
+    assert not h.value
+    # null filters
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, None, None, None, None) == fi.FI_EINVAL
+    # null out pointer
+    assert lib.fi_init(None, 1, 1, 1, 8, f, None, None, None) == fi.FI_EINVAL
+    # misaligned workspace
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, None, ctypes.c_void_p(0x1001), None) == fi.FI_EINVAL
+    # invalid option value
+    o = fi.default_options()
+    o.map = 7
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
+
+
+def test_null_context_calls_are_rejected(lib):
+    assert lib.fi_step(None, None, None) == fi.FI_EINVAL
+    assert lib.fi_generate(None, 1, None) == fi.FI_EINVAL
+    assert lib.fi_position(None) == -1
+    assert lib.fi_destroy(None) == fi.FI_OK
+    assert lib.fi_debug_schedule(None, 1, None, None) == fi.FI_EINVAL

@@ -1,0 +1,217 @@
+"""GPU parity of the relaxed-tiling HIP path against the CPU oracle, through
+the C-ABI (ctypes binding).  Small shapes that still span every block-size
+class, both block paths and ragged chain counts."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_convolution_sequence_amd import fi, workloads
+from tests._parity import TF_TOL, check_replay, say
+
+pytestmark = pytest.mark.gpu
+
+TAUS = {"direct": fi.TAU_DIRECT, "fft": fi.TAU_FFT, "auto": fi.TAU_AUTO}
+
+
+def _filters(M, D, L, seed, decay=None):
+    r = np.random.default_rng(seed)
+    h = r.standard_normal((M, D, L))
+    if decay:
+        h *= np.exp(-np.arange(L) / decay)
+    return h.astype(np.float32)
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("tau", list(TAUS))
+def test_single_layer_teacher_forced_matches_definition(tau):
+    M, B, D, L = 1, 2, 5, 256
+    say(f"case single-layer teacher-forced tau={tau} M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 1)
+    x = np.random.default_rng(2).standard_normal((L, B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B, tau_mode=TAUS[tau], map=fi.MAP_IDENTITY) as ctx:
+        paths = [p for (_, p, _, _) in ctx.tau_table()]
+        if tau == "fft":
+            assert all(p == fi.PATH_FFT for p in paths[2:]) and paths[:2] == [fi.PATH_DIRECT] * 2
+        if tau == "direct":
+            assert all(p == fi.PATH_DIRECT for p in paths)
+        y = ctx.prefill(_cuda(x)).cpu().numpy()
+        assert ctx.position == L
+    worst = 0.0
+    for b in range(B):
+        for c in range(D):
+            ref = oracle.conv_rows(h[0, c], x[:, b, c])
+            tol = TF_TOL * np.abs(h[0, c].astype(np.float64)).sum() * np.abs(x[:, :, c]).max()
+            worst = max(worst, np.abs(y[:, b, c] - ref).max() / tol)
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+    # much tighter than the bar: the tiling adds only fp32 rounding
+    assert worst <= 0.05
+
+
+@pytest.mark.parametrize("tau", list(TAUS))
+def test_stack_teacher_forced_per_layer_replay(tau):
+    M, B, D, L = 3, 2, 6, 512
+    say(f"case stack teacher-forced replay tau={tau} M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 3, decay=128.0)
+    x = np.random.default_rng(4).standard_normal((L, B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B, tau_mode=TAUS[tau], record=True) as ctx:
+        y = ctx.prefill(_cuda(x)).cpu().numpy()
+        x0 = ctx.history(0, 0).cpu().numpy()
+        assert np.array_equal(x0, np.transpose(x, (1, 2, 0)))       # inputs land in their slots
+        for l in range(M - 1):                                       # inter-layer map
+            yl = ctx.history(l, 1).cpu().numpy()
+            xn = ctx.history(l + 1, 0).cpu().numpy()
+            assert np.allclose(xn, np.tanh(yl.astype(np.float64)), rtol=0, atol=4e-7)
+        assert np.array_equal(np.transpose(ctx.history(M - 1, 1).cpu().numpy(), (2, 0, 1)), y)
+        worst = check_replay(h, ctx)
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+
+
+def test_feedback_small_config_replay_and_horizon():
+    """1 layer, B=1, D=4, L=1024, h ~ N(0,1) exp(-k/256), x_1 ~ N(0,1), x_{t+1} = tanh(y_t)."""
+    w = workloads.WORKLOADS[1]
+    say(f"case feedback {w.name}")
+    h = workloads.filters(w)
+    x1 = workloads.x_first(w)
+    with fi.Context(_cuda(h), w.B, record=True) as ctx:
+        ctx.set_input(_cuda(x1))
+        y = ctx.generate(w.L).cpu().numpy()            # [L][B][D]
+        xs = ctx.history(0, 0).cpu().numpy()           # [B][D][L]
+        worst = check_replay(h, ctx)
+    say(f"  replay worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+    # the feedback wiring: x_1 given, x_{n+1} = tanh(y_n)
+    assert np.array_equal(xs[:, :, 0], x1)
+    assert np.allclose(xs[:, :, 1:], np.tanh(np.transpose(y, (1, 2, 0))[:, :, :-1].astype(np.float64)),
+                       rtol=0, atol=4e-7)
+    # free-running against the fp64 oracle within the measured divergence horizon
+    chans = np.arange(w.D)
+    y64, _ = oracle.stack(h, chans, x1[0], w.L)
+    y32, _ = oracle.stack_f32(h, chans, x1[0], w.L)
+    scale = np.abs(y64[:, 0]).max()
+    d32 = np.abs(y32[:, 0] - y64[:, 0]).max(axis=0) / scale
+    over = np.nonzero(d32 > 1e-3)[0]
+    horizon = int(over[0]) if over.size else w.L
+    dgpu = np.abs(y[:, 0, :].T - y64[:, 0]).max(axis=0) / scale
+    say(f"  fp32-vs-fp64 horizon {horizon}; GPU rel error over first half {dgpu[:horizon // 2].max():.2e}")
+    assert horizon >= 256
+    assert dgpu[:horizon // 2].max() <= 1e-3
+
+
+def test_paths_agree_and_runs_are_deterministic():
+    M, B, D, L = 2, 3, 7, 1024
+    say(f"case path agreement M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 5, decay=300.0) * 0.05
+    x1 = np.random.default_rng(6).standard_normal((B, D)).astype(np.float32)
+    outs = {}
+    for name, tau in TAUS.items():
+        for graphs in (True, False):
+            with fi.Context(_cuda(h), B, tau_mode=tau, use_graphs=graphs) as ctx:
+                ctx.set_input(_cuda(x1))
+                outs[(name, graphs)] = ctx.generate(L).cpu().numpy()
+    for name in TAUS:
+        assert np.array_equal(outs[(name, True)], outs[(name, False)]), name
+    ref = outs[("direct", True)]
+    for name in ("fft", "auto"):
+        rel = np.abs(outs[(name, True)] - ref).max() / np.abs(ref).max()
+        say(f"  {name} vs direct rel diff {rel:.2e}")
+        assert rel <= 1e-3
+    with fi.Context(_cuda(h), B, tau_mode=fi.TAU_FFT) as ctx:
+        ctx.set_input(_cuda(x1))
+        again = ctx.generate(L).cpu().numpy()
+    assert np.array_equal(again, outs[("fft", True)])
+
+
+def test_prefill_equals_steps_then_generation_continues():
+    M, B, D, L, P = 2, 2, 5, 256, 77
+    say(f"case prefill == steps M={M} B={B} D={D} L={L} P={P}")
+    h = _filters(M, D, L, 7, decay=64.0)
+    x = np.random.default_rng(8).standard_normal((P, B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B) as a, fi.Context(_cuda(h), B) as b:
+        ya = a.prefill(_cuda(x))
+        yb = torch.stack([b.step(_cuda(x[i])) for i in range(P)])
+        assert torch.equal(ya, yb)
+        ga = a.generate(L - P)
+        gb = torch.cat([b.step()[None] for _ in range(L - P)])
+        assert torch.equal(ga, gb)
+        assert a.position == b.position == L
+        with pytest.raises(fi.FiError) as e:
+            a.step()
+        assert e.value.status == fi.FI_ERANGE
+
+
+def test_lazy_baseline_matches_tiled():
+    M, B, D, L = 2, 2, 3, 256
+    say(f"case lazy vs tiled M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 9, decay=64.0) * 0.2
+    x1 = np.random.default_rng(10).standard_normal((B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B, record=True) as ctx:
+        ctx.set_input(_cuda(x1))
+        yt = ctx.generate(L).cpu().numpy()
+        ctx.reset()
+        ctx.set_input(_cuda(x1))
+        yl = ctx.lazy_generate(L).cpu().numpy()
+        worst = check_replay(h, ctx)
+        ctx.reset()
+        ctx.lazy_generate(10, want_y=False)
+        with pytest.raises(fi.FiError) as e:       # tiled and Lazy state do not mix
+            ctx.generate(1)
+        assert e.value.status == fi.FI_ESTATE
+    say(f"  lazy replay worst {worst:.2e}; lazy vs tiled {np.abs(yl - yt).max():.2e}")
+    assert worst <= 1.0
+    assert np.abs(yl - yt).max() <= 1e-3 * np.abs(yt).max()
+
+
+def test_external_block_mode_equals_identity_map():
+    M, B, D, L = 3, 2, 4, 128
+    say(f"case external block mode M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 11, decay=32.0) * 0.3
+    x = np.random.default_rng(12).standard_normal((L, B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B, map=fi.MAP_IDENTITY, tau_mode=fi.TAU_FFT) as ref:
+        yref = ref.prefill(_cuda(x))
+    with fi.Context(_cuda(h), B, map=fi.MAP_EXTERNAL, tau_mode=fi.TAU_FFT) as ext:
+        ys = []
+        for n in range(L):
+            q = _cuda(x[n])
+            for l in range(M):
+                q = ext.layer_red(l, q).clone()   # identity block between layers
+            ys.append(q)
+            ext.tiles()
+        yext = torch.stack(ys)
+    assert torch.equal(yext, yref)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8, 32])
+def test_edge_lengths_and_ragged_chain_counts(L):
+    M, B, D = 2, 3, 7
+    say(f"case edge L={L} M={M} B={B} D={D}")
+    h = _filters(M, D, L, 13)
+    x = np.random.default_rng(14).standard_normal((L, B, D)).astype(np.float32)
+    for tau in (fi.TAU_DIRECT, fi.TAU_FFT):
+        with fi.Context(_cuda(h), B, tau_mode=tau, record=True, map=fi.MAP_IDENTITY) as ctx:
+            ctx.prefill(_cuda(x))
+            assert check_replay(h, ctx) <= 1.0
+            with pytest.raises(fi.FiError):
+                ctx.step(_cuda(x[0]))
+
+
+def test_schedule_and_stamps():
+    M, B, D, L = 1, 1, 4, 64
+    say(f"case schedule/stamps L={L}")
+    h = _filters(M, D, L, 15)
+    with fi.Context(_cuda(h), B) as ctx:
+        for n in range(1, L + 1):
+            q, _ = ctx.schedule(n)
+            assert q == (-1 if n == L else (n & -n).bit_length() - 1)
+        ctx.generate(L, want_y=False)
+        st = ctx.stamps(1, L)
+        assert (st > 0).all() and (np.diff(st) >= 0).all()
+        ctx.reset()
+        assert ctx.position == 0
+        ctx.generate(3, want_y=False)
+        assert ctx.position == 3
