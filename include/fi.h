@@ -82,7 +82,10 @@ typedef struct fi_options {
     int block_graph_log2;  /* k: a block graph replays the 2^k - 1 positions between
                               multiples of 2^k (default 6; 0 disables) */
     int filters_on_device; /* 1: the filters pointer given to fi_init is device memory */
-    int reserved[8];       /* must be zero */
+    int fft_max_log2;      /* widest gray block done as one workgroup transform, as
+                              log2(U) in [12, 14] (default 14: 128 KB of LDS); wider
+                              blocks are split into sub-blocks of that width */
+    int reserved[7];       /* must be zero */
 } fi_options;
 
 /* Fill *opt with the defaults listed above. */

@@ -24,7 +24,8 @@ namespace {
 
 constexpr int kMaxDirectLog = 7;   // direct gray blocks exist for U <= 128
 constexpr int kMinFftLog = 2;      // FFT gray blocks exist for U >= 4
-constexpr int kMaxLdsFftLog = 14;  // largest transform held in one workgroup's LDS
+constexpr int kMaxLdsFftLog = 14;  // largest transform held in one workgroup's LDS (128 KB)
+constexpr int kMinSubLog = 12;     // smallest sub-block width a split block may use
 constexpr int kMaxLayers = 64;
 constexpr int kMaxP = 24;
 
@@ -44,21 +45,29 @@ int ctz64(int64_t n) {
 }
 
 struct Layout {
-    size_t filt = 0, buf = 0, rec = 0, twid = 0, xin = 0, ylast = 0, stamps = 0, state = 0;
+    size_t filt = 0, buf = 0, rec = 0, twid = 0, xin = 0, ylast = 0, stamps = 0, state = 0, scratch = 0;
     size_t spec[kMaxP] = {0};
     size_t total = 0;
     int logNT = 0;
 };
 
-bool fft_exists(int q, int P) { return q >= kMinFftLog && q <= kMaxLdsFftLog && q <= P - 1; }
+bool fft_exists(int q, int P) { return q >= kMinFftLog && q <= P - 1; }
 bool direct_exists(int q) { return q <= kMaxDirectLog; }
+// classes wider than one workgroup transform (2^vlog) are split into
+// K = U / 2^vlog sub-blocks
+bool is_sub(int q, int vlog) { return q > vlog; }
+int sub_k(int q, int vlog) { return 1 << (q - vlog); }
+// float4 entries of class q's spectra per (l, c) row
+size_t spec_row_f4(int q, int vlog) {
+    return is_sub(q, vlog) ? (size_t)(2 * sub_k(q, vlog) - 1) * ((size_t(1) << vlog) / 2) : (size_t(1) << q) / 2;
+}
 
 bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &lay) {
     const int P = ilog2_exact(L);
     if (M < 1 || M > kMaxLayers || B < 1 || D < 1 || P < 0 || P > kMaxP) return false;
+    const int vlog = o.fft_max_log2;
+    if (vlog < kMinSubLog || vlog > kMaxLdsFftLog) return false;
     if ((int64_t)B * D > (int64_t(1) << 24)) return false;
-    // every block size must have a path: above the direct range only FFT blocks exist
-    if (P - 1 > kMaxLdsFftLog) return false;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o2 = off;
@@ -69,10 +78,10 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.filt = take(rowsMD * L * sizeof(float));
     lay.buf = take(rowsMBD * L * sizeof(float));
     lay.rec = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
-    for (int q = 0; q < P; ++q) {
-        lay.spec[q] = fft_exists(q, P) ? take(rowsMD * (size_t(1) << q) * 8) : 0;  // U/2 float4
-    }
-    const int nmax_log = std::min(P - 1, kMaxLdsFftLog);
+    for (int q = 0; q < P; ++q) lay.spec[q] = fft_exists(q, P) ? take(rowsMD * spec_row_f4(q, vlog) * 16) : 0;
+    // forward sub-block spectra of the widest split class: [M*B*D][U/2] float4
+    lay.scratch = (P - 1 > vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
+    const int nmax_log = std::min(P - 1, vlog);
     lay.logNT = std::max(2, nmax_log + 1);
     lay.twid = take((size_t(1) << lay.logNT) * sizeof(float2));
     lay.xin = take((size_t)2 * B * D * sizeof(float));
@@ -96,6 +105,7 @@ struct fi_ctx {
     Layout lay;
     Dev dev{};
     float4 *spec[kMaxP] = {nullptr};
+    float4 *scratch = nullptr;
     int path[kMaxP] = {0};
     double us_direct[kMaxP], us_fft[kMaxP];
     int64_t pos = 0;
@@ -184,16 +194,39 @@ hipError_t launch_fft_n(fi_ctx *c, hipStream_t s, int advance) {
 }
 
 template <int LOGN>
-hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s) {
+hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long goff, long long stride) {
     using S = FftShape<LOGN>;
     const long long rows = (long long)c->M * c->D;
     const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_spectrum<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev,
-                       c->spec[LOGN], 0LL);
+    hipLaunchKernelGGL((k_spectrum<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst, goff,
+                       stride);
     return hipGetLastError();
 }
 
+template <int LOGV>
+hipError_t launch_fft_sub_v(fi_ctx *c, int q, hipStream_t s, int advance) {
+    const int K = sub_k(q, LOGV);
+    const unsigned grid = (unsigned)((long long)c->M * c->B * c->D * K);
+    hipLaunchKernelGGL((k_fft_sub_fwd<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev,
+                       c->scratch, K);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_fft_sub_inv<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev,
+                       (const float4 *)c->scratch, (const float4 *)c->spec[q], K, advance);
+    return hipGetLastError();
+}
+
+hipError_t launch_fft_sub(fi_ctx *c, int q, hipStream_t s, int advance) {
+    switch (c->opt.fft_max_log2) {
+        case 12: return launch_fft_sub_v<12>(c, q, s, advance);
+        case 13: return launch_fft_sub_v<13>(c, q, s, advance);
+        case 14: return launch_fft_sub_v<14>(c, q, s, advance);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_fft(fi_ctx *c, int q, hipStream_t s, int advance) {
+    if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, q, s, advance);
     switch (q) {
         case 2: return launch_fft_n<2>(c, s, advance);
         case 3: return launch_fft_n<3>(c, s, advance);
@@ -213,20 +246,36 @@ hipError_t launch_fft(fi_ctx *c, int q, hipStream_t s, int advance) {
 }
 
 hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
+    float4 *dst = c->spec[q];
+    const int vlog = c->opt.fft_max_log2;
+    const long long stride = (long long)spec_row_f4(q, vlog);
+    if (is_sub(q, vlog)) {
+        // offset spectra d = 1 .. 2K-1: taps h[(d-1)V .. (d+1)V-1]
+        const long long V = 1LL << vlog;
+        for (int d = 1; d <= 2 * sub_k(q, vlog) - 1; ++d) {
+            float4 *dd = dst + (d - 1) * (V / 2);
+            const long long goff = (d - 1) * V;
+            hipError_t e = vlog == 12   ? launch_spectrum_n<12>(c, s, dd, goff, stride)
+                           : vlog == 13 ? launch_spectrum_n<13>(c, s, dd, goff, stride)
+                                        : launch_spectrum_n<14>(c, s, dd, goff, stride);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     switch (q) {
-        case 2: return launch_spectrum_n<2>(c, s);
-        case 3: return launch_spectrum_n<3>(c, s);
-        case 4: return launch_spectrum_n<4>(c, s);
-        case 5: return launch_spectrum_n<5>(c, s);
-        case 6: return launch_spectrum_n<6>(c, s);
-        case 7: return launch_spectrum_n<7>(c, s);
-        case 8: return launch_spectrum_n<8>(c, s);
-        case 9: return launch_spectrum_n<9>(c, s);
-        case 10: return launch_spectrum_n<10>(c, s);
-        case 11: return launch_spectrum_n<11>(c, s);
-        case 12: return launch_spectrum_n<12>(c, s);
-        case 13: return launch_spectrum_n<13>(c, s);
-        case 14: return launch_spectrum_n<14>(c, s);
+        case 2: return launch_spectrum_n<2>(c, s, dst, 0, stride);
+        case 3: return launch_spectrum_n<3>(c, s, dst, 0, stride);
+        case 4: return launch_spectrum_n<4>(c, s, dst, 0, stride);
+        case 5: return launch_spectrum_n<5>(c, s, dst, 0, stride);
+        case 6: return launch_spectrum_n<6>(c, s, dst, 0, stride);
+        case 7: return launch_spectrum_n<7>(c, s, dst, 0, stride);
+        case 8: return launch_spectrum_n<8>(c, s, dst, 0, stride);
+        case 9: return launch_spectrum_n<9>(c, s, dst, 0, stride);
+        case 10: return launch_spectrum_n<10>(c, s, dst, 0, stride);
+        case 11: return launch_spectrum_n<11>(c, s, dst, 0, stride);
+        case 12: return launch_spectrum_n<12>(c, s, dst, 0, stride);
+        case 13: return launch_spectrum_n<13>(c, s, dst, 0, stride);
+        case 14: return launch_spectrum_n<14>(c, s, dst, 0, stride);
         default: return hipErrorInvalidValue;
     }
 }
@@ -388,6 +437,7 @@ void fi_default_options(fi_options *o) {
     o->use_graphs = 1;
     o->block_graph_log2 = 6;
     o->filters_on_device = 0;
+    o->fft_max_log2 = kMaxLdsFftLog;
 }
 
 const char *fi_version(void) { return "fi 0.1 gfx950"; }
@@ -465,6 +515,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     d.fb = o.feedback == FI_FEEDBACK_IDENTITY ? 1 : 0;
     for (int q = 0; q < c->P; ++q)
         c->spec[q] = fft_exists(q, c->P) ? (float4 *)(c->ws + lay.spec[q]) : nullptr;
+    c->scratch = lay.scratch ? (float4 *)(c->ws + lay.scratch) : nullptr;
 
     // filters
     const size_t fbytes = (size_t)layers * channels * L * sizeof(float);

@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, const f
 // ---------------------------------------------------------------------------
 template <int LOGN>
 __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 *__restrict__ spec,
-                                                                  long long goff) {
+                                                                  long long goff, long long row_stride) {
     using S = FftShape<LOGN>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0;
     __shared__ float2 smem[S::LDS];
@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     const float inv = 1.0f / (float)N;
-    float4 *dst = spec + (size_t)rowi * (N / 2);
+    float4 *dst = spec + (size_t)rowi * (size_t)row_stride;
     for (int j = lt; j < N / 2 && active; j += TT) {
         if (j == 0) {
             const float2 C0 = X[0];
@@ -287,6 +287,126 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
             dst[j] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Gray blocks wider than one workgroup's LDS transform (U = K * V, V = 2^LOGV).
+// The block is split into K input sub-blocks i and K output sub-blocks o of
+// V positions; sub-block i reaches sub-block o through taps offset by
+// d*V, d = K + o - i (1 <= d <= 2K-1), and each such pair is again a
+// length-2V circular convolution whose upper half is exact.  The sum over i is
+// taken in frequency space, so each output sub-block needs one inverse
+// transform.  Spectra: per (l, c), 2K-1 spectra (d = 1..2K-1) of the taps
+// h[(d-1)V .. (d+1)V-1], each V/2 float4 in pair order.
+//
+// k_fft_sub_fwd: per (l, b, c, i), the real bins of the zero-padded input
+// sub-block i, stored in pair order in `scratch` ([tile][i][V/2] float4).
+// ---------------------------------------------------------------------------
+template <int LOGV>
+__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, float4 *__restrict__ scratch,
+                                                                     int K) {
+    using S = FftShape<LOGV>;
+    constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
+    static_assert(S::PER_BLOCK == 1, "sub-block transforms fill a workgroup");
+    __shared__ float2 smem[S::LDS];
+    const int lt = threadIdx.x;
+    const long long U = (long long)K * N;
+    const long long n = p.st->pos + 1;
+    const long long t = n - 1;
+    if (n > p.L || n % U != 0 || n + U > p.L) return;  // uniform guard
+    const long long tile = (long long)blockIdx.x / K;
+    const int i = (int)(blockIdx.x % K);
+    const size_t row = (size_t)tile * (size_t)p.L;
+    const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + t - U + 1 + (long long)i * N);
+    float2 *X = smem;
+    float2 v[1 << R0];
+#pragma unroll
+    for (int m = 0; m < HALF0; ++m) {
+        v[m] = xsrc[lt + (m << QLOG0)];
+        v[m + HALF0] = make_float2(0.f, 0.f);
+    }
+    dif_stages<R0>(v, lt, LOGV, QLOG0, p.twid, p.logNT);
+#pragma unroll
+    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    forward_groups<LOGV, 1>(X, lt, p.twid, p.logNT);
+    __syncthreads();
+    float4 *dst = scratch + ((size_t)tile * K + i) * (N / 2);
+    for (int j = lt; j < N / 2; j += TT) {
+        if (j == 0) {
+            const float2 C0 = X[0];
+            const float2 Ch = X[lpad(1)];
+            dst[0] = make_float4(C0.x + C0.y, C0.x - C0.y, Ch.x, -Ch.y);
+        } else {
+            float2 A1, A2;
+            real_bins(X[lpad(bitrev<LOGV>(j))], X[lpad(bitrev<LOGV>(N - j))],
+                      twiddle(p.twid, p.logNT, LOGV + 1, j), A1, A2);
+            dst[j] = make_float4(A1.x, A1.y, A2.x, A2.y);
+        }
+    }
+}
+
+// k_fft_sub_inv: per (l, b, c, o), Z = sum_i A_i * G_{K+o-i}, then the inverse
+// transform and accumulation of its exact upper half into output sub-block o.
+template <int LOGV>
+__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, const float4 *__restrict__ scratch,
+                                                                     const float4 *__restrict__ spec, int K,
+                                                                     int advance) {
+    using S = FftShape<LOGV>;
+    constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
+    __shared__ float2 smem[S::LDS];
+    const int lt = threadIdx.x;
+    const long long U = (long long)K * N;
+    const long long n = p.st->pos + 1;
+    const long long t = n - 1;
+    if (n > p.L || n % U != 0 || n + U > p.L) return;  // uniform guard
+    const long long tile = (long long)blockIdx.x / K;
+    const int o = (int)(blockIdx.x % K);
+    const int c = (int)(tile % p.D);
+    const int l = (int)(tile / ((long long)p.D * p.B));
+    const size_t row = (size_t)tile * (size_t)p.L;
+    float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1 + (long long)o * N);
+    const float4 *A = scratch + (size_t)tile * K * (N / 2);
+    const float4 *G = spec + ((size_t)l * p.D + c) * (size_t)(2 * K - 1) * (N / 2);
+    float2 *X = smem;
+    float2 acc[HALF0];
+#pragma unroll
+    for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
+    for (int j = lt; j < N / 2; j += TT) {
+        if (j == 0) {
+            float Z0 = 0.f, ZN = 0.f;
+            float2 Zh = make_float2(0.f, 0.f);
+            for (int i = 0; i < K; ++i) {
+                const float4 a = A[(size_t)i * (N / 2)];
+                const float4 g = G[(size_t)(K + o - i - 1) * (N / 2)];
+                Z0 = fmaf(a.x, g.x, Z0);
+                ZN = fmaf(a.y, g.y, ZN);
+                Zh = cadd(Zh, cmul(make_float2(a.z, a.w), make_float2(g.z, g.w)));
+            }
+            X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
+            X[lpad(1)] = make_float2(Zh.x, -Zh.y);
+        } else {
+            float2 Z1 = make_float2(0.f, 0.f), Z2 = make_float2(0.f, 0.f);
+            for (int i = 0; i < K; ++i) {
+                const float4 a = A[(size_t)i * (N / 2) + j];
+                const float4 g = G[(size_t)(K + o - i - 1) * (N / 2) + j];
+                Z1 = cadd(Z1, cmul(make_float2(a.x, a.y), make_float2(g.x, g.y)));
+                Z2 = cadd(Z2, cmul(make_float2(a.z, a.w), make_float2(g.z, g.w)));
+            }
+            float2 D1, D2;
+            pack_inverse(Z1, Z2, twiddle(p.twid, p.logNT, LOGV + 1, j), D1, D2);
+            X[lpad(bitrev<LOGV>(j))] = D1;
+            X[lpad(bitrev<LOGV>(N - j))] = D2;
+        }
+    }
+    __syncthreads();
+    inverse_groups<LOGV, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    float2 v[1 << R0];
+#pragma unroll
+    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
+    dit_stages<R0>(v, lt, LOGV, QLOG0, p.twid, p.logNT);
+#pragma unroll
+    for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
+    finish_position(p, n, advance);
 }
 
 // ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ class Options(ctypes.Structure):
     _fields_ = [("map", ctypes.c_int), ("feedback", ctypes.c_int), ("tau_mode", ctypes.c_int),
                 ("tau_split", ctypes.c_int), ("record", ctypes.c_int), ("use_graphs", ctypes.c_int),
                 ("block_graph_log2", ctypes.c_int), ("filters_on_device", ctypes.c_int),
-                ("reserved", ctypes.c_int * 8)]
+                ("fft_max_log2", ctypes.c_int), ("reserved", ctypes.c_int * 7)]
 
 
 _lib = None
@@ -110,7 +110,8 @@ class Context:
     """
 
     def __init__(self, filters, batch, *, map=MAP_TANH, feedback=FEEDBACK_TANH, tau_mode=TAU_AUTO,
-                 tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, device=None):
+                 tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, fft_max_log2=14,
+                 device=None):
         import torch
         if not torch.cuda.is_available():
             raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
@@ -120,6 +121,7 @@ class Context:
         opt = default_options()
         opt.map, opt.feedback, opt.tau_mode, opt.tau_split = map, feedback, tau_mode, tau_split
         opt.record, opt.use_graphs, opt.block_graph_log2 = int(record), int(use_graphs), block_graph_log2
+        opt.fft_max_log2 = fft_max_log2
         if isinstance(filters, np.ndarray):
             f = np.ascontiguousarray(filters, dtype=np.float32)
             fptr = f.ctypes.data_as(ctypes.c_void_p)
