@@ -85,7 +85,10 @@ typedef struct fi_options {
     int fft_max_log2;      /* widest gray block done as one workgroup transform, as
                               log2(U) in [12, 14] (default 14: 128 KB of LDS); wider
                               blocks are split into sub-blocks of that width */
-    int reserved[7];       /* must be zero */
+    int time_blocks;       /* 1: fi_generate brackets every FFT gray-block launch with
+                              HIP events on the context stream (read with
+                              fi_block_times); those positions then bypass graphs */
+    int reserved[6];       /* must be zero */
 } fi_options;
 
 /* Fill *opt with the defaults listed above. */
@@ -193,6 +196,20 @@ fi_status fi_tiles(fi_ctx *ctx);
  * otherwise; likewise tiled calls after Lazy calls until fi_reset). */
 fi_status fi_lazy_step(fi_ctx *ctx, const float *x_t, float *y_t);
 fi_status fi_lazy_generate(fi_ctx *ctx, int64_t steps, float *y);
+
+/* Per-class FFT gray-block timing (needs time_blocks = 1): for q = 0..P-1,
+ * ms[q] = summed event-measured milliseconds of the FFT gray-block kernels of
+ * class q launched by fi_generate, count[q] = number of such launches.
+ * Synchronises the stream.  clear = 1 zeroes the sums afterwards.  Arrays hold
+ * at least P entries; either may be NULL. */
+fi_status fi_block_times(fi_ctx *ctx, int clear, double *ms, int64_t *count);
+
+/* Benchmark support for the Lazy baseline: the mean device time in
+ * microseconds of the Lazy work of position n (every layer's full O(n) sum
+ * plus the red cells), over `reps` launches timed with HIP events, without
+ * advancing.  The activation rows are overwritten: the context must be reset
+ * (fi_reset) before any further stepping (FI_ESTATE otherwise). */
+fi_status fi_lazy_time(fi_ctx *ctx, int64_t n, int reps, double *us);
 
 #ifdef __cplusplus
 }

@@ -115,6 +115,12 @@ struct fi_ctx {
     hipGraphExec_t gclass[kMaxP + 1] = {nullptr};
     hipGraphExec_t gblock = nullptr;
     int block_log = 0;
+    // FFT gray-block timing: recorded event pairs not yet read, and the sums
+    std::vector<hipEvent_t> ev;
+    std::vector<int> ev_class;
+    size_t ev_used = 0;
+    double blk_ms[kMaxP] = {0};
+    int64_t blk_count[kMaxP] = {0};
 };
 
 namespace {
@@ -332,6 +338,11 @@ fi_status clear_state(fi_ctx *c) {
     if (s != FI_OK) return s;
     c->pos = 0;
     c->mode = 0;
+    for (int q = 0; q < kMaxP; ++q) {
+        c->blk_ms[q] = 0.0;
+        c->blk_count[q] = 0;
+    }
+    c->ev_used = 0;
     return FI_OK;
 }
 
@@ -413,6 +424,45 @@ void destroy_graphs(fi_ctx *c) {
         }
     if (c->gblock) (void)hipGraphExecDestroy(c->gblock);
     c->gblock = nullptr;
+    for (auto &e : c->ev)
+        if (e) (void)hipEventDestroy(e);
+    c->ev.clear();
+}
+
+// Read every recorded event pair into the per-class sums (synchronises).
+fi_status harvest_events(fi_ctx *c) {
+    if (c->ev_used == 0) return FI_OK;
+    HIPCK(c, hipStreamSynchronize(c->stream));
+    for (size_t i = 0; i < c->ev_used; ++i) {
+        float ms = 0.f;
+        HIPCK(c, hipEventElapsedTime(&ms, c->ev[2 * i], c->ev[2 * i + 1]));
+        c->blk_ms[c->ev_class[i]] += ms;
+        c->blk_count[c->ev_class[i]] += 1;
+    }
+    c->ev_used = 0;
+    return FI_OK;
+}
+
+// One FFT-class position launched directly, its gray-block kernels bracketed
+// by events.
+fi_status launch_timed_position(fi_ctx *c, int q) {
+    constexpr size_t kPairs = 4096;
+    if (c->ev.empty()) {
+        c->ev.resize(2 * kPairs, nullptr);
+        c->ev_class.resize(kPairs, 0);
+        for (auto &e : c->ev) HIPCK(c, hipEventCreate(&e));
+    }
+    if (c->ev_used == kPairs) {
+        fi_status s = harvest_events(c);
+        if (s != FI_OK) return s;
+    }
+    const size_t i = c->ev_used++;
+    c->ev_class[i] = q;
+    HIPCK(c, launch_red(c, c->stream, nullptr, nullptr, 0));
+    HIPCK(c, hipEventRecord(c->ev[2 * i], c->stream));
+    HIPCK(c, launch_fft(c, q, c->stream, 1));
+    HIPCK(c, hipEventRecord(c->ev[2 * i + 1], c->stream));
+    return FI_OK;
 }
 
 fi_status enter_mode(fi_ctx *c, int mode) {
@@ -649,10 +699,14 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
             continue;
         }
         const int q = class_of(c, n);
-        if (graphs)
+        if (c->opt.time_blocks && q < c->P && c->path[q] == FI_PATH_FFT) {
+            s = launch_timed_position(c, q);
+            if (s != FI_OK) return s;
+        } else if (graphs) {
             HIPCK(c, hipGraphLaunch(c->gclass[q], c->stream));
-        else
+        } else {
             HIPCK(c, launch_position(c, q, c->stream, nullptr, nullptr, 1));
+        }
         c->pos = n;
     }
     if (y && steps > 0) {
@@ -739,6 +793,50 @@ fi_status fi_lazy_step(fi_ctx *c, const float *x_t, float *y_t) {
     HIPCK(c, hipGetLastError());
     HIPCK(c, launch_red(c, c->stream, x_t, y_t, 1));
     c->pos += 1;
+    return FI_OK;
+}
+
+fi_status fi_block_times(fi_ctx *c, int clear, double *ms, int64_t *count) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if ((s = harvest_events(c)) != FI_OK) return s;
+    for (int q = 0; q < c->P; ++q) {
+        if (ms) ms[q] = c->blk_ms[q];
+        if (count) count[q] = c->blk_count[q];
+        if (clear) {
+            c->blk_ms[q] = 0.0;
+            c->blk_count[q] = 0;
+        }
+    }
+    return FI_OK;
+}
+
+fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (n < 1 || n > c->L || reps < 1 || !us) return FI_EINVAL;
+    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
+    if ((s = set_state_pos(c, n - 1)) != FI_OK) return s;
+    c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
+    const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    auto once = [&]() -> hipError_t {
+        hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev);
+        hipError_t e = hipGetLastError();
+        return e != hipSuccess ? e : launch_red(c, c->stream, nullptr, nullptr, 0);
+    };
+    HIPCK(c, once());  // warm-up
+    HIPCK(c, hipEventRecord(a, c->stream));
+    for (int r = 0; r < reps; ++r) HIPCK(c, once());
+    HIPCK(c, hipEventRecord(b, c->stream));
+    HIPCK(c, hipEventSynchronize(b));
+    float ms = 0.f;
+    HIPCK(c, hipEventElapsedTime(&ms, a, b));
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    *us = ms * 1000.0 / reps;
     return FI_OK;
 }
 

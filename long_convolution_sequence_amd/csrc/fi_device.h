@@ -50,19 +50,19 @@ __device__ __forceinline__ size_t filt_row(const Dev &p, int l, int c) {
 }
 
 // End of the last kernel of a position: the last workgroup to finish stamps
-// the device clock and publishes the new position.  Every thread fences its
-// own stores first so that "done" only counts completed workgroups.
+// the device clock and publishes the new position.  No memory fence is needed:
+// every workgroup read the position when it started, before it counts itself
+// done, and the next kernel (same stream) sees the new position and all of
+// this kernel's stores through the kernel boundary.
 __device__ __forceinline__ void finish_position(const Dev &p, long long n, int advance) {
     if (!advance) return;
-    __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned prev = atomicAdd(&p.st->done, 1u);
+        const unsigned prev = atomicAdd(&p.st->done, 1u);
         if (prev == gridDim.x - 1) {
             p.stamps[n] = (long long)wall_clock64();
             p.st->done = 0;
             p.st->pos = n;
-            __threadfence();
         }
     }
 }

@@ -19,6 +19,8 @@
 // straight into the accumulators.  Twiddles come from a table generated in
 // fp64 on the host.
 #pragma once
+#include <type_traits>
+
 #include "fi_device.h"
 
 namespace fi {
@@ -33,45 +35,119 @@ __device__ __forceinline__ float2 twiddle(const float2 *__restrict__ tw, int log
     return tw[j << (logNT - slog)];
 }
 
-// R radix-2 DIF stages on v[0..2^R).  The values sit at element offsets
-// r + m*Q (Q = 2^qlog) of a block whose size at the first stage is 2^slog.
-template <int R>
-__device__ __forceinline__ void dif_stages(float2 (&v)[1 << R], int r, int slog, int qlog,
-                                           const float2 *__restrict__ tw, int logNT) {
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const int half = (1 << R) >> (t + 1);
-#pragma unroll
-        for (int m = 0; m < (1 << R); ++m) {
-            if ((m & half) == 0) {
-                const int j = r + ((m & (half - 1)) << qlog);
-                const float2 a = v[m], b = v[m + half];
-                v[m] = cadd(a, b);
-                v[m + half] = cmul(csub(a, b), twiddle(tw, logNT, slog - t, j));
-            }
-        }
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
     }
 }
 
-// Inverse of dif_stages up to a factor 2 per stage (conjugate twiddles,
-// stages in reverse order).
+// d * W_16^K and d * conj(W_16^K) for 0 <= K < 8 (W_16 = exp(-2 pi i / 16)).
+constexpr float kC8 = 0.923879532511286756f;   // cos(pi/8)
+constexpr float kS8 = 0.382683432365089772f;   // sin(pi/8)
+constexpr float kR2 = 0.707106781186547524f;   // sqrt(2)/2
+template <int K>
+__device__ __forceinline__ float2 mul_w16(float2 d) {
+    if constexpr (K == 0) return d;
+    else if constexpr (K == 4) return make_float2(d.y, -d.x);
+    else if constexpr (K == 2) return make_float2(kR2 * (d.x + d.y), kR2 * (d.y - d.x));
+    else if constexpr (K == 6) return make_float2(kR2 * (d.y - d.x), -kR2 * (d.x + d.y));
+    else {
+        constexpr float c = K == 1 ? kC8 : K == 3 ? kS8 : K == 5 ? -kS8 : -kC8;
+        constexpr float s = K == 1 ? kS8 : K == 3 ? kC8 : K == 5 ? kC8 : kS8;
+        return make_float2(d.x * c + d.y * s, d.y * c - d.x * s);
+    }
+}
+template <int K>
+__device__ __forceinline__ float2 mul_w16c(float2 d) {
+    if constexpr (K == 0) return d;
+    else if constexpr (K == 4) return make_float2(-d.y, d.x);
+    else if constexpr (K == 2) return make_float2(kR2 * (d.x - d.y), kR2 * (d.x + d.y));
+    else if constexpr (K == 6) return make_float2(-kR2 * (d.x + d.y), kR2 * (d.x - d.y));
+    else {
+        constexpr float c = K == 1 ? kC8 : K == 3 ? kS8 : K == 5 ? -kS8 : -kC8;
+        constexpr float s = K == 1 ? kS8 : K == 3 ? kC8 : K == 5 ? kC8 : kS8;
+        return make_float2(d.x * c - d.y * s, d.y * c + d.x * s);
+    }
+}
+
+template <int R, int P>
+constexpr int rev_bits() {
+    int r = 0;
+    for (int i = 0; i < R; ++i) r |= ((P >> i) & 1) << (R - 1 - i);
+    return r;
+}
+
+// pw[k] = w^k, k < 2^R, by a product tree of depth <= R.
 template <int R>
-__device__ __forceinline__ void dit_stages(float2 (&v)[1 << R], int r, int slog, int qlog,
-                                           const float2 *__restrict__ tw, int logNT) {
-#pragma unroll
-    for (int t = R - 1; t >= 0; --t) {
-        const int half = (1 << R) >> (t + 1);
-#pragma unroll
-        for (int m = 0; m < (1 << R); ++m) {
-            if ((m & half) == 0) {
-                const int j = r + ((m & (half - 1)) << qlog);
+__device__ __forceinline__ void powers(float2 w, float2 (&pw)[1 << R]) {
+    pw[0] = make_float2(1.f, 0.f);
+    if constexpr (R > 0) pw[1] = w;
+    static_for<2, (1 << R)>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        pw[k] = cmul(pw[k / 2], pw[k - k / 2]);
+    });
+}
+
+// One group of R radix-2 DIF stages on v[0..2^R): the values sit at element
+// offsets r + m*Q of a block of size S = 2^slog (Q = S / 2^R).  Equivalent
+// form used here: a 2^R-point DFT over m with constant roots (output k left
+// in register rev(k)), then the outer twiddle W_S^{r*k}.  PRUNED: the upper
+// half of v is known to be zero.
+template <int R, bool PRUNED = false>
+__device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
+                                          const float2 *__restrict__ tw, int logNT) {
+    static_for<0, R>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int half = (1 << R) >> (t + 1);
+        static_for<0, (1 << R)>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr ((m & half) == 0) {
+                constexpr int k = (m & (half - 1)) * (16 / (2 * half));
+                if constexpr (PRUNED && t == 0) {
+                    v[m + half] = mul_w16<k>(v[m]);
+                } else {
+                    const float2 a = v[m], b = v[m + half];
+                    v[m] = cadd(a, b);
+                    v[m + half] = mul_w16<k>(csub(a, b));
+                }
+            }
+        });
+    });
+    float2 pw[1 << R];
+    powers<R>(twiddle(tw, logNT, slog, r), pw);
+    static_for<1, (1 << R)>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        v[p] = cmul(v[p], pw[rev_bits<R, p>()]);
+    });
+}
+
+// Inverse of dif_group up to the factor 2^R: conjugate outer twiddles, then
+// the stages in reverse order with conjugate constant roots.
+template <int R>
+__device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
+                                          const float2 *__restrict__ tw, int logNT) {
+    float2 pw[1 << R];
+    powers<R>(twiddle(tw, logNT, slog, r), pw);
+    static_for<1, (1 << R)>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        v[p] = cmulc(v[p], pw[rev_bits<R, p>()]);
+    });
+    static_for<0, R>([&](auto tc) {
+        constexpr int t = R - 1 - decltype(tc)::value;
+        constexpr int half = (1 << R) >> (t + 1);
+        static_for<0, (1 << R)>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr ((m & half) == 0) {
+                constexpr int k = (m & (half - 1)) * (16 / (2 * half));
                 const float2 a = v[m];
-                const float2 b = cmulc(v[m + half], twiddle(tw, logNT, slog - t, j));
+                const float2 b = mul_w16c<k>(v[m + half]);
                 v[m] = cadd(a, b);
                 v[m + half] = csub(a, b);
             }
-        }
-    }
+        });
+    });
 }
 
 // Compile-time description of a transform of 2^LOGN complex points.
@@ -102,10 +178,10 @@ __device__ __forceinline__ void lds_group(float2 *X, int lt, const float2 *__res
         float2 v[1 << R];
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) v[m] = X[lpad(base + (m << QLOG))];
-        if (FWD)
-            dif_stages<R>(v, r, SLOG, QLOG, tw, logNT);
+        if constexpr (FWD)
+            dif_group<R>(v, r, SLOG, tw, logNT);
         else
-            dit_stages<R>(v, r, SLOG, QLOG, tw, logNT);
+            dit_group<R>(v, r, SLOG, tw, logNT);
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) X[lpad(base + (m << QLOG))] = v[m];
     }

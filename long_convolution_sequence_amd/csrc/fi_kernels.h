@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, const f
         v[m] = active ? xsrc[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
         v[m + HALF0] = make_float2(0.f, 0.f);
     }
-    dif_stages<R0>(v, lt, LOGN, QLOG0, p.twid, p.logNT);
+    dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, const f
     inverse_groups<LOGN, S::NPASS - 1>(X, lt, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_stages<R0>(v, lt, LOGN, QLOG0, p.twid, p.logNT);
+    dit_group<R0>(v, lt, LOGN, p.twid, p.logNT);
     if (active) {
 #pragma unroll
         for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
     float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = active ? src[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
-    dif_stages<R0>(v, lt, LOGN, QLOG0, p.twid, p.logNT);
+    dif_group<R0>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, floa
         v[m] = xsrc[lt + (m << QLOG0)];
         v[m + HALF0] = make_float2(0.f, 0.f);
     }
-    dif_stages<R0>(v, lt, LOGV, QLOG0, p.twid, p.logNT);
+    dif_group<R0, true>(v, lt, LOGV, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
     forward_groups<LOGV, 1>(X, lt, p.twid, p.logNT);
@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, cons
     float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_stages<R0>(v, lt, LOGV, QLOG0, p.twid, p.logNT);
+    dit_group<R0>(v, lt, LOGV, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
     finish_position(p, n, advance);

@@ -34,7 +34,8 @@ class Options(ctypes.Structure):
     _fields_ = [("map", ctypes.c_int), ("feedback", ctypes.c_int), ("tau_mode", ctypes.c_int),
                 ("tau_split", ctypes.c_int), ("record", ctypes.c_int), ("use_graphs", ctypes.c_int),
                 ("block_graph_log2", ctypes.c_int), ("filters_on_device", ctypes.c_int),
-                ("fft_max_log2", ctypes.c_int), ("reserved", ctypes.c_int * 7)]
+                ("fft_max_log2", ctypes.c_int), ("time_blocks", ctypes.c_int),
+                ("reserved", ctypes.c_int * 6)]
 
 
 _lib = None
@@ -75,6 +76,8 @@ def load_library():
         "fi_tiles": (I, [P]),
         "fi_lazy_step": (I, [P, P, P]),
         "fi_lazy_generate": (I, [P, I64, P]),
+        "fi_block_times": (I, [P, I, P, P]),
+        "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -111,7 +114,7 @@ class Context:
 
     def __init__(self, filters, batch, *, map=MAP_TANH, feedback=FEEDBACK_TANH, tau_mode=TAU_AUTO,
                  tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, fft_max_log2=14,
-                 device=None):
+                 time_blocks=False, device=None):
         import torch
         if not torch.cuda.is_available():
             raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
@@ -122,6 +125,7 @@ class Context:
         opt.map, opt.feedback, opt.tau_mode, opt.tau_split = map, feedback, tau_mode, tau_split
         opt.record, opt.use_graphs, opt.block_graph_log2 = int(record), int(use_graphs), block_graph_log2
         opt.fft_max_log2 = fft_max_log2
+        opt.time_blocks = int(time_blocks)
         if isinstance(filters, np.ndarray):
             f = np.ascontiguousarray(filters, dtype=np.float32)
             fptr = f.ctypes.data_as(ctypes.c_void_p)
@@ -228,6 +232,20 @@ class Context:
         uf = (ctypes.c_double * P)()
         self._check(self._lib.fi_tau_table(self._h, path, ud, uf))
         return [(q, path[q], ud[q], uf[q]) for q in range(self.P)]
+
+    def block_times(self, clear=False):
+        """Per class q: (summed FFT gray-block ms, launches) measured with HIP events."""
+        P = max(self.P, 1)
+        ms = (ctypes.c_double * P)()
+        cnt = (ctypes.c_int64 * P)()
+        self._check(self._lib.fi_block_times(self._h, int(clear), ms, cnt))
+        return [(q, ms[q], cnt[q]) for q in range(self.P)]
+
+    def lazy_time(self, n, reps=3):
+        """Mean microseconds of the Lazy baseline's work at position n (needs reset after)."""
+        us = ctypes.c_double()
+        self._check(self._lib.fi_lazy_time(self._h, int(n), int(reps), ctypes.byref(us)))
+        return us.value
 
     def schedule(self, n):
         q, pth = ctypes.c_int(), ctypes.c_int()
