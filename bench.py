@@ -81,13 +81,19 @@ def cpu_baseline(w, h, target_s=12.0):
     rng = np.random.default_rng(0)
     chains = np.sort(rng.choice(w.B * w.D, nch, replace=False))
     cs = (chains % w.D).astype(np.int32)
-    t0 = time.time()
-    oracle.stack(h, cs, x1[chains], 512)                     # probe, then one sized run
-    probe = max(time.time() - t0, 1e-3)
-    steps = int(min(w.L, max(512, 512 * np.sqrt(target_s / probe))))
-    t0 = time.time()
-    oracle.stack(h, cs, x1[chains], steps)
-    dt = time.time() - t0
+    def run(steps):
+        t0 = time.time()
+        oracle.stack(h, cs, x1[chains], steps)
+        return time.time() - t0
+
+    steps = 1024                                  # grow the prefix until a run takes >= 1 s,
+    dt = run(steps)                               # then size one run to about target_s
+    while dt < 1.0 and steps < w.L:
+        steps = min(w.L, steps * 2)
+        dt = run(steps)
+    if dt < target_s and steps < w.L:
+        steps = int(min(w.L, steps * np.sqrt(target_s / dt)))
+        dt = run(steps)
     # sum_{n<=L} n / sum_{n<=steps} n  and  chains total / sampled
     full = dt * (w.L * (w.L + 1)) / (steps * (steps + 1)) * (w.B * w.D) / nch
     return {

@@ -77,7 +77,7 @@ typedef struct fi_options {
     int tau_mode;          /* FI_TAU_*; default FI_TAU_AUTO */
     int tau_split;         /* -1: per-class choice (AUTO calibrates); q >= 0: classes
                               with U = 2^q' >= 2^q use FFT, smaller ones DIRECT */
-    int record;            /* 1: keep every layer's mixer output y^l_n (tests) */
+    int record;            /* 1: keep every layer's input and mixer output (tests) */
     int use_graphs;        /* 1 (default): fi_generate replays captured hipGraphs */
     int block_graph_log2;  /* k: a block graph replays the 2^k - 1 positions between
                               multiples of 2^k (default 6; 0 disables) */
@@ -170,9 +170,9 @@ fi_status fi_debug_schedule(const fi_ctx *ctx, int64_t n, int *q, int *path);
  * at least P entries; any pointer may be NULL. */
 fi_status fi_tau_table(const fi_ctx *ctx, int *path, double *us_direct, double *us_fft);
 
-/* Copy positions 1..count of one layer's rows into dst (device fp32,
- * [B][D][count]):  what = 0: the layer inputs x^l_s (valid for s <= position);
- * what = 1: the mixer outputs y^l_s (needs record = 1). */
+/* Copy positions 1..count of one layer into dst (device fp32, [count][B][D]):
+ * what = 0: the layer inputs x^l_s, what = 1: the mixer outputs y^l_s (valid
+ * for s <= position).  Needs record = 1 (FI_ESTATE otherwise). */
 fi_status fi_history(const fi_ctx *ctx, int layer, int what, int64_t count, float *dst);
 
 /* Device wall-clock stamps (100 MHz counter ticks) written when each position

@@ -28,6 +28,8 @@ constexpr int kMaxLdsFftLog = 14;  // largest transform held in one workgroup's 
 constexpr int kMinSubLog = 12;     // smallest sub-block width a split block may use
 constexpr int kMaxLayers = 64;
 constexpr int kMaxP = 24;
+constexpr int kRing = 512;        // ring slots: pending sums reach at most W/2 = 256 ahead
+constexpr int kHeadTaps = 256;    // taps h[0..255] serve direct blocks up to U = 128
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -45,7 +47,9 @@ int ctz64(int64_t n) {
 }
 
 struct Layout {
-    size_t filt = 0, buf = 0, rec = 0, twid = 0, xin = 0, ylast = 0, stamps = 0, state = 0, scratch = 0;
+    size_t filt = 0, hh = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
+           stamps = 0, state = 0, scratch = 0;
+    int HK = 0;
     size_t spec[kMaxP] = {0};
     size_t total = 0;
     int logNT = 0;
@@ -75,9 +79,14 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
         return o2;
     };
     const size_t rowsMD = (size_t)M * D, rowsMBD = (size_t)M * B * D;
+    lay.HK = (int)std::min<int64_t>(kHeadTaps, L);
     lay.filt = take(rowsMD * L * sizeof(float));
+    lay.hh = take(rowsMD * lay.HK * sizeof(float));
     lay.buf = take(rowsMBD * L * sizeof(float));
-    lay.rec = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
+    lay.xr = take((size_t)kRing * rowsMBD * sizeof(float));
+    lay.ar = take((size_t)kRing * rowsMBD * sizeof(float));
+    lay.recx = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
+    lay.recy = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
     for (int q = 0; q < P; ++q) lay.spec[q] = fft_exists(q, P) ? take(rowsMD * spec_row_f4(q, vlog) * 16) : 0;
     // forward sub-block spectra of the widest split class: [M*B*D][U/2] float4
     lay.scratch = (P - 1 > vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
@@ -112,6 +121,7 @@ struct fi_ctx {
     int mode = 0;  // 0 fresh, 1 tiled, 2 lazy
     bool poisoned = false;
     std::string err;
+    int qd = 0;  // first block-size class computed by FFT (classes below are direct)
     hipGraphExec_t gclass[kMaxP + 1] = {nullptr};
     hipGraphExec_t gblock = nullptr;
     int block_log = 0;
@@ -141,28 +151,36 @@ fi_status fail(fi_ctx *c, fi_status s, const std::string &msg) {
 
 // ---- kernel dispatch over compile-time block sizes -------------------------
 
-int direct_ch(int M, int U) { return std::max(1, 256 / (M * U)); }
-size_t direct_lds(int M, int CH, int U) { return (size_t)M * CH * (4 * U + 1) * sizeof(float); }
+// Layers per block of a direct position: enough blocks to spread the U x U
+// products, few enough that the red cells are not recomputed needlessly.
+int direct_lg(int M, int U) {
+    const int lg = U <= 2 ? M : U == 4 ? 6 : U == 8 ? 3 : U == 16 ? 2 : 1;
+    return std::min(M, lg);
+}
+// inputs (U) + taps (2U-1) + pending outputs (U) per layer and lane
+size_t direct_lds(int LG, int U) { return U > 0 ? (size_t)LG * (4 * U - 1) * 64 * sizeof(float) : 0; }
+size_t ring_lds(int LG, int G) { return (size_t)LG * G * 65 * sizeof(float); }
 
 template <int U, bool CHAIN>
-hipError_t launch_direct_u(fi_ctx *c, hipStream_t s, const float *xext, float *yext, int advance) {
-    const int CH = direct_ch(c->M, U);
-    const int grid = (c->B * c->D + CH - 1) / CH;
-    hipLaunchKernelGGL((k_step_direct<U, CHAIN>), dim3(grid), dim3(256), direct_lds(c->M, CH, U), s,
-                       c->dev, CH, xext, yext, advance);
+hipError_t launch_direct_u(fi_ctx *c, int rd, hipStream_t s, const float *xext, float *yext, int advance,
+                           int rowx) {
+    const int LG = direct_lg(c->M, U);
+    const dim3 grid((c->B * c->D + 63) / 64, (c->M + LG - 1) / LG);
+    hipLaunchKernelGGL((k_direct<U, CHAIN>), grid, dim3(256), direct_lds(LG, U), s, c->dev, rd, LG, xext, yext,
+                       advance, rowx);
     return hipGetLastError();
 }
 
 template <int U, bool CHAIN>
 hipError_t allow_direct_lds_u(fi_ctx *c) {
-    const size_t bytes = direct_lds(c->M, direct_ch(c->M, U), U);
-    return hipFuncSetAttribute((const void *)k_step_direct<U, CHAIN>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    const size_t bytes = std::max<size_t>(direct_lds(direct_lg(c->M, U), U), 1);
+    return hipFuncSetAttribute((const void *)k_direct<U, CHAIN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
 }
 
 template <bool CHAIN>
 hipError_t allow_direct_lds(fi_ctx *c) {
-    hipError_t e = hipSuccess;
+    hipError_t e = allow_direct_lds_u<0, CHAIN>(c);
     if (e == hipSuccess) e = allow_direct_lds_u<1, CHAIN>(c);
     if (e == hipSuccess) e = allow_direct_lds_u<2, CHAIN>(c);
     if (e == hipSuccess) e = allow_direct_lds_u<4, CHAIN>(c);
@@ -171,30 +189,52 @@ hipError_t allow_direct_lds(fi_ctx *c) {
     if (e == hipSuccess) e = allow_direct_lds_u<32, CHAIN>(c);
     if (e == hipSuccess) e = allow_direct_lds_u<64, CHAIN>(c);
     if (e == hipSuccess) e = allow_direct_lds_u<128, CHAIN>(c);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_red_fft<CHAIN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)ring_lds(1, kRing / 2));
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_drain, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)ring_lds(1, kRing / 2));
     return e;
 }
 
+// q < 0: red cells only (the last position).  rd = (n-1)&1 for position n.
 template <bool CHAIN>
-hipError_t launch_direct(fi_ctx *c, int q, hipStream_t s, const float *xext, float *yext, int advance) {
+hipError_t launch_direct(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext, int advance,
+                         int rowx = 0) {
     switch (q) {
-        case 0: return launch_direct_u<1, CHAIN>(c, s, xext, yext, advance);
-        case 1: return launch_direct_u<2, CHAIN>(c, s, xext, yext, advance);
-        case 2: return launch_direct_u<4, CHAIN>(c, s, xext, yext, advance);
-        case 3: return launch_direct_u<8, CHAIN>(c, s, xext, yext, advance);
-        case 4: return launch_direct_u<16, CHAIN>(c, s, xext, yext, advance);
-        case 5: return launch_direct_u<32, CHAIN>(c, s, xext, yext, advance);
-        case 6: return launch_direct_u<64, CHAIN>(c, s, xext, yext, advance);
-        case 7: return launch_direct_u<128, CHAIN>(c, s, xext, yext, advance);
+        case -1: return launch_direct_u<0, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 0: return launch_direct_u<1, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 1: return launch_direct_u<2, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 2: return launch_direct_u<4, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 3: return launch_direct_u<8, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 4: return launch_direct_u<16, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 5: return launch_direct_u<32, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 6: return launch_direct_u<64, CHAIN>(c, rd, s, xext, yext, advance, rowx);
+        case 7: return launch_direct_u<128, CHAIN>(c, rd, s, xext, yext, advance, rowx);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <bool CHAIN>
+hipError_t launch_red_fft(fi_ctx *c, int rd, hipStream_t s, const float *xext, float *yext) {
+    const dim3 grid((c->B * c->D + 63) / 64, c->M);
+    hipLaunchKernelGGL((k_red_fft<CHAIN>), grid, dim3(256), ring_lds(1, c->dev.G), s, c->dev, rd, 1, xext, yext);
+    return hipGetLastError();
+}
+
+hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
+    const dim3 grid((c->B * c->D + 63) / 64, c->M);
+    hipLaunchKernelGGL(k_drain, grid, dim3(256), (size_t)c->dev.G * 65 * sizeof(float), s, c->dev, rd, advance);
+    return hipGetLastError();
+}
+
 template <int LOGN>
-hipError_t launch_fft_n(fi_ctx *c, hipStream_t s, int advance) {
+hipError_t launch_fft_n(fi_ctx *c, int rd, hipStream_t s, int advance) {
     using S = FftShape<LOGN>;
     const long long tiles = (long long)c->M * c->B * c->D;
     const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_fft_tile<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev,
+    hipLaunchKernelGGL((k_fft_tile<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, rd,
                        (const float4 *)c->spec[LOGN], advance);
     return hipGetLastError();
 }
@@ -210,43 +250,43 @@ hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long go
 }
 
 template <int LOGV>
-hipError_t launch_fft_sub_v(fi_ctx *c, int q, hipStream_t s, int advance) {
+hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
     const int K = sub_k(q, LOGV);
     const unsigned grid = (unsigned)((long long)c->M * c->B * c->D * K);
-    hipLaunchKernelGGL((k_fft_sub_fwd<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev,
+    hipLaunchKernelGGL((k_fft_sub_fwd<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev, rd,
                        c->scratch, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_fft_sub_inv<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev,
+    hipLaunchKernelGGL((k_fft_sub_inv<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev, rd,
                        (const float4 *)c->scratch, (const float4 *)c->spec[q], K, advance);
     return hipGetLastError();
 }
 
-hipError_t launch_fft_sub(fi_ctx *c, int q, hipStream_t s, int advance) {
+hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
     switch (c->opt.fft_max_log2) {
-        case 12: return launch_fft_sub_v<12>(c, q, s, advance);
-        case 13: return launch_fft_sub_v<13>(c, q, s, advance);
-        case 14: return launch_fft_sub_v<14>(c, q, s, advance);
+        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance);
+        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance);
+        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_fft(fi_ctx *c, int q, hipStream_t s, int advance) {
-    if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, q, s, advance);
+hipError_t launch_fft(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
+    if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, rd, q, s, advance);
     switch (q) {
-        case 2: return launch_fft_n<2>(c, s, advance);
-        case 3: return launch_fft_n<3>(c, s, advance);
-        case 4: return launch_fft_n<4>(c, s, advance);
-        case 5: return launch_fft_n<5>(c, s, advance);
-        case 6: return launch_fft_n<6>(c, s, advance);
-        case 7: return launch_fft_n<7>(c, s, advance);
-        case 8: return launch_fft_n<8>(c, s, advance);
-        case 9: return launch_fft_n<9>(c, s, advance);
-        case 10: return launch_fft_n<10>(c, s, advance);
-        case 11: return launch_fft_n<11>(c, s, advance);
-        case 12: return launch_fft_n<12>(c, s, advance);
-        case 13: return launch_fft_n<13>(c, s, advance);
-        case 14: return launch_fft_n<14>(c, s, advance);
+        case 2: return launch_fft_n<2>(c, rd, s, advance);
+        case 3: return launch_fft_n<3>(c, rd, s, advance);
+        case 4: return launch_fft_n<4>(c, rd, s, advance);
+        case 5: return launch_fft_n<5>(c, rd, s, advance);
+        case 6: return launch_fft_n<6>(c, rd, s, advance);
+        case 7: return launch_fft_n<7>(c, rd, s, advance);
+        case 8: return launch_fft_n<8>(c, rd, s, advance);
+        case 9: return launch_fft_n<9>(c, rd, s, advance);
+        case 10: return launch_fft_n<10>(c, rd, s, advance);
+        case 11: return launch_fft_n<11>(c, rd, s, advance);
+        case 12: return launch_fft_n<12>(c, rd, s, advance);
+        case 13: return launch_fft_n<13>(c, rd, s, advance);
+        case 14: return launch_fft_n<14>(c, rd, s, advance);
         default: return hipErrorInvalidValue;
     }
 }
@@ -286,30 +326,32 @@ hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
     }
 }
 
-hipError_t launch_red(fi_ctx *c, hipStream_t s, const float *xext, float *yext, int advance) {
-    const int n = c->B * c->D;
-    hipLaunchKernelGGL(k_red, dim3((n + 255) / 256), dim3(256), 0, s, c->dev, xext, yext, advance);
-    return hipGetLastError();
+// All kernels of one position of class q (q == P: the last position, red cells only).
+//   direct class:  [red cells + direct gray block]
+//   FFT class:     [red cells + ring -> history copy] [FFT gray block] [drain]
+template <bool CHAIN>
+hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
+                             int advance) {
+    if (q >= c->P) return launch_direct<CHAIN>(c, rd, -1, s, xext, yext, advance);
+    if (q < c->qd) return launch_direct<CHAIN>(c, rd, q, s, xext, yext, advance);
+    hipError_t e = launch_red_fft<CHAIN>(c, rd, s, xext, yext);
+    if (e == hipSuccess) e = launch_fft(c, rd, q, s, 0);
+    if (e == hipSuccess) e = launch_drain(c, rd, s, advance);
+    return e;
 }
 
-// All kernels of one position of class q (q == P: the last position, red cells only).
-hipError_t launch_position(fi_ctx *c, int q, hipStream_t s, const float *xext, float *yext, int advance) {
-    if (q >= c->P) return launch_red(c, s, xext, yext, advance);
-    if (c->path[q] == FI_PATH_DIRECT) return launch_direct<true>(c, q, s, xext, yext, advance);
-    hipError_t e = launch_red(c, s, xext, yext, 0);
-    if (e != hipSuccess) return e;
-    return launch_fft(c, q, s, advance);
+hipError_t launch_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
+                           int advance) {
+    return launch_position_t<true>(c, rd, q, s, xext, yext, advance);
 }
 
 // Gray blocks only (external-block mode): the layer inputs at n are in place.
-hipError_t launch_tiles(fi_ctx *c, int q, hipStream_t s) {
-    if (q >= c->P) {
-        hipLaunchKernelGGL(k_finish, dim3(1), dim3(64), 0, s, c->dev);
-        return hipGetLastError();
-    }
-    if (c->path[q] == FI_PATH_DIRECT) return launch_direct<false>(c, q, s, nullptr, nullptr, 1);
-    return launch_fft(c, q, s, 1);
+hipError_t launch_tiles(fi_ctx *c, int rd, int q, hipStream_t s) {
+    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, 1);
 }
+
+// Parity slot read by the kernels of position n.
+int rd_of(int64_t n) { return (int)((n - 1) & 1); }
 
 int class_of(const fi_ctx *c, int64_t n) { return n < c->L ? ctz64(n) : c->P; }
 
@@ -321,7 +363,8 @@ fi_status check_usable(fi_ctx *c) {
 
 fi_status set_state_pos(fi_ctx *c, int64_t pos) {
     State st{};
-    st.pos = pos;
+    st.pos[pos & 1] = pos;
+    st.pos[(pos & 1) ^ 1] = pos - 1;
     HIPCK(c, hipMemcpyAsync(c->dev.st, &st, sizeof(State), hipMemcpyHostToDevice, c->stream));
     HIPCK(c, hipStreamSynchronize(c->stream));
     return FI_OK;
@@ -330,7 +373,12 @@ fi_status set_state_pos(fi_ctx *c, int64_t pos) {
 fi_status clear_state(fi_ctx *c) {
     const size_t rowsMBD = (size_t)c->M * c->B * c->D;
     HIPCK(c, hipMemsetAsync(c->dev.buf, 0, rowsMBD * c->L * sizeof(float), c->stream));
-    if (c->dev.rec) HIPCK(c, hipMemsetAsync(c->dev.rec, 0, rowsMBD * c->L * sizeof(float), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.xr, 0, (size_t)kRing * rowsMBD * sizeof(float), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.ar, 0, (size_t)kRing * rowsMBD * sizeof(float), c->stream));
+    if (c->dev.recx) {
+        HIPCK(c, hipMemsetAsync(c->dev.recx, 0, rowsMBD * c->L * sizeof(float), c->stream));
+        HIPCK(c, hipMemsetAsync(c->dev.recy, 0, rowsMBD * c->L * sizeof(float), c->stream));
+    }
     HIPCK(c, hipMemsetAsync(c->dev.xin, 0, 2 * (size_t)c->B * c->D * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.ylast, 0, (size_t)c->L * c->B * c->D * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.stamps, 0, (size_t)(c->L + 1) * sizeof(long long), c->stream));
@@ -360,10 +408,15 @@ fi_status time_class(fi_ctx *c, int q, double &us_direct, double &us_fft) {
         const bool direct = which == 0;
         if (direct && !direct_exists(q)) continue;
         if (!direct && !fft_exists(q, c->P)) continue;
+        // the FFT path is timed as if q were the first FFT class (copy/drain block G = U)
+        c->dev.G = 1 << q;
+        const int rd = rd_of(int64_t(1) << q);
         auto run = [&]() -> hipError_t {
-            if (direct) return launch_direct<true>(c, q, c->stream, nullptr, nullptr, 0);
-            hipError_t e = launch_red(c, c->stream, nullptr, nullptr, 0);
-            return e != hipSuccess ? e : launch_fft(c, q, c->stream, 0);
+            if (direct) return launch_direct<true>(c, rd, q, c->stream, nullptr, nullptr, 0);
+            hipError_t e = launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr);
+            if (e == hipSuccess) e = launch_fft(c, rd, q, c->stream, 0);
+            if (e == hipSuccess) e = launch_drain(c, rd, c->stream, 0);
+            return e;
         };
         for (int w = 0; w < 2; ++w) HIPCK(c, run());
         double total = 0.0;
@@ -383,12 +436,13 @@ fi_status time_class(fi_ctx *c, int q, double &us_direct, double &us_fft) {
     return FI_OK;
 }
 
-fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<int> &classes) {
+// Record the positions (class, parity slot) into one graph.
+fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<std::pair<int, int>> &positions) {
     hipGraph_t g = nullptr;
     HIPCK(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal));
     hipError_t err = hipSuccess;
-    for (int q : classes) {
-        err = launch_position(c, q, c->cap, nullptr, nullptr, 1);
+    for (const auto &qr : positions) {
+        err = launch_position(c, qr.second, qr.first, c->cap, nullptr, nullptr, 1);
         if (err != hipSuccess) break;
     }
     hipError_t e2 = hipStreamEndCapture(c->cap, &g);
@@ -401,15 +455,17 @@ fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<int> &classe
 }
 
 fi_status build_graphs(fi_ctx *c) {
+    // class q: n odd iff q == 0; the last position L is even
     for (int q = 0; q <= c->P; ++q) {
-        fi_status s = capture(c, &c->gclass[q], {q});
+        fi_status s = capture(c, &c->gclass[q], {{q, q == 0 ? 0 : 1}});
         if (s != FI_OK) return s;
     }
+    // positions m*2^k + j, j = 1 .. 2^k-1: class ctz(j), parity of j
     const int k = c->opt.block_graph_log2;
     if (k >= 1 && k < c->P) {
-        std::vector<int> cls;
-        for (int64_t j = 1; j < (int64_t(1) << k); ++j) cls.push_back(ctz64(j));
-        fi_status s = capture(c, &c->gblock, cls);
+        std::vector<std::pair<int, int>> pos;
+        for (int64_t j = 1; j < (int64_t(1) << k); ++j) pos.push_back({ctz64(j), rd_of(j)});
+        fi_status s = capture(c, &c->gblock, pos);
         if (s != FI_OK) return s;
         c->block_log = k;
     }
@@ -445,7 +501,8 @@ fi_status harvest_events(fi_ctx *c) {
 
 // One FFT-class position launched directly, its gray-block kernels bracketed
 // by events.
-fi_status launch_timed_position(fi_ctx *c, int q) {
+fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
+    const int rd = rd_of(n);
     constexpr size_t kPairs = 4096;
     if (c->ev.empty()) {
         c->ev.resize(2 * kPairs, nullptr);
@@ -458,10 +515,11 @@ fi_status launch_timed_position(fi_ctx *c, int q) {
     }
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
-    HIPCK(c, launch_red(c, c->stream, nullptr, nullptr, 0));
+    HIPCK(c, launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr));
     HIPCK(c, hipEventRecord(c->ev[2 * i], c->stream));
-    HIPCK(c, launch_fft(c, q, c->stream, 1));
+    HIPCK(c, launch_fft(c, rd, q, c->stream, 0));
     HIPCK(c, hipEventRecord(c->ev[2 * i + 1], c->stream));
+    HIPCK(c, launch_drain(c, rd, c->stream, 1));
     return FI_OK;
 }
 
@@ -549,8 +607,15 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
 
     Dev &d = c->dev;
     d.filt = (const float *)(c->ws + lay.filt);
+    d.hh = (const float *)(c->ws + lay.hh);
     d.buf = (float *)(c->ws + lay.buf);
-    d.rec = o.record ? (float *)(c->ws + lay.rec) : nullptr;
+    d.xr = (float *)(c->ws + lay.xr);
+    d.ar = (float *)(c->ws + lay.ar);
+    d.recx = o.record ? (float *)(c->ws + lay.recx) : nullptr;
+    d.recy = o.record ? (float *)(c->ws + lay.recy) : nullptr;
+    d.HK = lay.HK;
+    d.W = kRing;
+    d.G = 0;
     d.xin = (float *)(c->ws + lay.xin);
     d.ylast = (float *)(c->ws + lay.ylast);
     d.st = (State *)(c->ws + lay.state);
@@ -586,9 +651,15 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
             hipStreamSynchronize(c->stream) != hipSuccess)
             return bail(fail(c, FI_EDEVICE, "twiddle copy failed"));
     }
-    // the direct kernels size their LDS at launch (up to 131 KB for 64 layers)
+    // the direct and ring-copy kernels size their LDS at launch (up to 98 KB)
     if (allow_direct_lds<true>(c) != hipSuccess || allow_direct_lds<false>(c) != hipSuccess)
         return bail(fail(c, FI_EDEVICE, "direct kernel LDS attribute"));
+    {
+        const size_t nh = (size_t)layers * lay.HK * channels;
+        hipLaunchKernelGGL(k_heads, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, c->stream, c->dev,
+                           (float *)(c->ws + lay.hh));
+        if (hipGetLastError() != hipSuccess) return bail(fail(c, FI_EDEVICE, "filter heads"));
+    }
     if (clear_state(c) != FI_OK) return bail(FI_EDEVICE);
 
     // spectra of every class an FFT block may serve
@@ -597,26 +668,37 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         if (launch_spectrum(c, q, c->stream) != hipSuccess) return bail(fail(c, FI_EDEVICE, "spectrum launch"));
     }
 
-    // path table
-    for (int q = 0; q < c->P; ++q) {
-        const bool de = direct_exists(q), fe = fft_exists(q, c->P);
-        int pth = de ? FI_PATH_DIRECT : FI_PATH_FFT;
-        if (o.tau_mode == FI_TAU_DIRECT) pth = de ? FI_PATH_DIRECT : FI_PATH_FFT;
-        else if (o.tau_mode == FI_TAU_FFT) pth = fe ? FI_PATH_FFT : FI_PATH_DIRECT;
-        else if (o.tau_split >= 0) pth = (q >= o.tau_split && fe) || !de ? FI_PATH_FFT : FI_PATH_DIRECT;
-        c->path[q] = pth;
-    }
+    // Path table.  Blocks of edge 2^q with q < qd are direct, the rest FFT (direct
+    // blocks exist up to U = 128, so qd <= 8; FFT blocks from U = 4).  A single
+    // split keeps every FFT position a multiple of G = 2^qd, the ring-copy block.
+    int qd = std::min(c->P, kMaxDirectLog + 1);              // default: direct wherever it exists
+    if (o.tau_mode == FI_TAU_FFT) qd = std::min(c->P, kMinFftLog);
+    else if (o.tau_mode == FI_TAU_AUTO && o.tau_split >= 0)
+        qd = std::min(c->P, std::max(kMinFftLog, std::min(o.tau_split, kMaxDirectLog + 1)));
     if (o.tau_mode == FI_TAU_AUTO && o.tau_split < 0) {
-        for (int q = 0; q < c->P; ++q) {
-            if (!(direct_exists(q) && fft_exists(q, c->P))) continue;
+        // time both paths per class at the real shape, then pick the split that
+        // minimises the whole run: class q runs 2^(P-1-q) times
+        for (int q = kMinFftLog; q <= std::min(kMaxDirectLog, c->P - 1); ++q) {
             double ud, uf;
             if (time_class(c, q, ud, uf) != FI_OK) return bail(FI_EDEVICE);
             c->us_direct[q] = ud;
             c->us_fft[q] = uf;
-            c->path[q] = (uf >= 0 && uf < ud) ? FI_PATH_FFT : FI_PATH_DIRECT;
+        }
+        double best = -1.0;
+        for (int cand = kMinFftLog; cand <= std::min(kMaxDirectLog + 1, c->P); ++cand) {
+            double cost = 0.0;
+            for (int q = kMinFftLog; q <= std::min(kMaxDirectLog, c->P - 1); ++q)
+                cost += std::ldexp(q < cand ? c->us_direct[q] : c->us_fft[q], c->P - 1 - q);
+            if (best < 0 || cost < best) {
+                best = cost;
+                qd = cand;
+            }
         }
         if (clear_state(c) != FI_OK) return bail(FI_EDEVICE);
     }
+    c->qd = qd;
+    for (int q = 0; q < c->P; ++q) c->path[q] = q < qd ? FI_PATH_DIRECT : FI_PATH_FFT;
+    c->dev.G = qd < c->P ? (1 << qd) : 0;
     if (o.use_graphs && o.map != FI_MAP_EXTERNAL) {
         if (build_graphs(c) != FI_OK) return bail(FI_EDEVICE);
     }
@@ -663,7 +745,7 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const int64_t n = c->pos + 1;
-    HIPCK(c, launch_position(c, class_of(c, n), c->stream, x_t, y_t, 1));
+    HIPCK(c, launch_position(c, rd_of(n), class_of(c, n), c->stream, x_t, y_t, 1));
     c->pos = n;
     return FI_OK;
 }
@@ -700,12 +782,12 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
         }
         const int q = class_of(c, n);
         if (c->opt.time_blocks && q < c->P && c->path[q] == FI_PATH_FFT) {
-            s = launch_timed_position(c, q);
+            s = launch_timed_position(c, n, q);
             if (s != FI_OK) return s;
         } else if (graphs) {
             HIPCK(c, hipGraphLaunch(c->gclass[q], c->stream));
         } else {
-            HIPCK(c, launch_position(c, q, c->stream, nullptr, nullptr, 1));
+            HIPCK(c, launch_position(c, rd_of(n), q, c->stream, nullptr, nullptr, 1));
         }
         c->pos = n;
     }
@@ -741,11 +823,12 @@ fi_status fi_history(const fi_ctx *cc, int layer, int what, int64_t count, float
     if (s != FI_OK) return s;
     if (layer < 0 || layer >= c->M || count < 0 || count > c->L || !dst || what < 0 || what > 1)
         return FI_EINVAL;
-    if (what == 1 && !c->dev.rec) return fail(c, FI_ESTATE, "outputs are recorded only with record = 1");
+    if (!c->dev.recx) return fail(c, FI_ESTATE, "histories are recorded only with record = 1");
     if (count == 0) return FI_OK;
-    const float *src = (what == 0 ? c->dev.buf : c->dev.rec) + (size_t)layer * c->B * c->D * c->L;
-    HIPCK(c, hipMemcpy2DAsync(dst, count * sizeof(float), src, c->L * sizeof(float), count * sizeof(float),
-                              (size_t)c->B * c->D, hipMemcpyDeviceToDevice, c->stream));
+    const size_t BD = (size_t)c->B * c->D;
+    const float *src = (what == 0 ? c->dev.recx : c->dev.recy) + (size_t)layer * BD;
+    HIPCK(c, hipMemcpy2DAsync(dst, BD * sizeof(float), src, (size_t)c->M * BD * sizeof(float), BD * sizeof(float),
+                              (size_t)count, hipMemcpyDeviceToDevice, c->stream));
     return FI_OK;
 }
 
@@ -766,7 +849,8 @@ fi_status fi_layer_red(fi_ctx *c, int layer, const float *q, float *y) {
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const int n = c->B * c->D;
-    hipLaunchKernelGGL(k_red_layer, dim3((n + 255) / 256), dim3(256), 0, c->stream, c->dev, layer, q, y);
+    hipLaunchKernelGGL(k_red_layer, dim3((n + 255) / 256), dim3(256), 0, c->stream, c->dev, rd_of(c->pos + 1),
+                       layer, q, y);
     HIPCK(c, hipGetLastError());
     return FI_OK;
 }
@@ -777,7 +861,7 @@ fi_status fi_tiles(fi_ctx *c) {
     if (c->opt.map != FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_tiles needs FI_MAP_EXTERNAL");
     if (c->pos >= c->L) return FI_ERANGE;
     const int64_t n = c->pos + 1;
-    HIPCK(c, launch_tiles(c, class_of(c, n), c->stream));
+    HIPCK(c, launch_tiles(c, rd_of(n), class_of(c, n), c->stream));
     c->pos = n;
     return FI_OK;
 }
@@ -789,9 +873,11 @@ fi_status fi_lazy_step(fi_ctx *c, const float *x_t, float *y_t) {
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 2)) != FI_OK) return s;
     const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
-    hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev);
+    const int rd = rd_of(c->pos + 1);
+    hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev, rd);
     HIPCK(c, hipGetLastError());
-    HIPCK(c, launch_red(c, c->stream, x_t, y_t, 1));
+    // red cells; the inputs also go to the row-major history the next sums read
+    HIPCK(c, launch_direct<true>(c, rd, -1, c->stream, x_t, y_t, 1, 1));
     c->pos += 1;
     return FI_OK;
 }
@@ -822,10 +908,11 @@ fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
     hipEvent_t a, b;
     HIPCK(c, hipEventCreate(&a));
     HIPCK(c, hipEventCreate(&b));
+    const int rd = rd_of(n);
     auto once = [&]() -> hipError_t {
-        hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev);
+        hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev, rd);
         hipError_t e = hipGetLastError();
-        return e != hipSuccess ? e : launch_red(c, c->stream, nullptr, nullptr, 0);
+        return e != hipSuccess ? e : launch_direct<true>(c, rd, -1, c->stream, nullptr, nullptr, 0, 1);
     };
     HIPCK(c, once());  // warm-up
     HIPCK(c, hipEventRecord(a, c->stream));

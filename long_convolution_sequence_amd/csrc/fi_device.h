@@ -1,13 +1,18 @@
 // Device-side state and helpers shared by every kernel of the library.
 //
 // Data layout in HBM (fp32 unless noted; M layers, B batch rows, D channels,
-// L positions, positions 1-based, slot t = position - 1):
-//   filt  [M][D][L]      filter taps h^l[c][k]
-//   buf   [M][B][D][L]   activation rows: slot t holds the layer input x^l_{t+1}
-//                        once position t+1 is produced, and the pending sum
-//                        for position t+1 before that (activation reuse from
-//                        Flash Inference's "Speicheroptimierung")
-//   rec   [M][B][D][L]   optional record of every mixer output y^l
+// L positions, positions 1-based, "row" r = (l*B + b)*D + c, "chain" = b*D + c):
+//   filt  [M][D][L]      filter taps h^l[c][k] (spectra, Lazy baseline)
+//   hh    [M][HK][D]     filter heads h^l[c][0..HK-1], channel innermost (red
+//                        cells and direct gray blocks: coalesced over channels)
+//   xr    [W][M][B][D]   ring of recent layer inputs x^l_p, slot p mod W
+//   ar    [W][M][B][D]   ring of pending sums for positions p in (n, n+W/2]
+//   buf   [M][B][D][L]   row-major history: the inputs of every position up to
+//                        the last FFT position (copied from the ring in blocks
+//                        of G), and the FFT gray blocks' pending sums for later
+//                        positions until they are drained into the ring
+//                        (activation reuse, Flash Inference "Speicheroptimierung")
+//   recx, recy [L][M][B][D]  optional record of every layer input and output
 //   xin   [2][B][D]      next layer-0 input, double-buffered by position parity
 //   ylast [L][B][D]      last layer's mixer output per position
 //   stamps[L+1] (i64)    device wall clock at the end of each position
@@ -18,16 +23,21 @@
 
 namespace fi {
 
+// Positions produced so far, in two slots by parity: the kernels of position
+// n read slot (n-1)&1 (holding n-1) and the last kernel of position n writes n
+// into slot n&1, so no kernel ever reads the slot it may be overwriting.
 struct State {
-    long long pos;      // positions produced so far
-    unsigned done;      // workgroups finished in the current kernel (last-block pattern)
-    unsigned pad;
+    long long pos[2];
 };
 
 struct Dev {
     const float *filt;
+    const float *hh;
     float *buf;
-    float *rec;
+    float *xr;
+    float *ar;
+    float *recx;
+    float *recy;
     float *xin;
     float *ylast;
     State *st;
@@ -36,9 +46,20 @@ struct Dev {
     int M, B, D;
     int logNT;
     long long L;
+    int HK;    // filter-head taps kept per (l, c)
+    int W;     // ring slots (power of two)
+    int G;     // copy/drain block between ring and row-major history
     int map;   // 0 tanh, 1 identity, 2 external
     int fb;    // 0 tanh, 1 identity
 };
+
+// Ring entry of (position pos, layer l, chain 0): add the chain index.
+__device__ __forceinline__ size_t ring(const Dev &p, long long pos, int l) {
+    return ((size_t)(pos & (p.W - 1)) * p.M + l) * (size_t)(p.B * p.D);
+}
+__device__ __forceinline__ size_t head(const Dev &p, int l, int k, int c) {
+    return ((size_t)l * p.HK + k) * p.D + c;
+}
 
 __device__ __forceinline__ float apply_map(int kind, float y) { return kind == 0 ? tanhf(y) : y; }
 
@@ -49,20 +70,40 @@ __device__ __forceinline__ size_t filt_row(const Dev &p, int l, int c) {
     return ((size_t)l * p.D + c) * (size_t)p.L;
 }
 
-// End of the last kernel of a position: the last workgroup to finish stamps
-// the device clock and publishes the new position.  No memory fence is needed:
-// every workgroup read the position when it started, before it counts itself
-// done, and the next kernel (same stream) sees the new position and all of
-// this kernel's stores through the kernel boundary.
+// Position of the kernel: slot rd = (n-1)&1 holds n-1 (rd is a launch argument
+// fixed when a position's launches are recorded, so graphs can replay them).
+__device__ __forceinline__ long long position_of(const Dev &p, int rd) { return p.st->pos[rd] + 1; }
+
+// End of the last kernel of position n: block 0 publishes n (into the other
+// parity slot, which no kernel of this position reads) and stamps the device
+// clock.  The next kernel on the stream sees the new value through the kernel
+// boundary.  The stamp is block 0's end, within a block's run time of the
+// kernel's end.
 __device__ __forceinline__ void finish_position(const Dev &p, long long n, int advance) {
     if (!advance) return;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&p.st->done, 1u);
-        if (prev == gridDim.x - 1) {
-            p.stamps[n] = (long long)wall_clock64();
-            p.st->done = 0;
-            p.st->pos = n;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        p.stamps[n] = (long long)wall_clock64();
+        p.st->pos[n & 1] = n;
+    }
+}
+
+// Copy helper: every thread of the block moves elements tid, tid+bs, ... of a
+// strided index space; loads are issued in batches of 16 before any store, so a
+// copy costs a few memory round trips instead of one per element.
+template <typename Load, typename Store>
+__device__ __forceinline__ void batched_copy(int total, int tid, int bs, Load ld, Store st) {
+    constexpr int BATCH = 16;
+    for (int base = tid; base < total; base += BATCH * bs) {
+        float v[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int i = base + k * bs;
+            if (i < total) v[k] = ld(i);
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int i = base + k * bs;
+            if (i < total) st(i, v[k]);
         }
     }
 }

@@ -13,164 +13,251 @@
 
 namespace fi {
 
-// ---------------------------------------------------------------------------
-// Red cells of one (b, c) chain through all layers at position n.
-// Reads the pending sums, writes the layer inputs into their slots (the slot
-// of position n switches from "pending sum" to "input"), the recorded y, the
-// last output and the next feedback input.  xs (optional) receives x^l_n.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float chain_input(const Dev &p, long long n, int chain, const float *xext) {
-    const int BD = p.B * p.D;
-    return xext ? xext[chain] : p.xin[(size_t)(n & 1) * BD + chain];
-}
+constexpr int kLanes = 64;  // chains per block: one per lane, so every access is coalesced
 
+// ---------------------------------------------------------------------------
+// Red cells of one (b, c) chain at position n, layers 0..l1-1, from the ring.
+// The pending sum for (l, n) is final when position n starts; y^l_n adds the
+// own-position term h^l[c][0] x^l_n and x^{l+1}_n = map(y^l_n).  Only layers
+// l >= l0 are "owned" by the caller: their inputs go to the ring (and to xs,
+// the caller's LDS copy, at stride xs_stride), the records, and (rowx) the
+// row-major history.  The owner of the last layer also writes the output and
+// the next feedback input.
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ void chain_output(const Dev &p, long long n, int chain, float ylast, float *yext) {
     const int BD = p.B * p.D;
-    const long long t = n - 1;
-    p.ylast[(size_t)t * BD + chain] = ylast;
+    p.ylast[(size_t)(n - 1) * BD + chain] = ylast;
     if (yext) yext[chain] = ylast;
     p.xin[(size_t)((n + 1) & 1) * BD + chain] = apply_map(p.fb, ylast);
 }
 
-// Red cells for every chain; one thread per (b, c).  `advance` is set when no
-// other kernel of this position follows.
-__global__ void __launch_bounds__(256) k_red(Dev p, const float *xext, float *yext, int advance) {
-    const long long n = p.st->pos + 1;
-    const long long t = n - 1;
-    if (n > p.L) return;  // uniform: never touch memory past position L
-    const int chain = blockIdx.x * blockDim.x + threadIdx.x;
-    if (chain < p.B * p.D) {
-        const int b = chain / p.D, c = chain % p.D;
-        float x = chain_input(p, n, chain, xext);
-        float y = 0.f;
-        constexpr int CHUNK = 16;
-        for (int l0 = 0; l0 < p.M; l0 += CHUNK) {
-            float pend[CHUNK], h0[CHUNK];
+__device__ __forceinline__ void run_chain(const Dev &p, long long n, int chain, int l0, int l1,
+                                          const float *xext, float *yext, float *xs, int xs_stride, bool rowx) {
+    const int BD = p.B * p.D;
+    const int b = chain / p.D, c = chain % p.D;
+    float x = xext ? xext[chain] : p.xin[(size_t)(n & 1) * BD + chain];
+    float y = 0.f;
+    constexpr int CHUNK = 24;
+    for (int lb = 0; lb < l1; lb += CHUNK) {
+        float pend[CHUNK], h0[CHUNK];
 #pragma unroll
-            for (int i = 0; i < CHUNK; ++i) {
-                if (l0 + i < p.M) {
-                    pend[i] = p.buf[act_row(p, l0 + i, b, c) + t];
-                    h0[i] = p.filt[filt_row(p, l0 + i, c)];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < CHUNK; ++i) {
-                if (l0 + i < p.M) {
-                    const int l = l0 + i;
-                    const size_t r = act_row(p, l, b, c) + t;
-                    y = fmaf(h0[i], x, pend[i]);
-                    p.buf[r] = x;
-                    if (p.rec) p.rec[r] = y;
-                    x = apply_map(p.map, y);
-                }
+        for (int i = 0; i < CHUNK; ++i) {
+            if (lb + i < l1) {
+                pend[i] = p.ar[ring(p, n, lb + i) + chain];
+                h0[i] = p.hh[head(p, lb + i, 0, c)];
             }
         }
-        chain_output(p, n, chain, y, yext);
+#pragma unroll
+        for (int i = 0; i < CHUNK; ++i) {
+            const int l = lb + i;
+            if (l < l1) {
+                y = fmaf(h0[i], x, pend[i]);
+                if (l >= l0) {
+                    p.xr[ring(p, n, l) + chain] = x;
+                    if (xs) xs[(l - l0) * xs_stride] = x;
+                    if (p.recx) {
+                        const size_t r = ((size_t)(n - 1) * p.M + l) * BD + chain;
+                        p.recx[r] = x;
+                        p.recy[r] = y;
+                    }
+                    if (rowx) p.buf[act_row(p, l, b, c) + (n - 1)] = x;
+                }
+                x = apply_map(p.map, y);
+            }
+        }
+    }
+    if (l1 == p.M) chain_output(p, n, chain, y, yext);
+}
+
+// The ring slot of position n + W/2 is reused by that position: clear it for
+// the owned layers.  Nothing reads or adds to it during position n (pending
+// sums only ever target positions n+1 .. n+W/2-1 before the drain, which runs
+// after this kernel).
+__device__ __forceinline__ void clear_ahead(const Dev &p, long long n, int chain, int l0, int l1, int wave,
+                                            int waves) {
+    for (int l = l0 + wave; l < l1; l += waves) p.ar[ring(p, n + p.W / 2, l) + chain] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// One position whose gray block (edge U) is computed directly, fused with the
+// red cells.  Block = 64 chains (lanes) x 4 waves, grid = chain blocks x layer
+// groups of LG layers.  Each block recomputes the red cells of its chains up to
+// its last layer (cheap, and no other block can be waited on) but writes only
+// its own layers.  The gray block is a U x U Toeplitz product per chain:
+//   pending(n+1+j) += sum_k h[j+U-k] x_{n-U+1+k},  j, k in [0, U)
+// with inputs and taps staged in LDS and a sliding register window of J taps.
+// U = 0: red cells only (the last position).  CHAIN = false: the layer inputs
+// at n are already in the ring (external block mode).
+// ---------------------------------------------------------------------------
+template <int U, bool CHAIN>
+__global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const float *xext, float *yext,
+                                                int advance, int rowx) {
+    extern __shared__ float sm[];
+    const long long n = position_of(p, rd);
+    if (n > p.L) return;  // uniform guards: never touch memory past position L
+    if constexpr (U > 0) {
+        if (n % U != 0 || n + U > p.L) return;
+    }
+    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
+    const int BD = p.B * p.D;
+    const int cb = blockIdx.x * kLanes;
+    const int chain = cb + lane;
+    const bool live = chain < BD;
+    const int l0 = blockIdx.y * LG, l1 = min(p.M, l0 + LG), nl = l1 - l0;
+    if constexpr (U == 0) {
+        if (wave == 0 && CHAIN && live) run_chain(p, n, chain, l0, l1, xext, yext, nullptr, 0, rowx != 0);
+        if (live) clear_ahead(p, n, chain, l0, l1, wave, blockDim.x / kLanes);
+    } else {
+        constexpr int TAPS = 2 * U - 1;
+        float *xw = sm;                               // [LG][U][64]: inputs at n-U+1 .. n
+        float *tp = xw + (size_t)LG * U * kLanes;     // [LG][2U-1][64]: taps h[1 .. 2U-1]
+        float *aw = tp + (size_t)LG * TAPS * kLanes;  // [LG][U][64]: pending sums at n+1 .. n+U
+        if (wave == 0) {
+            // wave 0: the red cells (its loads are the first it issues)
+            if (CHAIN && live)
+                run_chain(p, n, chain, l0, l1, xext, yext, xw + (U - 1) * kLanes + lane, U * kLanes, rowx != 0);
+        } else {
+            // waves 1..: stage the input window, the taps and the pending outputs
+            const int t2 = threadIdx.x - kLanes, b2 = blockDim.x - kLanes;
+            constexpr int KW = CHAIN ? U - 1 : U;     // window entries taken from the ring
+            batched_copy(nl * KW * kLanes, t2, b2,
+                [&](int i) {
+                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                    return cb + ln < BD ? p.xr[ring(p, n - U + 1 + k, l0 + li) + cb + ln] : 0.f;
+                },
+                [&](int i, float v) {
+                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                    xw[(li * U + k) * kLanes + ln] = v;
+                });
+            batched_copy(nl * TAPS * kLanes, t2, b2,
+                [&](int i) {
+                    const int ln = i & (kLanes - 1), m = (i / kLanes) % TAPS, li = (i / kLanes) / TAPS;
+                    return cb + ln < BD ? p.hh[head(p, l0 + li, 1 + m, (cb + ln) % p.D)] : 0.f;
+                },
+                [&](int i, float v) { tp[i] = v; });
+            batched_copy(nl * U * kLanes, t2, b2,
+                [&](int i) {
+                    const int ln = i & (kLanes - 1), j = (i / kLanes) % U, li = (i / kLanes) / U;
+                    return cb + ln < BD ? p.ar[ring(p, n + 1 + j, l0 + li) + cb + ln] : 0.f;
+                },
+                [&](int i, float v) { aw[i] = v; });
+            if (live) clear_ahead(p, n, chain, l0, l1, wave - 1, blockDim.x / kLanes - 1);
+        }
+        __syncthreads();
+        constexpr int J = U < 8 ? U : 8;              // outputs per task
+        constexpr int NJ = U / J;
+        if (live) {
+            for (int task = wave; task < nl * NJ; task += blockDim.x / kLanes) {
+                const int li = task / NJ, j0 = (task % NJ) * J;
+                const float *x = xw + (size_t)li * U * kLanes + lane;
+                const float *h = tp + (size_t)li * TAPS * kLanes + lane;   // h[m*64] = tap m+1
+                const float *a = aw + (size_t)li * U * kLanes + lane;
+                float acc[J], hw[J];
+#pragma unroll
+                for (int jj = 0; jj < J; ++jj) {
+                    acc[jj] = a[(j0 + jj) * kLanes];
+                    hw[jj] = h[(j0 + jj + U - 1) * kLanes];                // tap index for k = 0
+                }
+#pragma unroll
+                for (int k = 0; k < U; ++k) {
+                    const float xv = x[k * kLanes];
+#pragma unroll
+                    for (int jj = 0; jj < J; ++jj) acc[jj] = fmaf(hw[jj], xv, acc[jj]);
+                    if (k + 1 < U) {                                        // slide: tap index - 1
+#pragma unroll
+                        for (int jj = J - 1; jj > 0; --jj) hw[jj] = hw[jj - 1];
+                        hw[0] = h[(j0 + U - k - 2) * kLanes];
+                    }
+                }
+#pragma unroll
+                for (int jj = 0; jj < J; ++jj) p.ar[ring(p, n + 1 + j0 + jj, l0 + li) + chain] = acc[jj];
+            }
+        }
     }
     finish_position(p, n, advance);
 }
 
 // ---------------------------------------------------------------------------
-// One position whose gray block is computed directly, fused with the red
-// cells: a workgroup owns CH whole chains (all layers), so the slot written by
-// a red cell is read by tiles of the same workgroup only.
-//   phase 0: every thread prefetches pending sums, h0, the input window,
-//            the taps h[1..2U-1] and the U pending outputs into LDS;
-//   phase 1: one thread per chain runs the red cells through the layers;
-//   phase 2: one thread per output adds the U-term dot product.
-// CHAIN = false: the layer inputs at n are already in their slots (external
-// block mode); phase 1 is skipped.
+// First kernel of a position with an FFT gray block (n a multiple of G): the
+// red cells, then the inputs of positions n-G+1 .. n of every owned row are
+// copied from the ring into the row-major history (through an LDS transpose so
+// both sides are coalesced).  CHAIN = false: external block mode.
 // ---------------------------------------------------------------------------
-template <int U, bool CHAIN>
-__global__ void __launch_bounds__(256) k_step_direct(Dev p, int CH, const float *xext, float *yext,
-                                                     int advance) {
-    extern __shared__ float sm[];
-    const int M = p.M;
-    const int items = M * CH;
-    float *pend = sm;                    // [M*CH]
-    float *h0 = pend + items;            // [M*CH]
-    float *xw = h0 + items;              // [M*CH][U]   inputs at n-U+1..n
-    float *tp = xw + items * U;          // [M*CH][2U-1] taps h[1..2U-1]
-    float *aw = tp + items * (2 * U - 1);  // [M*CH][U] pending sums at n+1..n+U
-
-    const long long n = p.st->pos + 1;
-    const long long t = n - 1;
-    // uniform guard: a gray block of edge U exists only after multiples of U
-    // and ends at or before L; any other position is left untouched
-    if (n > p.L || n % U != 0 || n + U > p.L) return;
+template <bool CHAIN>
+__global__ void __launch_bounds__(256) k_red_fft(Dev p, int rd, int LG, const float *xext, float *yext) {
+    extern __shared__ float sm[];                 // [LG][G][65]
+    const long long n = position_of(p, rd);
+    const int G = p.G;
+    if (n > p.L || G < 1 || n % G != 0) return;  // uniform guard
+    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
     const int BD = p.B * p.D;
-    const int ch0 = blockIdx.x * CH;
-    const int nch = min(CH, BD - ch0);
-    const int tid = threadIdx.x, bs = blockDim.x;
-
-    for (int i = tid; i < items; i += bs) {
-        const int l = i / CH, k = i % CH;
-        if (k < nch) {
-            const int chain = ch0 + k, b = chain / p.D, c = chain % p.D;
-            if (CHAIN) pend[i] = p.buf[act_row(p, l, b, c) + t];
-            h0[i] = p.filt[filt_row(p, l, c)];
-        }
-    }
-    constexpr int XW = CHAIN ? U - 1 : U;  // window entries read from memory
-    if constexpr (XW > 0) {
-        for (int i = tid; i < items * XW; i += bs) {
-            const int lk = i / XW, kk = i % XW;
-            const int l = lk / CH, k = lk % CH;
-            if (k < nch) {
-                const int chain = ch0 + k, b = chain / p.D, c = chain % p.D;
-                xw[lk * U + kk] = p.buf[act_row(p, l, b, c) + t - (U - 1) + kk];
-            }
-        }
-    }
-    for (int i = tid; i < items * (2 * U - 1); i += bs) {
-        const int lk = i / (2 * U - 1), m = i % (2 * U - 1);
-        const int l = lk / CH, k = lk % CH;
-        if (k < nch) {
-            const int c = (ch0 + k) % p.D;
-            tp[i] = p.filt[filt_row(p, l, c) + 1 + m];
-        }
-    }
-    for (int i = tid; i < items * U; i += bs) {
-        const int lk = i / U, j = i % U;
-        const int l = lk / CH, k = lk % CH;
-        if (k < nch) {
-            const int chain = ch0 + k, b = chain / p.D, c = chain % p.D;
-            aw[i] = p.buf[act_row(p, l, b, c) + t + 1 + j];
-        }
+    const int cb = blockIdx.x * kLanes;
+    const int chain = cb + lane;
+    const bool live = chain < BD;
+    const int l0 = blockIdx.y * LG, l1 = min(p.M, l0 + LG), nl = l1 - l0;
+    constexpr int PAD = kLanes + 1;
+    if (wave == 0) {
+        if (CHAIN && live) run_chain(p, n, chain, l0, l1, xext, yext, sm + (G - 1) * PAD + lane, G * PAD, false);
+    } else {
+        const int KW = CHAIN ? G - 1 : G;
+        batched_copy(nl * KW * kLanes, threadIdx.x - kLanes, blockDim.x - kLanes,
+            [&](int i) {
+                const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                return cb + ln < BD ? p.xr[ring(p, n - G + 1 + k, l0 + li) + cb + ln] : 0.f;
+            },
+            [&](int i, float v) {
+                const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                sm[(li * G + k) * PAD + ln] = v;
+            });
+        if (live) clear_ahead(p, n, chain, l0, l1, wave - 1, blockDim.x / kLanes - 1);
     }
     __syncthreads();
-
-    if (CHAIN && tid < nch) {
-        const int chain = ch0 + tid, b = chain / p.D, c = chain % p.D;
-        float x = chain_input(p, n, chain, xext);
-        float y = 0.f;
-        for (int l = 0; l < M; ++l) {
-            const int i = l * CH + tid;
-            const size_t r = act_row(p, l, b, c) + t;
-            y = fmaf(h0[i], x, pend[i]);
-            p.buf[r] = x;
-            if (p.rec) p.rec[r] = y;
-            xw[i * U + (U - 1)] = x;
-            x = apply_map(p.map, y);
-        }
-        chain_output(p, n, chain, y, yext);
+    for (int i = threadIdx.x; i < nl * kLanes * G; i += blockDim.x) {
+        const int k = i % G, ln = (i / G) % kLanes, li = (i / G) / kLanes;
+        const int ch = cb + ln;
+        if (ch < BD) p.buf[act_row(p, l0 + li, ch / p.D, ch % p.D) + (n - G) + k] = sm[(li * G + k) * PAD + ln];
     }
+}
+
+// Last kernel of an FFT position: the FFT gray blocks' pending sums for
+// positions n+1 .. n+G are final (the next FFT block starts at n+G); add them
+// from the row-major history into the ring.  Grid = chain blocks x layers.
+__global__ void __launch_bounds__(256) k_drain(Dev p, int rd, int advance) {
+    extern __shared__ float sm[];                 // [G][65]
+    const long long n = position_of(p, rd);
+    const int G = p.G;
+    if (n > p.L || G < 1 || n % G != 0 || n + G > p.L) return;  // uniform guard
+    constexpr int PAD = kLanes + 1;
+    const int BD = p.B * p.D;
+    const int l = blockIdx.y;
+    const int cb = blockIdx.x * kLanes;
+    batched_copy(kLanes * G, threadIdx.x, blockDim.x,
+        [&](int i) {
+            const int k = i % G, ch = cb + i / G;
+            return ch < BD ? p.buf[act_row(p, l, ch / p.D, ch % p.D) + n + k] : 0.f;
+        },
+        [&](int i, float v) { sm[(i % G) * PAD + i / G] = v; });
     __syncthreads();
-
-    for (int i = tid; i < items * U; i += bs) {
-        const int lk = i / U, j = i % U;
-        const int l = lk / CH, k = lk % CH;
-        if (k < nch) {
-            const int chain = ch0 + k, b = chain / p.D, c = chain % p.D;
-            const float *x = xw + lk * U;
-            const float *h = tp + lk * (2 * U - 1) + j + U - 1;   // h[j+U-kk] = h[-kk]
-            float s = aw[i];
-#pragma unroll
-            for (int kk = 0; kk < U; ++kk) s = fmaf(h[-kk], x[kk], s);
-            p.buf[act_row(p, l, b, c) + t + 1 + j] = s;
-        }
-    }
+    // ring += staged sums: load a batch of ring entries, then store the sums
+    batched_copy(kLanes * G, threadIdx.x, blockDim.x,
+        [&](int i) {
+            const int ln = i & (kLanes - 1), k = i / kLanes;
+            return cb + ln < BD ? p.ar[ring(p, n + 1 + k, l) + cb + ln] + sm[k * PAD + ln] : 0.f;
+        },
+        [&](int i, float v) {
+            const int ln = i & (kLanes - 1), k = i / kLanes;
+            if (cb + ln < BD) p.ar[ring(p, n + 1 + k, l) + cb + ln] = v;
+        });
     finish_position(p, n, advance);
+}
+
+// Filter heads h^l[c][0..HK-1], channel innermost.
+__global__ void __launch_bounds__(256) k_heads(Dev p, float *hh) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)p.M * p.HK * p.D;
+    if (i >= total) return;
+    const int c = (int)(i % p.D), k = (int)((i / p.D) % p.HK), l = (int)(i / ((size_t)p.D * p.HK));
+    hh[i] = k < p.L ? p.filt[filt_row(p, l, c) + k] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -180,15 +267,15 @@ __global__ void __launch_bounds__(256) k_step_direct(Dev p, int CH, const float 
 //   spec: per (l, c), U/2 float4 in pair order (see k_spectrum), scaled by 1/U.
 // ---------------------------------------------------------------------------
 template <int LOGN>
-__global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, const float4 *__restrict__ spec,
+__global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec,
                                                                   int advance) {
     using S = FftShape<LOGN>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
     __shared__ float2 smem[S::LDS];
     const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
-    const long long n = p.st->pos + 1;
+    const long long n = position_of(p, rd);
     const long long t = n - 1;
-    if (n > p.L || n % N != 0 || n + N > p.L) return;  // uniform guard, as in k_step_direct
+    if (n > p.L || n % N != 0 || n + N > p.L) return;  // uniform guard, as in k_direct
     const long long ntiles = (long long)p.M * p.B * p.D;
     const long long tile = (long long)blockIdx.x * S::PER_BLOCK + team;
     const bool active = tile < ntiles;
@@ -211,12 +298,23 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, const f
     dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    // this thread's spectrum pairs, loaded together while the transform runs
+    constexpr int PAIRS = (N / 2 + TT - 1) / TT;
+    float4 gs[PAIRS];
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) {
+        const int j = lt + m * TT;
+        gs[m] = (active && j < N / 2) ? sp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
 
     // bins of the real transform times the filter spectrum, re-packed for the inverse
-    for (int j = lt; j < N / 2; j += TT) {
-        const float4 g = active ? sp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) {
+        const int j = lt + m * TT;
+        if (j >= N / 2) break;
+        const float4 g = gs[m];
         if (j == 0) {
             const float2 C0 = X[0];
             const float2 Ch = X[lpad(1)];
@@ -303,7 +401,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
 // sub-block i, stored in pair order in `scratch` ([tile][i][V/2] float4).
 // ---------------------------------------------------------------------------
 template <int LOGV>
-__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, float4 *__restrict__ scratch,
+__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int rd, float4 *__restrict__ scratch,
                                                                      int K) {
     using S = FftShape<LOGV>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
@@ -311,7 +409,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, floa
     __shared__ float2 smem[S::LDS];
     const int lt = threadIdx.x;
     const long long U = (long long)K * N;
-    const long long n = p.st->pos + 1;
+    const long long n = position_of(p, rd);
     const long long t = n - 1;
     if (n > p.L || n % U != 0 || n + U > p.L) return;  // uniform guard
     const long long tile = (long long)blockIdx.x / K;
@@ -348,7 +446,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, floa
 // k_fft_sub_inv: per (l, b, c, o), Z = sum_i A_i * G_{K+o-i}, then the inverse
 // transform and accumulation of its exact upper half into output sub-block o.
 template <int LOGV>
-__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, const float4 *__restrict__ scratch,
+__global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int rd, const float4 *__restrict__ scratch,
                                                                      const float4 *__restrict__ spec, int K,
                                                                      int advance) {
     using S = FftShape<LOGV>;
@@ -356,7 +454,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, cons
     __shared__ float2 smem[S::LDS];
     const int lt = threadIdx.x;
     const long long U = (long long)K * N;
-    const long long n = p.st->pos + 1;
+    const long long n = position_of(p, rd);
     const long long t = n - 1;
     if (n > p.L || n % U != 0 || n + U > p.L) return;  // uniform guard
     const long long tile = (long long)blockIdx.x / K;
@@ -371,31 +469,54 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, cons
     float2 acc[HALF0];
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
-    for (int j = lt; j < N / 2; j += TT) {
-        if (j == 0) {
-            float Z0 = 0.f, ZN = 0.f;
-            float2 Zh = make_float2(0.f, 0.f);
-            for (int i = 0; i < K; ++i) {
-                const float4 a = A[(size_t)i * (N / 2)];
-                const float4 g = G[(size_t)(K + o - i - 1) * (N / 2)];
-                Z0 = fmaf(a.x, g.x, Z0);
-                ZN = fmaf(a.y, g.y, ZN);
-                Zh = cadd(Zh, cmul(make_float2(a.z, a.w), make_float2(g.z, g.w)));
+    // Z = sum_i A_i * G_{K+o-i} for this thread's pairs, four pairs at a time,
+    // the 2x4 loads of each sub-block issued together
+    constexpr int PAIRS = (N / 2 + TT - 1) / TT;
+    static_assert(PAIRS % 4 == 0, "pairs per thread");
+    for (int m0 = 0; m0 < PAIRS; m0 += 4) {
+        float4 Z[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Z[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < K; ++i) {
+            const float4 *Ai = A + (size_t)i * (N / 2);
+            const float4 *Gi = G + (size_t)(K + o - i - 1) * (N / 2);
+            float4 a[4], g[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = lt + (m0 + m) * TT;
+                a[m] = Ai[j];
+                g[m] = Gi[j];
             }
-            X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
-            X[lpad(1)] = make_float2(Zh.x, -Zh.y);
-        } else {
-            float2 Z1 = make_float2(0.f, 0.f), Z2 = make_float2(0.f, 0.f);
-            for (int i = 0; i < K; ++i) {
-                const float4 a = A[(size_t)i * (N / 2) + j];
-                const float4 g = G[(size_t)(K + o - i - 1) * (N / 2) + j];
-                Z1 = cadd(Z1, cmul(make_float2(a.x, a.y), make_float2(g.x, g.y)));
-                Z2 = cadd(Z2, cmul(make_float2(a.z, a.w), make_float2(g.z, g.w)));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = lt + (m0 + m) * TT;
+                if (j == 0) {  // (G_0, G_N) real, G_{N/2} complex
+                    Z[m].x = fmaf(a[m].x, g[m].x, Z[m].x);
+                    Z[m].y = fmaf(a[m].y, g[m].y, Z[m].y);
+                    const float2 h = cmul(make_float2(a[m].z, a[m].w), make_float2(g[m].z, g[m].w));
+                    Z[m].z += h.x;
+                    Z[m].w += h.y;
+                } else {
+                    const float2 z1 = cmul(make_float2(a[m].x, a[m].y), make_float2(g[m].x, g[m].y));
+                    const float2 z2 = cmul(make_float2(a[m].z, a[m].w), make_float2(g[m].z, g[m].w));
+                    Z[m] = make_float4(Z[m].x + z1.x, Z[m].y + z1.y, Z[m].z + z2.x, Z[m].w + z2.y);
+                }
             }
-            float2 D1, D2;
-            pack_inverse(Z1, Z2, twiddle(p.twid, p.logNT, LOGV + 1, j), D1, D2);
-            X[lpad(bitrev<LOGV>(j))] = D1;
-            X[lpad(bitrev<LOGV>(N - j))] = D2;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = lt + (m0 + m) * TT;
+            if (j == 0) {
+                const float Z0 = Z[m].x, ZN = Z[m].y;
+                X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
+                X[lpad(1)] = make_float2(Z[m].z, -Z[m].w);
+            } else {
+                float2 D1, D2;
+                pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w),
+                             twiddle(p.twid, p.logNT, LOGV + 1, j), D1, D2);
+                X[lpad(bitrev<LOGV>(j))] = D1;
+                X[lpad(bitrev<LOGV>(N - j))] = D2;
+            }
         }
     }
     __syncthreads();
@@ -414,8 +535,8 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, cons
 // whole history term sum_{s=1..n-1} h[n-s] x_s, written into slot n-1; the
 // red cells (k_red) then add h[0] x_n.  One workgroup per row.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_lazy_dot(Dev p) {
-    const long long n = p.st->pos + 1;
+__global__ void __launch_bounds__(256) k_lazy_dot(Dev p, int rd) {
+    const long long n = position_of(p, rd);
     const long long t = n - 1;
     if (n > p.L) return;
     const long long rowi = blockIdx.x;
@@ -433,36 +554,32 @@ __global__ void __launch_bounds__(256) k_lazy_dot(Dev p) {
     if (threadIdx.x == 0) {
         float tot = 0.f;
         for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += part[w];
-        p.buf[act_row(p, l, b, c) + t] = tot;
+        p.ar[ring(p, n, l) + (size_t)b * p.D + c] = tot;
     }
 }
 
 // ---------------------------------------------------------------------------
 // External-block mode: the red cell of one layer at position n for all (b, c):
-// y = pending + h0 * q, and q becomes the slot's input.
+// y = pending + h0 * q, and q becomes the layer input at n.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_red_layer(Dev p, int l, const float *q, float *y) {
-    const long long n = p.st->pos + 1;
-    const long long t = n - 1;
+__global__ void __launch_bounds__(256) k_red_layer(Dev p, int rd, int l, const float *q, float *y) {
+    const long long n = position_of(p, rd);
     if (n > p.L) return;
+    const int BD = p.B * p.D;
     const int chain = blockIdx.x * blockDim.x + threadIdx.x;
-    if (chain < p.B * p.D) {
-        const int b = chain / p.D, c = chain % p.D;
-        const size_t r = act_row(p, l, b, c) + t;
+    if (chain < BD) {
+        const int c = chain % p.D;
         const float x = q[chain];
-        const float v = fmaf(p.filt[filt_row(p, l, c)], x, p.buf[r]);
-        p.buf[r] = x;
-        if (p.rec) p.rec[r] = v;
+        const float v = fmaf(p.hh[head(p, l, 0, c)], x, p.ar[ring(p, n, l) + chain]);
+        p.xr[ring(p, n, l) + chain] = x;
+        if (p.recx) {
+            const size_t r = ((size_t)(n - 1) * p.M + l) * BD + chain;
+            p.recx[r] = x;
+            p.recy[r] = v;
+        }
         y[chain] = v;
-        if (l == p.M - 1) p.ylast[(size_t)t * p.B * p.D + chain] = v;
+        if (l == p.M - 1) p.ylast[(size_t)(n - 1) * BD + chain] = v;
     }
-}
-
-// Publish position n when no gray block follows (the last position, or
-// external mode's last position).
-__global__ void k_finish(Dev p) {
-    if (p.st->pos + 1 > p.L) return;
-    finish_position(p, p.st->pos + 1, 1);
 }
 
 }  // namespace fi

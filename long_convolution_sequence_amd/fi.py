@@ -211,11 +211,10 @@ class Context:
         self._check(self._lib.fi_tiles(self._h))
 
     def history(self, layer, what, count=None):
-        """[B][D][count] device tensor: what=0 layer inputs x, what=1 recorded outputs y."""
+        """[count][B][D] device tensor: what=0 layer inputs x, what=1 mixer outputs y."""
         count = self.position if count is None else count
-        dst = self._torch.empty((self.B, self.D, max(count, 1)), dtype=self._torch.float32,
-                                device=self.device)[..., :count]
-        dst = dst.contiguous()
+        dst = self._torch.empty((max(count, 1), self.B, self.D), dtype=self._torch.float32,
+                                device=self.device)[:count]
         self._check(self._lib.fi_history(self._h, int(layer), int(what), int(count), _dptr(dst)))
         return dst
 

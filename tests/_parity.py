@@ -39,8 +39,8 @@ def check_replay(h, ctx, layers=None, chans=None, count=None):
     layers = range(ctx.M) if layers is None else layers
     worst = 0.0
     for l in layers:
-        xs = ctx.history(l, 0, count).cpu().numpy()
+        xs = ctx.history(l, 0, count).cpu().numpy()          # [T][B][D]
         ys = ctx.history(l, 1, count).cpu().numpy()
         for c in (range(ctx.D) if chans is None else chans):
-            worst = max(worst, replay_ratio(h[l, c], xs[:, c], ys[:, c]))
+            worst = max(worst, replay_ratio(h[l, c], xs[:, :, c].T, ys[:, :, c].T))
     return worst

@@ -72,10 +72,10 @@ def test_small_stack_d256_feedback():
     with fi.Context(torch.from_numpy(h).cuda(), w.B, record=True) as ctx:
         ctx.set_input(torch.from_numpy(workloads.x_first(w)).cuda())
         y = ctx.generate(w.L).cpu().numpy()
-        xs = ctx.history(0, 0).cpu().numpy()
+        xs = ctx.history(0, 0).cpu().numpy()          # [L][B][D]
         ys = ctx.history(0, 1).cpu().numpy()
     rng = np.random.default_rng(1)
-    worst = max(replay_ratio(h[0, c], xs[:, c], ys[:, c]) for c in rng.choice(w.D, 24, replace=False))
+    worst = max(replay_ratio(h[0, c], xs[:, :, c].T, ys[:, :, c].T) for c in rng.choice(w.D, 24, replace=False))
     say(f"  replay worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
     horizon, rel = _free_running(y, h, w, list(rng.choice(w.D, 8, replace=False)), w.L)
@@ -101,18 +101,20 @@ def _stack_feedback_case(idx, replay_layers, prefix, points=None):
         y = y.cpu().numpy()
         worst = 0.0
         for l in replay_layers:
-            xs = ctx.history(l, 0).cpu().numpy()
+            xs = ctx.history(l, 0).cpu().numpy()      # [L][B][D]
             ys = ctx.history(l, 1).cpu().numpy()
             for _ in range(6):
                 b, c = int(rng.integers(w.B)), int(rng.integers(w.D))
+                xrow = np.ascontiguousarray(xs[:, b, c])
+                yrow = np.ascontiguousarray(ys[:, b, c])
                 if points is None:
-                    worst = max(worst, replay_ratio(h[l, c], xs[b, c][None], ys[b, c][None]))
+                    worst = max(worst, replay_ratio(h[l, c], xrow[None], yrow[None]))
                 else:
                     ts = np.unique(np.concatenate([rng.integers(0, w.L, points),
                                                    [w.L - 1, w.L // 2, w.L // 2 - 1]]))
-                    ref = oracle.conv_points(h[l, c], xs[b, c], ts)
-                    tol = TF_TOL * np.abs(h[l, c].astype(np.float64)).sum() * np.abs(xs[b, c]).max()
-                    worst = max(worst, np.abs(ys[b, c][ts] - ref).max() / tol)
+                    ref = oracle.conv_points(h[l, c], xrow, ts)
+                    tol = TF_TOL * np.abs(h[l, c].astype(np.float64)).sum() * np.abs(xrow).max()
+                    worst = max(worst, np.abs(yrow[ts] - ref).max() / tol)
         say(f"  replay worst error/tolerance {worst:.3e}")
         assert worst <= 1.0
     chains = list(rng.choice(w.B * w.D, 4, replace=False))

@@ -61,12 +61,12 @@ def test_stack_teacher_forced_per_layer_replay(tau):
     with fi.Context(_cuda(h), B, tau_mode=TAUS[tau], record=True) as ctx:
         y = ctx.prefill(_cuda(x)).cpu().numpy()
         x0 = ctx.history(0, 0).cpu().numpy()
-        assert np.array_equal(x0, np.transpose(x, (1, 2, 0)))       # inputs land in their slots
+        assert np.array_equal(x0, x)                                 # inputs land in their slots
         for l in range(M - 1):                                       # inter-layer map
             yl = ctx.history(l, 1).cpu().numpy()
             xn = ctx.history(l + 1, 0).cpu().numpy()
             assert np.allclose(xn, np.tanh(yl.astype(np.float64)), rtol=0, atol=4e-7)
-        assert np.array_equal(np.transpose(ctx.history(M - 1, 1).cpu().numpy(), (2, 0, 1)), y)
+        assert np.array_equal(ctx.history(M - 1, 1).cpu().numpy(), y)
         worst = check_replay(h, ctx)
     say(f"  worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
@@ -81,14 +81,13 @@ def test_feedback_small_config_replay_and_horizon():
     with fi.Context(_cuda(h), w.B, record=True) as ctx:
         ctx.set_input(_cuda(x1))
         y = ctx.generate(w.L).cpu().numpy()            # [L][B][D]
-        xs = ctx.history(0, 0).cpu().numpy()           # [B][D][L]
+        xs = ctx.history(0, 0).cpu().numpy()           # [L][B][D]
         worst = check_replay(h, ctx)
     say(f"  replay worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
     # the feedback wiring: x_1 given, x_{n+1} = tanh(y_n)
-    assert np.array_equal(xs[:, :, 0], x1)
-    assert np.allclose(xs[:, :, 1:], np.tanh(np.transpose(y, (1, 2, 0))[:, :, :-1].astype(np.float64)),
-                       rtol=0, atol=4e-7)
+    assert np.array_equal(xs[0], x1)
+    assert np.allclose(xs[1:], np.tanh(y[:-1].astype(np.float64)), rtol=0, atol=4e-7)
     # free-running against the fp64 oracle within the measured divergence horizon
     chans = np.arange(w.D)
     y64, _ = oracle.stack(h, chans, x1[0], w.L)
