@@ -61,8 +61,15 @@ typedef enum fi_status {
  * (The pages' synthetic model puts a block after each mixer and a sampler at
  * the end, "LCSM-Inferenz-Algorithmus"; the elementwise tanh stands in for both.)
  * FI_MAP_EXTERNAL: the caller runs its own block between layers with
- * fi_layer_red() / fi_tiles(). */
-enum { FI_MAP_TANH = 0, FI_MAP_IDENTITY = 1, FI_MAP_EXTERNAL = 2 };
+ * fi_layer_red() / fi_tiles().
+ * FI_MAP_HYENA: the library runs a Hyena-style block after every mixer
+ * ("Modellarchitektur": a^l = block^l(mixer^l(a^{l-1}))), weights given by
+ * fi_set_block_weights: [u|v|w] = x W, the mixer convolves q = u*w, its output
+ * c gates m = v*c, z = GELU(m W1) W2 (exact-erf GELU, no biases),
+ * a = z / sqrt(mean(z^2) + 1e-6), next layer input a, next position's layer-0
+ * input fb(a^{M-1}).  Needs D % 8 == 0 and B <= 8.  Here "y" of fi_step /
+ * fi_generate is a^{M-1}_n, the value the feedback is applied to. */
+enum { FI_MAP_TANH = 0, FI_MAP_IDENTITY = 1, FI_MAP_EXTERNAL = 2, FI_MAP_HYENA = 3 };
 enum { FI_FEEDBACK_TANH = 0, FI_FEEDBACK_IDENTITY = 1 };
 
 /* How gray blocks are computed. AUTO: per block size, the faster path as timed
@@ -170,10 +177,19 @@ fi_status fi_debug_schedule(const fi_ctx *ctx, int64_t n, int *q, int *path);
  * at least P entries; any pointer may be NULL. */
 fi_status fi_tau_table(const fi_ctx *ctx, int *path, double *us_direct, double *us_fft);
 
-/* Copy positions 1..count of one layer into dst (device fp32, [count][B][D]):
- * what = 0: the layer inputs x^l_s, what = 1: the mixer outputs y^l_s (valid
- * for s <= position).  Needs record = 1 (FI_ESTATE otherwise). */
-fi_status fi_history(const fi_ctx *ctx, int layer, int what, int64_t count, float *dst);
+/* Copy positions first..first+count-1 (first >= 1) of one layer into dst
+ * (device fp32, [count][B][D]):
+ * what = 0: the layer's convolution inputs x^l_s, what = 1: its mixer outputs
+ * y^l_s, what = 2 (FI_MAP_HYENA only): its block outputs a^l_s (valid for
+ * s <= position).  Needs record = 1 (FI_ESTATE otherwise). */
+fi_status fi_history(const fi_ctx *ctx, int layer, int what, int64_t first, int64_t count, float *dst);
+
+/* Block weights for FI_MAP_HYENA, as bf16 bit patterns in row-major x*W
+ * layout: W [M][D][3D], W1 [M][D][4D], W2 [M][4D][D]; host memory unless
+ * on_device.  Copied (stored transposed); the caller keeps ownership.
+ * Synchronises the stream.  Must precede any step in that mode (FI_ESTATE). */
+fi_status fi_set_block_weights(fi_ctx *ctx, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
+                               int on_device);
 
 /* Device wall-clock stamps (100 MHz counter ticks) written when each position
  * finished: dst (host int64 [count]) receives the stamps of positions

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/fi.h"
+#include "fi_block.h"
 #include "fi_kernels.h"
 
 using namespace fi;
@@ -48,7 +49,7 @@ int ctz64(int64_t n) {
 
 struct Layout {
     size_t filt = 0, hh = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
-           stamps = 0, state = 0, scratch = 0;
+           stamps = 0, state = 0, scratch = 0, wt = 0, w1t = 0, w2t = 0, zb = 0, mb = 0, hb = 0, reca = 0;
     int HK = 0;
     size_t spec[kMaxP] = {0};
     size_t total = 0;
@@ -71,6 +72,8 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     if (M < 1 || M > kMaxLayers || B < 1 || D < 1 || P < 0 || P > kMaxP) return false;
     const int vlog = o.fft_max_log2;
     if (vlog < kMinSubLog || vlog > kMaxLdsFftLog) return false;
+    const bool hyena = o.map == FI_MAP_HYENA;
+    if (hyena && (D % 8 != 0 || B > kBlockMaxB)) return false;
     if ((int64_t)B * D > (int64_t(1) << 24)) return false;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -87,6 +90,16 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.ar = take((size_t)kRing * rowsMBD * sizeof(float));
     lay.recx = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
     lay.recy = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
+    if (hyena) {
+        const size_t DD = (size_t)D * D;
+        lay.wt = take((size_t)M * 3 * DD * 2);
+        lay.w1t = take((size_t)M * 4 * DD * 2);
+        lay.w2t = take((size_t)M * 4 * DD * 2);
+        lay.zb = take((size_t)B * D * sizeof(float));
+        lay.mb = take((size_t)B * D * sizeof(float));
+        lay.hb = take((size_t)B * 4 * D * sizeof(float));
+        lay.reca = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
+    }
     for (int q = 0; q < P; ++q) lay.spec[q] = fft_exists(q, P) ? take(rowsMD * spec_row_f4(q, vlog) * 16) : 0;
     // forward sub-block spectra of the widest split class: [M*B*D][U/2] float4
     lay.scratch = (P - 1 > vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
@@ -122,6 +135,7 @@ struct fi_ctx {
     bool poisoned = false;
     std::string err;
     int qd = 0;  // first block-size class computed by FFT (classes below are direct)
+    bool weights_set = false;
     hipGraphExec_t gclass[kMaxP + 1] = {nullptr};
     hipGraphExec_t gblock = nullptr;
     int block_log = 0;
@@ -340,8 +354,27 @@ hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const floa
     return e;
 }
 
+// Hyena-style block position: per layer projection + red cell, GELU up,
+// down; then the output / feedback; then every layer's gray block.
+hipError_t launch_hyena_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
+                                 int advance) {
+    const int B = c->B, D = c->D;
+    const size_t lds_d = (size_t)B * D * sizeof(float), lds_4d = 4 * lds_d;
+    for (int l = 0; l < c->M; ++l) {
+        hipLaunchKernelGGL(k_hy_proj, dim3((D + 3) / 4), dim3(256), lds_d, s, c->dev, rd, l,
+                           l == 0 ? xext : nullptr);
+        hipLaunchKernelGGL(k_hy_up, dim3(D), dim3(256), lds_d, s, c->dev, rd, l);
+        hipLaunchKernelGGL(k_hy_down, dim3((D + 3) / 4), dim3(256), lds_4d, s, c->dev, rd, l);
+    }
+    hipLaunchKernelGGL(k_hy_out, dim3(1), dim3(256), 0, s, c->dev, rd, yext);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, advance);
+}
+
 hipError_t launch_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
                            int advance) {
+    if (c->opt.map == FI_MAP_HYENA) return launch_hyena_position(c, rd, q, s, xext, yext, advance);
     return launch_position_t<true>(c, rd, q, s, xext, yext, advance);
 }
 
@@ -379,6 +412,7 @@ fi_status clear_state(fi_ctx *c) {
         HIPCK(c, hipMemsetAsync(c->dev.recx, 0, rowsMBD * c->L * sizeof(float), c->stream));
         HIPCK(c, hipMemsetAsync(c->dev.recy, 0, rowsMBD * c->L * sizeof(float), c->stream));
     }
+    if (c->dev.reca) HIPCK(c, hipMemsetAsync(c->dev.reca, 0, rowsMBD * c->L * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.xin, 0, 2 * (size_t)c->B * c->D * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.ylast, 0, (size_t)c->L * c->B * c->D * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.stamps, 0, (size_t)(c->L + 1) * sizeof(long long), c->stream));
@@ -461,7 +495,8 @@ fi_status build_graphs(fi_ctx *c) {
         if (s != FI_OK) return s;
     }
     // positions m*2^k + j, j = 1 .. 2^k-1: class ctz(j), parity of j
-    const int k = c->opt.block_graph_log2;
+    // (a block-mode position is ~3M+5 kernels: only the per-class graphs there)
+    const int k = c->opt.map == FI_MAP_HYENA ? 0 : c->opt.block_graph_log2;
     if (k >= 1 && k < c->P) {
         std::vector<std::pair<int, int>> pos;
         for (int64_t j = 1; j < (int64_t(1) << k); ++j) pos.push_back({ctz64(j), rd_of(j)});
@@ -571,7 +606,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         o = *opt;
     else
         fi_default_options(&o);
-    if (o.map < FI_MAP_TANH || o.map > FI_MAP_EXTERNAL) return FI_EINVAL;
+    if (o.map < FI_MAP_TANH || o.map > FI_MAP_HYENA) return FI_EINVAL;
     if (o.feedback < FI_FEEDBACK_TANH || o.feedback > FI_FEEDBACK_IDENTITY) return FI_EINVAL;
     if (o.tau_mode < FI_TAU_AUTO || o.tau_mode > FI_TAU_FFT) return FI_EINVAL;
     if ((uintptr_t)workspace % 256 != 0) return FI_EINVAL;
@@ -626,7 +661,20 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     d.D = channels;
     d.L = L;
     d.logNT = lay.logNT;
-    d.map = o.map == FI_MAP_IDENTITY ? 1 : (o.map == FI_MAP_EXTERNAL ? 2 : 0);
+    d.map = o.map == FI_MAP_IDENTITY ? 1 : o.map == FI_MAP_EXTERNAL ? 2 : o.map == FI_MAP_HYENA ? 3 : 0;
+    if (o.map == FI_MAP_HYENA) {
+        d.Wt = (const unsigned short *)(c->ws + lay.wt);
+        d.W1t = (const unsigned short *)(c->ws + lay.w1t);
+        d.W2t = (const unsigned short *)(c->ws + lay.w2t);
+        d.zb = (float *)(c->ws + lay.zb);
+        d.mb = (float *)(c->ws + lay.mb);
+        d.hb = (float *)(c->ws + lay.hb);
+        d.reca = o.record ? (float *)(c->ws + lay.reca) : nullptr;
+        const int lds_4d = (int)((size_t)batch * 4 * channels * sizeof(float));
+        if (hipFuncSetAttribute((const void *)k_hy_down, hipFuncAttributeMaxDynamicSharedMemorySize, lds_4d) !=
+            hipSuccess)
+            return bail(fail(c, FI_EDEVICE, "block kernel LDS attribute"));
+    }
     d.fb = o.feedback == FI_FEEDBACK_IDENTITY ? 1 : 0;
     for (int q = 0; q < c->P; ++q)
         c->spec[q] = fft_exists(q, c->P) ? (float4 *)(c->ws + lay.spec[q]) : nullptr;
@@ -742,6 +790,7 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
     if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_step in external-block mode");
+    if (c->opt.map == FI_MAP_HYENA && !c->weights_set) return fail(c, FI_ESTATE, "block weights not set");
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const int64_t n = c->pos + 1;
@@ -767,6 +816,7 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
     if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_generate in external-block mode");
+    if (c->opt.map == FI_MAP_HYENA && !c->weights_set) return fail(c, FI_ESTATE, "block weights not set");
     if (steps < 0) return FI_EINVAL;
     if (c->pos + steps > c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
@@ -817,18 +867,55 @@ fi_status fi_tau_table(const fi_ctx *c, int *path, double *us_direct, double *us
     return FI_OK;
 }
 
-fi_status fi_history(const fi_ctx *cc, int layer, int what, int64_t count, float *dst) {
+fi_status fi_history(const fi_ctx *cc, int layer, int what, int64_t first, int64_t count, float *dst) {
     fi_ctx *c = const_cast<fi_ctx *>(cc);
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
-    if (layer < 0 || layer >= c->M || count < 0 || count > c->L || !dst || what < 0 || what > 1)
+    if (layer < 0 || layer >= c->M || first < 1 || count < 0 || first - 1 + count > c->L || !dst || what < 0 ||
+        what > 2)
         return FI_EINVAL;
     if (!c->dev.recx) return fail(c, FI_ESTATE, "histories are recorded only with record = 1");
+    if (what == 2 && !c->dev.reca) return fail(c, FI_ESTATE, "block outputs exist only with FI_MAP_HYENA");
     if (count == 0) return FI_OK;
     const size_t BD = (size_t)c->B * c->D;
-    const float *src = (what == 0 ? c->dev.recx : c->dev.recy) + (size_t)layer * BD;
+    const float *src = (what == 0 ? c->dev.recx : what == 1 ? c->dev.recy : c->dev.reca) + (size_t)layer * BD +
+                       (size_t)(first - 1) * c->M * BD;
     HIPCK(c, hipMemcpy2DAsync(dst, BD * sizeof(float), src, (size_t)c->M * BD * sizeof(float), BD * sizeof(float),
                               (size_t)count, hipMemcpyDeviceToDevice, c->stream));
+    return FI_OK;
+}
+
+fi_status fi_set_block_weights(fi_ctx *c, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
+                               int on_device) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map != FI_MAP_HYENA) return fail(c, FI_ESTATE, "block weights need FI_MAP_HYENA");
+    if (!W || !W1 || !W2) return FI_EINVAL;
+    const int D = c->D, M = c->M;
+    const size_t DD = (size_t)D * D;
+    unsigned short *tmp = nullptr;
+    HIPCK(c, hipMalloc((void **)&tmp, 4 * DD * sizeof(unsigned short)));
+    struct Part { const uint16_t *src; unsigned short *dst; int rows, cols; };
+    const Part parts[3] = {{W, const_cast<unsigned short *>(c->dev.Wt), D, 3 * D},
+                           {W1, const_cast<unsigned short *>(c->dev.W1t), D, 4 * D},
+                           {W2, const_cast<unsigned short *>(c->dev.W2t), 4 * D, D}};
+    hipError_t e = hipSuccess;
+    for (int pi = 0; pi < 3 && e == hipSuccess; ++pi) {
+        const Part &pt = parts[pi];
+        const size_t per = (size_t)pt.rows * pt.cols;
+        for (int l = 0; l < M && e == hipSuccess; ++l) {
+            e = hipMemcpyAsync(tmp, pt.src + l * per, per * sizeof(unsigned short),
+                               on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, c->stream);
+            if (e != hipSuccess) break;
+            hipLaunchKernelGGL(k_transpose16, dim3((pt.cols + 31) / 32, (pt.rows + 31) / 32), dim3(256), 0,
+                               c->stream, tmp, pt.dst + l * per, pt.rows, pt.cols);
+            e = hipGetLastError();
+        }
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    (void)hipFree(tmp);
+    if (e != hipSuccess) return fail(c, FI_EDEVICE, std::string("block weights: ") + hipGetErrorString(e));
+    c->weights_set = true;
     return FI_OK;
 }
 
@@ -869,7 +956,8 @@ fi_status fi_tiles(fi_ctx *c) {
 fi_status fi_lazy_step(fi_ctx *c, const float *x_t, float *y_t) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
-    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
+    if (c->opt.map == FI_MAP_EXTERNAL || c->opt.map == FI_MAP_HYENA)
+        return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 2)) != FI_OK) return s;
     const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
@@ -901,7 +989,8 @@ fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
     if (n < 1 || n > c->L || reps < 1 || !us) return FI_EINVAL;
-    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
+    if (c->opt.map == FI_MAP_EXTERNAL || c->opt.map == FI_MAP_HYENA)
+        return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
     if ((s = set_state_pos(c, n - 1)) != FI_OK) return s;
     c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
     const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);

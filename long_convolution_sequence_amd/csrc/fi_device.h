@@ -13,6 +13,7 @@
 //                        positions until they are drained into the ring
 //                        (activation reuse, Flash Inference "Speicheroptimierung")
 //   recx, recy [L][M][B][D]  optional record of every layer input and output
+//   Wt, W1t, W2t, zb, mb, hb, reca   Hyena-style block (see fi_block.h)
 //   xin   [2][B][D]      next layer-0 input, double-buffered by position parity
 //   ylast [L][B][D]      last layer's mixer output per position
 //   stamps[L+1] (i64)    device wall clock at the end of each position
@@ -49,8 +50,16 @@ struct Dev {
     int HK;    // filter-head taps kept per (l, c)
     int W;     // ring slots (power of two)
     int G;     // copy/drain block between ring and row-major history
-    int map;   // 0 tanh, 1 identity, 2 external
+    int map;   // 0 tanh, 1 identity, 2 external, 3 Hyena-style block
     int fb;    // 0 tanh, 1 identity
+    // Hyena-style block: transposed bf16 weights and per-position activations
+    const unsigned short *Wt;   // [M][3D][D]
+    const unsigned short *W1t;  // [M][4D][D]
+    const unsigned short *W2t;  // [M][D][4D]
+    float *zb;                  // [B][D]   down-projection output (before RMSNorm)
+    float *mb;                  // [B][D]   gated mixer output
+    float *hb;                  // [B][4D]  GELU hidden units
+    float *reca;                // [L][M][B][D] optional record of block outputs
 };
 
 // Ring entry of (position pos, layer l, chain 0): add the chain index.

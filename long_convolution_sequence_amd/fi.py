@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfi.so")
 
 FI_OK, FI_EINVAL, FI_ENOMEM, FI_EDEVICE, FI_ERANGE, FI_ESTATE = 0, -1, -2, -3, -4, -5
-MAP_TANH, MAP_IDENTITY, MAP_EXTERNAL = 0, 1, 2
+MAP_TANH, MAP_IDENTITY, MAP_EXTERNAL, MAP_HYENA = 0, 1, 2, 3
 FEEDBACK_TANH, FEEDBACK_IDENTITY = 0, 1
 TAU_AUTO, TAU_DIRECT, TAU_FFT = 0, 1, 2
 PATH_NONE, PATH_DIRECT, PATH_FFT = 0, 1, 2
@@ -70,13 +70,14 @@ def load_library():
         "fi_last_error": (ctypes.c_char_p, [P]),
         "fi_debug_schedule": (I, [P, I64, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "fi_tau_table": (I, [P, P, P, P]),
-        "fi_history": (I, [P, I, I, I64, P]),
+        "fi_history": (I, [P, I, I, I64, I64, P]),
         "fi_stamps": (I, [P, I64, I64, P]),
         "fi_layer_red": (I, [P, I, P, P]),
         "fi_tiles": (I, [P]),
         "fi_lazy_step": (I, [P, P, P]),
         "fi_lazy_generate": (I, [P, I64, P]),
         "fi_block_times": (I, [P, I, P, P]),
+        "fi_set_block_weights": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
@@ -210,12 +211,26 @@ class Context:
     def tiles(self):
         self._check(self._lib.fi_tiles(self._h))
 
-    def history(self, layer, what, count=None):
-        """[count][B][D] device tensor: what=0 layer inputs x, what=1 mixer outputs y."""
-        count = self.position if count is None else count
+    def set_block_weights(self, W, W1, W2):
+        """Hyena-style block weights as bf16 bit patterns (uint16 numpy arrays or int16/uint16
+        device tensors): W [M][D][3D], W1 [M][D][4D], W2 [M][4D][D] (row-major x*W)."""
+        if isinstance(W, np.ndarray):
+            arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (W, W1, W2)]
+            ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+            on_dev = 0
+        else:
+            arrs = [a.contiguous() for a in (W, W1, W2)]
+            ptrs = [ctypes.c_void_p(a.data_ptr()) for a in arrs]
+            on_dev = 1
+        self._check(self._lib.fi_set_block_weights(self._h, *ptrs, on_dev))
+
+    def history(self, layer, what, count=None, first=1):
+        """[count][B][D] device tensor of positions first.. : what=0 layer (convolution) inputs,
+        1 mixer outputs, 2 block outputs (Hyena-style block mode)."""
+        count = self.position - first + 1 if count is None else count
         dst = self._torch.empty((max(count, 1), self.B, self.D), dtype=self._torch.float32,
                                 device=self.device)[:count]
-        self._check(self._lib.fi_history(self._h, int(layer), int(what), int(count), _dptr(dst)))
+        self._check(self._lib.fi_history(self._h, int(layer), int(what), int(first), int(count), _dptr(dst)))
         return dst
 
     def stamps(self, first, count):

@@ -57,14 +57,21 @@ def finish(c, v, W1, W2):
     return rmsnorm(hidden @ np.asarray(W2, dtype=np.float64))
 
 
-def generate(filters, W, W1, W2, x_first, steps):
-    """Whole-model feedback generation for ``steps`` positions, fp64.
+def generate(filters, W, W1, W2, x_first, steps, dtype=np.float64):
+    """Whole-model feedback generation for ``steps`` positions.
 
     filters : [M, D, L]; W, W1, W2 : [M, ...] per-layer weights (float arrays);
     x_first : [B, D] layer-0 input at the first position.
-    Returns dict with fp64 arrays q, c, a of shape [steps, M, B, D].
+    Returns dict with arrays q, c, a of shape [steps, M, B, D].
+    dtype fp64 is the oracle; fp32 (same operations, rounded to fp32 after each
+    step) exists only to measure how fast two correct evaluations diverge.
     Cost is O(steps^2 * M * B * D) for the convolutions: small cases only.
     """
+    f64 = dtype == np.float64
+
+    def r(a):
+        return np.asarray(a, dtype=np.float64) if f64 else np.asarray(a, dtype=np.float32).astype(np.float64)
+
     filters = np.asarray(filters, dtype=np.float64)
     M, D, L = filters.shape
     B = x_first.shape[0]
@@ -72,16 +79,17 @@ def generate(filters, W, W1, W2, x_first, steps):
     Q = np.zeros((steps, M, B, D))
     C = np.zeros((steps, M, B, D))
     A = np.zeros((steps, M, B, D))
-    x = np.asarray(x_first, dtype=np.float64)
+    x = r(x_first)
     for n in range(steps):
         for l in range(M):
             q, v = project(x, W[l])
+            q, v = r(q), r(v)
             q_hist[l, n] = q
             # c_n[b, ch] = sum_{s<=n} h^l[ch][n-s] q_s[b, ch]
             taps = filters[l, :, n::-1]                  # [D, n+1]: h[n-s] for s = 0..n
-            c = np.einsum("sbd,ds->bd", q_hist[l, :n + 1], taps)
-            a = finish(c, v, W1[l], W2[l])
+            c = r(np.einsum("sbd,ds->bd", q_hist[l, :n + 1], taps))
+            a = r(finish(c, v, W1[l], W2[l]))
             Q[n, l], C[n, l], A[n, l] = q, c, a
             x = a
-        x = np.tanh(A[n, M - 1])
+        x = r(np.tanh(A[n, M - 1]))
     return {"q": Q, "c": C, "a": A}
