@@ -220,6 +220,16 @@ fi_status fi_lazy_generate(fi_ctx *ctx, int64_t steps, float *y);
  * at least P entries; either may be NULL. */
 fi_status fi_block_times(fi_ctx *ctx, int clear, double *ms, int64_t *count);
 
+/* Per-size runtime of one gray-block path (the pages' runtime-per-tile-size
+ * comparison, "Pareto-Optimalitaetskurve"): the mean device time in
+ * microseconds of the gray-block kernels of class q (U = 2^q) over `reps`
+ * launches at position n = 2^q, timed with HIP events, without advancing.
+ * path = FI_PATH_DIRECT (the direct kernel, red cells included) or
+ * FI_PATH_FFT (the FFT kernels alone).  FI_EINVAL where the path does not
+ * exist for q.  Overwrites activation rows: fi_reset is required before any
+ * further stepping (FI_ESTATE otherwise). */
+fi_status fi_time_block(fi_ctx *ctx, int q, int path, int reps, double *us);
+
 /* Benchmark support for the Lazy baseline: the mean device time in
  * microseconds of the Lazy work of position n (every layer's full O(n) sum
  * plus the red cells), over `reps` launches timed with HIP events, without

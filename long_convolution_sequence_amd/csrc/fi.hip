@@ -985,6 +985,36 @@ fi_status fi_block_times(fi_ctx *c, int clear, double *ms, int64_t *count) {
     return FI_OK;
 }
 
+fi_status fi_time_block(fi_ctx *c, int q, int path, int reps, double *us) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (q < 0 || q >= c->P || reps < 1 || !us) return FI_EINVAL;
+    if (path == FI_PATH_DIRECT ? !direct_exists(q) : path == FI_PATH_FFT ? !fft_exists(q, c->P) : true)
+        return FI_EINVAL;
+    const int64_t n = int64_t(1) << q;
+    if ((s = set_state_pos(c, n - 1)) != FI_OK) return s;
+    c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
+    const int rd = rd_of(n);
+    auto once = [&]() -> hipError_t {
+        return path == FI_PATH_DIRECT ? launch_direct<true>(c, rd, q, c->stream, nullptr, nullptr, 0)
+                                      : launch_fft(c, rd, q, c->stream, 0);
+    };
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    HIPCK(c, once());  // warm-up
+    HIPCK(c, hipEventRecord(a, c->stream));
+    for (int r = 0; r < reps; ++r) HIPCK(c, once());
+    HIPCK(c, hipEventRecord(b, c->stream));
+    HIPCK(c, hipEventSynchronize(b));
+    float ms = 0.f;
+    HIPCK(c, hipEventElapsedTime(&ms, a, b));
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    *us = ms * 1000.0 / reps;
+    return FI_OK;
+}
+
 fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;

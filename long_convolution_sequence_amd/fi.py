@@ -79,6 +79,7 @@ def load_library():
         "fi_block_times": (I, [P, I, P, P]),
         "fi_set_block_weights": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
+        "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -254,6 +255,12 @@ class Context:
         cnt = (ctypes.c_int64 * P)()
         self._check(self._lib.fi_block_times(self._h, int(clear), ms, cnt))
         return [(q, ms[q], cnt[q]) for q in range(self.P)]
+
+    def time_block(self, q, path, reps=10):
+        """Mean microseconds of class q's gray-block kernels on one path (needs reset after)."""
+        us = ctypes.c_double()
+        self._check(self._lib.fi_time_block(self._h, int(q), int(path), int(reps), ctypes.byref(us)))
+        return us.value
 
     def lazy_time(self, n, reps=3):
         """Mean microseconds of the Lazy baseline's work at position n (needs reset after)."""
