@@ -94,8 +94,9 @@ __device__ __forceinline__ void powers(float2 w, float2 (&pw)[1 << R]) {
 // offsets r + m*Q of a block of size S = 2^slog (Q = S / 2^R).  Equivalent
 // form used here: a 2^R-point DFT over m with constant roots (output k left
 // in register rev(k)), then the outer twiddle W_S^{r*k}.  PRUNED: the upper
-// half of v is known to be zero.
-template <int R, bool PRUNED = false>
+// half of v is known to be zero.  TWIDDLE false: r is known to be 0 (the
+// group spans a whole block), so the outer twiddles are all 1.
+template <int R, bool PRUNED = false, bool TWIDDLE = true>
 __device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
                                           const float2 *__restrict__ tw, int logNT) {
     static_for<0, R>([&](auto tc) {
@@ -115,25 +116,29 @@ __device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
             }
         });
     });
-    float2 pw[1 << R];
-    powers<R>(twiddle(tw, logNT, slog, r), pw);
-    static_for<1, (1 << R)>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        v[p] = cmul(v[p], pw[rev_bits<R, p>()]);
-    });
+    if constexpr (TWIDDLE) {
+        float2 pw[1 << R];
+        powers<R>(twiddle(tw, logNT, slog, r), pw);
+        static_for<1, (1 << R)>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            v[p] = cmul(v[p], pw[rev_bits<R, p>()]);
+        });
+    }
 }
 
 // Inverse of dif_group up to the factor 2^R: conjugate outer twiddles, then
 // the stages in reverse order with conjugate constant roots.
-template <int R>
+template <int R, bool TWIDDLE = true>
 __device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
                                           const float2 *__restrict__ tw, int logNT) {
-    float2 pw[1 << R];
-    powers<R>(twiddle(tw, logNT, slog, r), pw);
-    static_for<1, (1 << R)>([&](auto pc) {
-        constexpr int p = decltype(pc)::value;
-        v[p] = cmulc(v[p], pw[rev_bits<R, p>()]);
-    });
+    if constexpr (TWIDDLE) {
+        float2 pw[1 << R];
+        powers<R>(twiddle(tw, logNT, slog, r), pw);
+        static_for<1, (1 << R)>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            v[p] = cmulc(v[p], pw[rev_bits<R, p>()]);
+        });
+    }
     static_for<0, R>([&](auto tc) {
         constexpr int t = R - 1 - decltype(tc)::value;
         constexpr int half = (1 << R) >> (t + 1);
@@ -179,9 +184,9 @@ __device__ __forceinline__ void lds_group(float2 *X, int lt, const float2 *__res
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) v[m] = X[lpad(base + (m << QLOG))];
         if constexpr (FWD)
-            dif_group<R>(v, r, SLOG, tw, logNT);
+            dif_group<R, false, (QLOG > 0)>(v, r, SLOG, tw, logNT);
         else
-            dit_group<R>(v, r, SLOG, tw, logNT);
+            dit_group<R, (QLOG > 0)>(v, r, SLOG, tw, logNT);
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) X[lpad(base + (m << QLOG))] = v[m];
     }

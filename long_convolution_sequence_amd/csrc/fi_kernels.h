@@ -120,13 +120,14 @@ __global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const flo
             // waves 1..: stage the input window, the taps and the pending outputs
             const int t2 = threadIdx.x - kLanes, b2 = blockDim.x - kLanes;
             constexpr int KW = CHAIN ? U - 1 : U;     // window entries taken from the ring
+            constexpr int KD = KW > 0 ? KW : 1;       // divisor (no entries when KW is 0)
             batched_copy(nl * KW * kLanes, t2, b2,
                 [&](int i) {
-                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KD, li = (i / kLanes) / KD;
                     return cb + ln < BD ? p.xr[ring(p, n - U + 1 + k, l0 + li) + cb + ln] : 0.f;
                 },
                 [&](int i, float v) {
-                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KW, li = (i / kLanes) / KW;
+                    const int ln = i & (kLanes - 1), k = (i / kLanes) % KD, li = (i / kLanes) / KD;
                     xw[(li * U + k) * kLanes + ln] = v;
                 });
             batched_copy(nl * TAPS * kLanes, t2, b2,
@@ -287,18 +288,18 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
     float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1);
     const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
 
-    float2 acc[HALF0];
     float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) {
-        acc[m] = active ? adst[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
         v[m] = active ? xsrc[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
         v[m + HALF0] = make_float2(0.f, 0.f);
     }
     dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
-    // this thread's spectrum pairs, loaded together while the transform runs
+    forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
+    // this thread's spectrum pairs, loaded only now: held across the forward
+    // transform they would cost the registers of a fourth wave per SIMD
     constexpr int PAIRS = (N / 2 + TT - 1) / TT;
     float4 gs[PAIRS];
 #pragma unroll
@@ -306,7 +307,6 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
         const int j = lt + m * TT;
         gs[m] = (active && j < N / 2) ? sp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
 
     // bins of the real transform times the filter spectrum, re-packed for the inverse
@@ -337,7 +337,10 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
     dit_group<R0>(v, lt, LOGN, p.twid, p.logNT);
-    if (active) {
+    if (active) {  // the accumulators, like the spectrum, are read late
+        float2 acc[HALF0];
+#pragma unroll
+        for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
 #pragma unroll
         for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
     }

@@ -131,7 +131,9 @@ def test_prefill_equals_steps_then_generation_continues():
     say(f"case prefill == steps M={M} B={B} D={D} L={L} P={P}")
     h = _filters(M, D, L, 7, decay=64.0)
     x = np.random.default_rng(8).standard_normal((P, B, D)).astype(np.float32)
-    with fi.Context(_cuda(h), B) as a, fi.Context(_cuda(h), B) as b:
+    # one fixed split for both contexts: two calibrations may pick different
+    # paths, which agree only to rounding
+    with fi.Context(_cuda(h), B, tau_split=4) as a, fi.Context(_cuda(h), B, tau_split=4) as b:
         ya = a.prefill(_cuda(x))
         yb = torch.stack([b.step(_cuda(x[i])) for i in range(P)])
         assert torch.equal(ya, yb)
