@@ -105,7 +105,7 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.scratch = (P - 1 > vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
     const int nmax_log = std::min(P - 1, vlog);
     lay.logNT = std::max(2, nmax_log + 1);
-    lay.twid = take((size_t(1) << lay.logNT) * sizeof(float2));
+    lay.twid = take((size_t(3) << (lay.logNT - 1)) * sizeof(float2));  // twiddles, then pair twiddles
     lay.xin = take((size_t)2 * B * D * sizeof(float));
     lay.ylast = take((size_t)L * B * D * sizeof(float));
     lay.stamps = take((size_t)(L + 1) * sizeof(long long));
@@ -656,6 +656,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     d.st = (State *)(c->ws + lay.state);
     d.stamps = (long long *)(c->ws + lay.stamps);
     d.twid = (const float2 *)(c->ws + lay.twid);
+    d.ptw = d.twid + (size_t(1) << lay.logNT);
     d.M = layers;
     d.B = batch;
     d.D = channels;
@@ -686,15 +687,24 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
                        o.filters_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
                        c->stream) != hipSuccess)
         return bail(fail(c, FI_EDEVICE, "filter copy failed"));
-    // twiddle table, fp64 on the host
+    // twiddle tables, fp64 on the host: W_NT^k, then for every transform size
+    // N = 2^logn the pair twiddle W_{2N}^j of each real-spectrum item
     {
         const size_t nt = size_t(1) << lay.logNT;
-        std::vector<float2> tw(nt);
+        std::vector<float2> tw(nt + nt / 2, make_float2(1.f, 0.f));
+        const double pi = 3.14159265358979323846;
         for (size_t k = 0; k < nt; ++k) {
-            const double a = -2.0 * 3.14159265358979323846 * (double)k / (double)nt;
+            const double a = -2.0 * pi * (double)k / (double)nt;
             tw[k] = make_float2((float)std::cos(a), (float)std::sin(a));
         }
-        if (hipMemcpyAsync((void *)d.twid, tw.data(), nt * sizeof(float2), hipMemcpyHostToDevice,
+        for (int logn = 2; logn < lay.logNT; ++logn) {
+            const int N = 1 << logn;
+            for (int e = 1; e < N / 2; ++e) {
+                const double a = -pi * (double)pair_slot(logn, e).j / (double)N;
+                tw[nt + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
+            }
+        }
+        if (hipMemcpyAsync((void *)d.twid, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice,
                            c->stream) != hipSuccess ||
             hipStreamSynchronize(c->stream) != hipSuccess)
             return bail(fail(c, FI_EDEVICE, "twiddle copy failed"));

@@ -18,6 +18,8 @@
 //   ylast [L][B][D]      last layer's mixer output per position
 //   stamps[L+1] (i64)    device wall clock at the end of each position
 //   twid  [NT] (float2)  exp(-2 pi i k / NT), generated in fp64 on the host
+//   ptw   [NT/2] (float2) per transform size N: W_{2N}^j of real-spectrum item e
+//         (pair_slot) at N/2 + e, also fp64 on the host
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,6 +46,7 @@ struct Dev {
     State *st;
     long long *stamps;
     const float2 *twid;
+    const float2 *ptw;  // pair twiddles: W_{2N}^j of item e at ptw[N/2 + e]
     int M, B, D;
     int logNT;
     long long L;

@@ -212,13 +212,57 @@ __device__ __forceinline__ void inverse_groups(float2 *X, int lt, const float2 *
     }
 }
 
-template <int LOGN>
-__device__ __forceinline__ int bitrev(int k) {
-    return (int)(__brev((unsigned)k) >> (32 - LOGN));
+// Bit reversal of the low w bits of k (1 <= w <= 31), for host and device.
+__host__ __device__ constexpr unsigned brev32(unsigned v) {
+    v = ((v >> 1) & 0x55555555u) | ((v & 0x55555555u) << 1);
+    v = ((v >> 2) & 0x33333333u) | ((v & 0x33333333u) << 2);
+    v = ((v >> 4) & 0x0f0f0f0fu) | ((v & 0x0f0f0f0fu) << 4);
+    v = ((v >> 8) & 0x00ff00ffu) | ((v & 0x00ff00ffu) << 8);
+    return (v >> 16) | (v << 16);
+}
+__host__ __device__ constexpr int rbits(int w, int k) { return (int)(brev32((unsigned)k) >> (32 - w)); }
+
+// Work items of the real-spectrum step.  Bins k and N-k of the complex
+// transform are combined; they sit at the bit-reversed positions
+// rev(k), rev(N-k).  Item e in [0, N/2) names one such pair:
+//   pj: position of bin j (0 <= j < N/2), pm: position of bin N-j.
+// Item 0 is special: bins 0 and N/2, both self-paired (positions 0 and 1).
+// For N >= 32 the items run over 16-position groups so that sixteen
+// consecutive items touch sixteen consecutive positions (and the reversed
+// run of the partner group), which keeps the LDS accesses of a wave free of
+// bank conflicts: with k = a*(N/16) + b (a = rev4 of the position's low four
+// bits, b = rev of its group index), bin N-k lies in group rev(N/16 - b) at
+// offset 15 - (low bits).  Items 0..7: group 0 (pairs a <-> 16-a);
+// 8..15: group rev(N/32) = 1 (self-partnered, offsets i <-> 15-i);
+// 16..: group pairs b <-> N/16 - b for 1 <= b < N/32.
+struct PairSlot {
+    int pj, pm, j;
+};
+__host__ __device__ inline PairSlot pair_slot(int logn, int e) {
+    const int N = 1 << logn;
+    if (e == 0) return {0, 1, 0};
+    int p1, p2;
+    if (logn <= 4) {
+        p1 = rbits(logn, e);
+        p2 = rbits(logn, N - e);
+    } else if (e < 8) {
+        p1 = rbits(4, e);
+        p2 = rbits(4, 16 - e);
+    } else if (e < 16) {
+        p1 = 16 + (e - 8);
+        p2 = 31 - (e - 8);
+    } else {
+        const int b = ((e - 16) >> 4) + 1, i = e & 15;
+        p1 = 16 * rbits(logn - 4, b) + i;
+        p2 = 16 * rbits(logn - 4, (N >> 4) - b) + 15 - i;
+    }
+    const int k1 = rbits(logn, p1);
+    if (k1 < N / 2) return {p1, p2, k1};
+    return {p2, p1, N - k1};
 }
 
 // Real-spectrum pairing.  C holds the complex transform of c_k = a_{2k} + i a_{2k+1}
-// (N points, bit-reversed positions).  For bin pair (k, N-k), with W = W_{2N}^k:
+// (N points, bit-reversed positions, see pair_slot).  For bin pair (k, N-k), with W = W_{2N}^k:
 //   E = (C_k + conj C_{N-k})/2,  O = (C_k - conj C_{N-k})/(2i)
 //   A_k = E + W O,  A_{N-k} = conj(E - W O)          (bins of the 2N-point real FFT)
 // and the inverse packing of a real spectrum Z into D (so that the inverse

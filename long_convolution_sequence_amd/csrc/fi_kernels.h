@@ -304,18 +304,18 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
     float4 gs[PAIRS];
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
-        const int j = lt + m * TT;
-        gs[m] = (active && j < N / 2) ? sp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int e = lt + m * TT;
+        gs[m] = (active && e < N / 2) ? sp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
 
     // bins of the real transform times the filter spectrum, re-packed for the inverse
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
-        const int j = lt + m * TT;
-        if (j >= N / 2) break;
+        const int e = lt + m * TT;
+        if (e >= N / 2) break;
         const float4 g = gs[m];
-        if (j == 0) {
+        if (e == 0) {
             const float2 C0 = X[0];
             const float2 Ch = X[lpad(1)];
             const float Z0 = (C0.x + C0.y) * g.x;
@@ -323,8 +323,9 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
             X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
             X[lpad(1)] = cmulc(Ch, make_float2(g.z, g.w));
         } else {
-            const int p1 = lpad(bitrev<LOGN>(j)), p2 = lpad(bitrev<LOGN>(N - j));
-            const float2 W = twiddle(p.twid, p.logNT, LOGN + 1, j);
+            const PairSlot ps = pair_slot(LOGN, e);
+            const int p1 = lpad(ps.pj), p2 = lpad(ps.pm);
+            const float2 W = p.ptw[N / 2 + e];
             float2 A1, A2, D1, D2;
             real_bins(X[p1], X[p2], W, A1, A2);
             pack_inverse(cmul(A1, make_float2(g.x, g.y)), cmul(A2, make_float2(g.z, g.w)), W, D1, D2);
@@ -350,8 +351,9 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_fft_tile(Dev p, int rd,
 // ---------------------------------------------------------------------------
 // Filter spectra ("FFT-Vorberechnung"): for every (l, c) row, the 2N-point real
 // FFT of the taps g_r = h[goff + r], r in [0, 2N), stored in pair order
+// (item e of pair_slot, bin j = pair_slot(e).j):
 //   spec[0] = (G_0, G_N, Re G_{N/2}, Im G_{N/2}) / N
-//   spec[j] = (G_j, G_{N-j}) / N,  0 < j < N/2.
+//   spec[e] = (G_j, G_{N-j}) / N,  0 < e < N/2.
 // The 1/N folds the inverse transform's normalisation into the spectrum.
 // ---------------------------------------------------------------------------
 template <int LOGN>
@@ -376,16 +378,16 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
     __syncthreads();
     const float inv = 1.0f / (float)N;
     float4 *dst = spec + (size_t)rowi * (size_t)row_stride;
-    for (int j = lt; j < N / 2 && active; j += TT) {
-        if (j == 0) {
+    for (int e = lt; e < N / 2 && active; e += TT) {
+        if (e == 0) {
             const float2 C0 = X[0];
             const float2 Ch = X[lpad(1)];
             dst[0] = make_float4((C0.x + C0.y) * inv, (C0.x - C0.y) * inv, Ch.x * inv, -Ch.y * inv);
         } else {
+            const PairSlot ps = pair_slot(LOGN, e);
             float2 A1, A2;
-            real_bins(X[lpad(bitrev<LOGN>(j))], X[lpad(bitrev<LOGN>(N - j))],
-                      twiddle(p.twid, p.logNT, LOGN + 1, j), A1, A2);
-            dst[j] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv);
+            real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], p.ptw[N / 2 + e], A1, A2);
+            dst[e] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv);
         }
     }
 }
@@ -432,16 +434,16 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
     forward_groups<LOGV, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     float4 *dst = scratch + ((size_t)tile * K + i) * (N / 2);
-    for (int j = lt; j < N / 2; j += TT) {
-        if (j == 0) {
+    for (int e = lt; e < N / 2; e += TT) {
+        if (e == 0) {
             const float2 C0 = X[0];
             const float2 Ch = X[lpad(1)];
             dst[0] = make_float4(C0.x + C0.y, C0.x - C0.y, Ch.x, -Ch.y);
         } else {
+            const PairSlot ps = pair_slot(LOGV, e);
             float2 A1, A2;
-            real_bins(X[lpad(bitrev<LOGV>(j))], X[lpad(bitrev<LOGV>(N - j))],
-                      twiddle(p.twid, p.logNT, LOGV + 1, j), A1, A2);
-            dst[j] = make_float4(A1.x, A1.y, A2.x, A2.y);
+            real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], p.ptw[N / 2 + e], A1, A2);
+            dst[e] = make_float4(A1.x, A1.y, A2.x, A2.y);
         }
     }
 }
@@ -514,11 +516,11 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
                 X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
                 X[lpad(1)] = make_float2(Z[m].z, -Z[m].w);
             } else {
+                const PairSlot ps = pair_slot(LOGV, j);
                 float2 D1, D2;
-                pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w),
-                             twiddle(p.twid, p.logNT, LOGV + 1, j), D1, D2);
-                X[lpad(bitrev<LOGV>(j))] = D1;
-                X[lpad(bitrev<LOGV>(N - j))] = D2;
+                pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w), p.ptw[N / 2 + j], D1, D2);
+                X[lpad(ps.pj)] = D1;
+                X[lpad(ps.pm)] = D2;
             }
         }
     }

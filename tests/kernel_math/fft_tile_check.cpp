@@ -27,22 +27,23 @@ template <int LOGN> struct Emu {
     }
     groups<1, true>(X, tw, logNT);
   }
-  static void spectrum(const float* g, std::vector<float4>& spec, const float2* tw, int logNT) {
+  // ptw: pair twiddles, W_{2N}^j of item e at ptw[N/2 + e] (as the library's table)
+  static void spectrum(const float* g, std::vector<float4>& spec, const float2* tw, const float2* ptw, int logNT) {
     std::vector<float2> X; forward(g, false, X, tw, logNT);
     spec.resize(N / 2); const float inv = 1.0f / N;
-    for (int j = 0; j < N / 2; ++j) {
-      if (j == 0) { float2 C0 = X[0], Ch = X[lpad(1)]; spec[0] = make_float4((C0.x + C0.y) * inv, (C0.x - C0.y) * inv, Ch.x * inv, -Ch.y * inv); }
-      else { float2 A1, A2; real_bins(X[lpad(bitrev<LOGN>(j))], X[lpad(bitrev<LOGN>(N - j))], twiddle(tw, logNT, LOGN + 1, j), A1, A2);
-             spec[j] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv); }
+    for (int e = 0; e < N / 2; ++e) {
+      if (e == 0) { float2 C0 = X[0], Ch = X[lpad(1)]; spec[0] = make_float4((C0.x + C0.y) * inv, (C0.x - C0.y) * inv, Ch.x * inv, -Ch.y * inv); }
+      else { PairSlot ps = pair_slot(LOGN, e); float2 A1, A2; real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], ptw[N / 2 + e], A1, A2);
+             spec[e] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv); }
     }
   }
-  static void tile(const float* x, const std::vector<float4>& sp, float* acc, const float2* tw, int logNT) {
+  static void tile(const float* x, const std::vector<float4>& sp, float* acc, const float2* tw, const float2* ptw, int logNT) {
     std::vector<float2> X; forward(x, true, X, tw, logNT);
-    for (int j = 0; j < N / 2; ++j) {
-      float4 g = sp[j];
-      if (j == 0) { float2 C0 = X[0], Ch = X[lpad(1)]; float Z0 = (C0.x + C0.y) * g.x, ZN = (C0.x - C0.y) * g.y;
+    for (int e = 0; e < N / 2; ++e) {
+      float4 g = sp[e];
+      if (e == 0) { float2 C0 = X[0], Ch = X[lpad(1)]; float Z0 = (C0.x + C0.y) * g.x, ZN = (C0.x - C0.y) * g.y;
         X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN)); X[lpad(1)] = cmulc(Ch, make_float2(g.z, g.w)); }
-      else { int p1 = lpad(bitrev<LOGN>(j)), p2 = lpad(bitrev<LOGN>(N - j)); float2 W = twiddle(tw, logNT, LOGN + 1, j);
+      else { PairSlot ps = pair_slot(LOGN, e); int p1 = lpad(ps.pj), p2 = lpad(ps.pm); float2 W = ptw[N / 2 + e];
         float2 A1, A2, D1, D2; real_bins(X[p1], X[p2], W, A1, A2);
         pack_inverse(cmul(A1, make_float2(g.x, g.y)), cmul(A2, make_float2(g.z, g.w)), W, D1, D2); X[p1] = D1; X[p2] = D2; }
     }
@@ -58,15 +59,16 @@ template <int LOGN> struct Emu {
 };
 template <int LOGN> double run(int logNT) {
   const int U = 1 << LOGN, NT = 1 << logNT;
-  std::vector<float2> tw(NT);
+  std::vector<float2> tw(NT), ptw(U, make_float2(1, 0));
   for (int k = 0; k < NT; ++k) { double a = -2.0 * M_PI * k / NT; tw[k] = make_float2((float)cos(a), (float)sin(a)); }
+  for (int e = 1; e < U / 2; ++e) { double a = -M_PI * pair_slot(LOGN, e).j / U; ptw[U / 2 + e] = make_float2((float)cos(a), (float)sin(a)); }
   std::mt19937 rng(LOGN); std::normal_distribution<float> nd;
   std::vector<float> h(2 * U), x(2 * U, 0.f), acc(U);
   for (auto& v : h) v = nd(rng);
   for (int i = 0; i < U; ++i) x[i] = nd(rng);
   for (auto& v : acc) v = nd(rng);
-  std::vector<float4> sp; Emu<LOGN>::spectrum(h.data(), sp, tw.data(), logNT);
-  std::vector<float> out = acc; Emu<LOGN>::tile(x.data(), sp, out.data(), tw.data(), logNT);
+  std::vector<float4> sp; Emu<LOGN>::spectrum(h.data(), sp, tw.data(), ptw.data(), logNT);
+  std::vector<float> out = acc; Emu<LOGN>::tile(x.data(), sp, out.data(), tw.data(), ptw.data(), logNT);
   double worst = 0, scale = 0;
   for (int j = 0; j < U; ++j) { // output j (slot t+1+j): sum_k h[j+U-k] x[k]
     double s = acc[j]; double a = 0;
@@ -75,9 +77,39 @@ template <int LOGN> double run(int logNT) {
   }
   return worst / scale;
 }
+// The real-spectrum items: every position exactly once, bins j and N-j at the
+// named positions, and (N >= 256) sixteen consecutive items touch sixteen
+// distinct LDS bank slots through either position.
+static int check_pairs(int logn) {
+  const int N = 1 << logn;
+  std::vector<int> seen(N, 0);
+  int bad = 0;
+  for (int e = 0; e < N / 2; ++e) {
+    PairSlot ps = pair_slot(logn, e);
+    seen[ps.pj]++; seen[ps.pm]++;
+    if (e == 0) { bad |= !(ps.pj == 0 && ps.pm == 1 && ps.j == 0); continue; }
+    const int kj = rbits(logn, ps.pj), km = rbits(logn, ps.pm);
+    bad |= !(kj == ps.j && ps.j > 0 && ps.j < N / 2 && km == N - ps.j);
+  }
+  for (int i = 0; i < N; ++i) bad |= seen[i] != 1;
+  if (logn >= 8)
+    for (int e0 = 0; e0 < N / 2; e0 += 16) {
+      int mj = 0, mm = 0;
+      for (int i = (e0 == 0 ? 1 : 0); i < 16; ++i) {
+        PairSlot ps = pair_slot(logn, e0 + i);
+        mj |= 1 << (lpad(ps.pj) & 15); mm |= 1 << (lpad(ps.pm) & 15);
+      }
+      const int want = e0 == 0 ? 15 : 16;
+      bad |= __builtin_popcount(mj) != want || __builtin_popcount(mm) != want;
+    }
+  printf("pairs LOGN=%d %s\n", logn, bad ? "BAD" : "ok");
+  return bad;
+}
 int main() {
+  int pbad = 0;
+  for (int logn = 2; logn <= 16; ++logn) pbad |= check_pairs(logn);
   double r[13] = { run<2>(15), run<3>(15), run<4>(15), run<5>(15), run<6>(15), run<7>(15), run<8>(15), run<9>(15), run<10>(15), run<11>(15), run<12>(15), run<13>(15), run<14>(15) };
   int bad = 0;
   for (int i = 0; i < 13; ++i) { printf("LOGN=%d rel err %.3e\n", i + 2, r[i]); if (!(r[i] < 1e-5)) bad = 1; }
-  return bad;
+  return bad | pbad;
 }

@@ -21,3 +21,4 @@ def test_fft_tile_arithmetic_matches_direct_sums(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert r.stdout.count("rel err") == 13
+    assert r.stdout.count(" ok") == 15
