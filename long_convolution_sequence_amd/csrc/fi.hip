@@ -6,6 +6,7 @@
 // "Implementierungsdetails" (graphs per token, filter DFT precomputation,
 // per-size preconfiguration) and the rebuttal page (per-shape, per-size
 // selection of the fastest block implementation by profiling).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -58,9 +59,10 @@ struct Layout {
 
 bool fft_exists(int q, int P) { return q >= kMinFftLog && q <= P - 1; }
 bool direct_exists(int q) { return q <= kMaxDirectLog; }
-// classes wider than one workgroup transform (2^vlog) are split into
-// K = U / 2^vlog sub-blocks
-bool is_sub(int q, int vlog) { return q > vlog; }
+// Class vlog + 1 runs its transform as two halves of 2^vlog points in one
+// workgroup; wider classes are split into K = U / 2^vlog sub-blocks.
+bool is_pair(int q, int vlog) { return q == vlog + 1; }
+bool is_sub(int q, int vlog) { return q > vlog + 1; }
 int sub_k(int q, int vlog) { return 1 << (q - vlog); }
 // float4 entries of class q's spectra per (l, c) row
 size_t spec_row_f4(int q, int vlog) {
@@ -102,10 +104,10 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     }
     for (int q = 0; q < P; ++q) lay.spec[q] = fft_exists(q, P) ? take(rowsMD * spec_row_f4(q, vlog) * 16) : 0;
     // forward sub-block spectra of the widest split class: [M*B*D][U/2] float4
-    lay.scratch = (P - 1 > vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
+    lay.scratch = is_sub(P - 1, vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
     const int nmax_log = std::min(P - 1, vlog);
     lay.logNT = std::max(2, nmax_log + 1);
-    lay.twid = take((size_t(3) << (lay.logNT - 1)) * sizeof(float2));  // twiddles, then pair twiddles
+    lay.twid = take((size_t(2) << lay.logNT) * sizeof(float2));  // twiddles, pair and odd-pair twiddles
     lay.xin = take((size_t)2 * B * D * sizeof(float));
     lay.ylast = take((size_t)L * B * D * sizeof(float));
     lay.stamps = take((size_t)(L + 1) * sizeof(long long));
@@ -243,13 +245,23 @@ hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
     return hipGetLastError();
 }
 
+// Kernel launch that, given events, has the dispatch itself stamp them at the
+// kernel's start and end (exact kernel time, no queueing in between).
+template <typename F, typename... Args>
+void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
 template <int LOGN>
-hipError_t launch_fft_n(fi_ctx *c, int rd, hipStream_t s, int advance) {
+hipError_t launch_fft_n(fi_ctx *c, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
     using S = FftShape<LOGN>;
     const long long tiles = (long long)c->M * c->B * c->D;
     const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_fft_tile<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, rd,
-                       (const float4 *)c->spec[LOGN], advance);
+    launch_k(k_fft_tile<LOGN>, dim3((unsigned)grid), dim3(S::TPB), s, ev0, ev1, c->dev, rd,
+             (const float4 *)c->spec[LOGN], advance);
     return hipGetLastError();
 }
 
@@ -264,45 +276,76 @@ hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long go
 }
 
 template <int LOGV>
-hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
+hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0,
+                            hipEvent_t ev1) {
     const int K = sub_k(q, LOGV);
     const unsigned grid = (unsigned)((long long)c->M * c->B * c->D * K);
-    hipLaunchKernelGGL((k_fft_sub_fwd<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev, rd,
-                       c->scratch, K);
+    launch_k(k_fft_sub_fwd<LOGV>, dim3(grid), dim3(FftShape<LOGV>::TPB), s, ev0, nullptr, c->dev, rd, c->scratch,
+             K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_fft_sub_inv<LOGV>), dim3(grid), dim3(FftShape<LOGV>::TPB), 0, s, c->dev, rd,
-                       (const float4 *)c->scratch, (const float4 *)c->spec[q], K, advance);
+    launch_k(k_fft_sub_inv<LOGV>, dim3(grid), dim3(FftShape<LOGV>::TPB), s, nullptr, ev1, c->dev, rd,
+             (const float4 *)c->scratch, (const float4 *)c->spec[q], K, advance);
     return hipGetLastError();
 }
 
-hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
+template <int LOGM>
+hipError_t launch_fft2_m(fi_ctx *c, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
+    using S = FftShape<LOGM>;
+    const long long tiles = (long long)c->M * c->B * c->D;
+    const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
+    launch_k(k_fft_tile2<LOGM>, dim3((unsigned)grid), dim3(S::TPB), s, ev0, ev1, c->dev, rd,
+             (const float4 *)c->spec[LOGM + 1], advance);
+    return hipGetLastError();
+}
+
+hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
     switch (c->opt.fft_max_log2) {
-        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance);
-        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance);
-        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance);
+        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance, ev0, ev1);
+        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance, ev0, ev1);
+        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_fft(fi_ctx *c, int rd, int q, hipStream_t s, int advance) {
-    if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, rd, q, s, advance);
+// FFT gray blocks of class q; ev0/ev1 (optional) are stamped at the start of
+// the first kernel and the end of the last.
+hipError_t launch_fft(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0 = nullptr,
+                      hipEvent_t ev1 = nullptr) {
+    if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, rd, q, s, advance, ev0, ev1);
+    if (is_pair(q, c->opt.fft_max_log2)) {
+        switch (c->opt.fft_max_log2) {
+            case 12: return launch_fft2_m<12>(c, rd, s, advance, ev0, ev1);
+            case 13: return launch_fft2_m<13>(c, rd, s, advance, ev0, ev1);
+            case 14: return launch_fft2_m<14>(c, rd, s, advance, ev0, ev1);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (q) {
-        case 2: return launch_fft_n<2>(c, rd, s, advance);
-        case 3: return launch_fft_n<3>(c, rd, s, advance);
-        case 4: return launch_fft_n<4>(c, rd, s, advance);
-        case 5: return launch_fft_n<5>(c, rd, s, advance);
-        case 6: return launch_fft_n<6>(c, rd, s, advance);
-        case 7: return launch_fft_n<7>(c, rd, s, advance);
-        case 8: return launch_fft_n<8>(c, rd, s, advance);
-        case 9: return launch_fft_n<9>(c, rd, s, advance);
-        case 10: return launch_fft_n<10>(c, rd, s, advance);
-        case 11: return launch_fft_n<11>(c, rd, s, advance);
-        case 12: return launch_fft_n<12>(c, rd, s, advance);
-        case 13: return launch_fft_n<13>(c, rd, s, advance);
-        case 14: return launch_fft_n<14>(c, rd, s, advance);
+        case 2: return launch_fft_n<2>(c, rd, s, advance, ev0, ev1);
+        case 3: return launch_fft_n<3>(c, rd, s, advance, ev0, ev1);
+        case 4: return launch_fft_n<4>(c, rd, s, advance, ev0, ev1);
+        case 5: return launch_fft_n<5>(c, rd, s, advance, ev0, ev1);
+        case 6: return launch_fft_n<6>(c, rd, s, advance, ev0, ev1);
+        case 7: return launch_fft_n<7>(c, rd, s, advance, ev0, ev1);
+        case 8: return launch_fft_n<8>(c, rd, s, advance, ev0, ev1);
+        case 9: return launch_fft_n<9>(c, rd, s, advance, ev0, ev1);
+        case 10: return launch_fft_n<10>(c, rd, s, advance, ev0, ev1);
+        case 11: return launch_fft_n<11>(c, rd, s, advance, ev0, ev1);
+        case 12: return launch_fft_n<12>(c, rd, s, advance, ev0, ev1);
+        case 13: return launch_fft_n<13>(c, rd, s, advance, ev0, ev1);
+        case 14: return launch_fft_n<14>(c, rd, s, advance, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int LOGM>
+hipError_t launch_spectrum2_m(fi_ctx *c, hipStream_t s, float4 *dst) {
+    using S = FftShape<LOGM>;
+    const long long rows = (long long)c->M * c->D;
+    const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
+    hipLaunchKernelGGL((k_spectrum2<LOGM>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
@@ -321,6 +364,14 @@ hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
+    }
+    if (is_pair(q, vlog)) {
+        switch (vlog) {
+            case 12: return launch_spectrum2_m<12>(c, s, dst);
+            case 13: return launch_spectrum2_m<13>(c, s, dst);
+            case 14: return launch_spectrum2_m<14>(c, s, dst);
+            default: return hipErrorInvalidValue;
+        }
     }
     switch (q) {
         case 2: return launch_spectrum_n<2>(c, s, dst, 0, stride);
@@ -534,8 +585,8 @@ fi_status harvest_events(fi_ctx *c) {
     return FI_OK;
 }
 
-// One FFT-class position launched directly, its gray-block kernels bracketed
-// by events.
+// One FFT-class position launched directly, its gray-block kernels timed by
+// events that their dispatch stamps.
 fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
     const int rd = rd_of(n);
     constexpr size_t kPairs = 4096;
@@ -551,9 +602,7 @@ fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
     HIPCK(c, launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr));
-    HIPCK(c, hipEventRecord(c->ev[2 * i], c->stream));
-    HIPCK(c, launch_fft(c, rd, q, c->stream, 0));
-    HIPCK(c, hipEventRecord(c->ev[2 * i + 1], c->stream));
+    HIPCK(c, launch_fft(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1]));
     HIPCK(c, launch_drain(c, rd, c->stream, 1));
     return FI_OK;
 }
@@ -657,6 +706,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     d.stamps = (long long *)(c->ws + lay.stamps);
     d.twid = (const float2 *)(c->ws + lay.twid);
     d.ptw = d.twid + (size_t(1) << lay.logNT);
+    d.optw = d.ptw + (size_t(1) << (lay.logNT - 1));
     d.M = layers;
     d.B = batch;
     d.D = channels;
@@ -691,7 +741,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     // N = 2^logn the pair twiddle W_{2N}^j of each real-spectrum item
     {
         const size_t nt = size_t(1) << lay.logNT;
-        std::vector<float2> tw(nt + nt / 2, make_float2(1.f, 0.f));
+        std::vector<float2> tw(2 * nt, make_float2(1.f, 0.f));
         const double pi = 3.14159265358979323846;
         for (size_t k = 0; k < nt; ++k) {
             const double a = -2.0 * pi * (double)k / (double)nt;
@@ -702,6 +752,11 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
             for (int e = 1; e < N / 2; ++e) {
                 const double a = -pi * (double)pair_slot(logn, e).j / (double)N;
                 tw[nt + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
+            }
+            // odd halves of 2N-point transforms: W_{4N}^k
+            for (int e = 0; e < N / 2; ++e) {
+                const double a = -pi * (double)odd_slot(logn, e).j / (double)(2 * N);
+                tw[nt + nt / 2 + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
             }
         }
         if (hipMemcpyAsync((void *)d.twid, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice,

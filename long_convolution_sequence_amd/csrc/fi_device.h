@@ -20,6 +20,8 @@
 //   twid  [NT] (float2)  exp(-2 pi i k / NT), generated in fp64 on the host
 //   ptw   [NT/2] (float2) per transform size N: W_{2N}^j of real-spectrum item e
 //         (pair_slot) at N/2 + e, also fp64 on the host
+//   optw  [NT/2] (float2) per half size M: W_{4M}^k of odd-half item e (odd_slot)
+//         at M/2 + e
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,7 +48,8 @@ struct Dev {
     State *st;
     long long *stamps;
     const float2 *twid;
-    const float2 *ptw;  // pair twiddles: W_{2N}^j of item e at ptw[N/2 + e]
+    const float2 *ptw;   // pair twiddles: W_{2N}^j of item e at ptw[N/2 + e]
+    const float2 *optw;  // odd-half pair twiddles: W_{4M}^k of odd item e at optw[M/2 + e]
     int M, B, D;
     int logNT;
     long long L;

@@ -72,6 +72,35 @@ __device__ __forceinline__ float2 mul_w16c(float2 d) {
     }
 }
 
+// d * W_32^K and d * conj(W_32^K) for 0 <= K < 16 (W_32 = exp(-2 pi i / 32)).
+constexpr float kCos16[9] = {1.f,
+                             0.980785280403230449f,   // cos(pi/16)
+                             0.923879532511286756f,   // cos(2 pi/16)
+                             0.831469612302545237f,   // cos(3 pi/16)
+                             0.707106781186547524f,   // cos(4 pi/16)
+                             0.555570233019602225f,   // cos(5 pi/16)
+                             0.382683432365089772f,   // cos(6 pi/16)
+                             0.195090322016128268f,   // cos(7 pi/16)
+                             0.f};
+template <int K>
+__device__ __forceinline__ float2 mul_w32(float2 d) {
+    if constexpr (K % 2 == 0) return mul_w16<K / 2>(d);
+    else {
+        constexpr float c = K < 8 ? kCos16[K] : -kCos16[16 - K];  // cos(K pi / 16)
+        constexpr float s = K < 8 ? kCos16[8 - K] : kCos16[K - 8];  // sin(K pi / 16)
+        return make_float2(d.x * c + d.y * s, d.y * c - d.x * s);
+    }
+}
+template <int K>
+__device__ __forceinline__ float2 mul_w32c(float2 d) {
+    if constexpr (K % 2 == 0) return mul_w16c<K / 2>(d);
+    else {
+        constexpr float c = K < 8 ? kCos16[K] : -kCos16[16 - K];
+        constexpr float s = K < 8 ? kCos16[8 - K] : kCos16[K - 8];
+        return make_float2(d.x * c - d.y * s, d.y * c + d.x * s);
+    }
+}
+
 template <int R, int P>
 constexpr int rev_bits() {
     int r = 0;
@@ -79,15 +108,34 @@ constexpr int rev_bits() {
     return r;
 }
 
-// pw[k] = w^k, k < 2^R, by a product tree of depth <= R.
-template <int R>
-__device__ __forceinline__ void powers(float2 w, float2 (&pw)[1 << R]) {
-    pw[0] = make_float2(1.f, 0.f);
-    if constexpr (R > 0) pw[1] = w;
-    static_for<2, (1 << R)>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        pw[k] = cmul(pw[k / 2], pw[k - k / 2]);
-    });
+// v[rev(k)] *= w^k (CONJ: conj(w)^k) for 0 < k < 2^R.  The powers come in
+// order, w^k = w^(k-4) w^4 from k = 5 on, so at most five of them are live
+// and none is more than five products away from w.
+template <int R, bool CONJ>
+__device__ __forceinline__ void apply_powers(float2 (&v)[1 << R], float2 w) {
+    constexpr int NP = 1 << R;
+    auto mul = [](float2 a, float2 b) { return CONJ ? cmulc(a, b) : cmul(a, b); };
+    if constexpr (NP >= 2) {
+        float2 pk[4];
+        pk[1] = w;
+        v[rev_bits<R, 1>()] = mul(v[rev_bits<R, 1>()], w);
+        if constexpr (NP >= 4) {
+            pk[2] = cmul(w, w);
+            pk[3] = cmul(pk[2], w);
+            v[rev_bits<R, 2>()] = mul(v[rev_bits<R, 2>()], pk[2]);
+            v[rev_bits<R, 3>()] = mul(v[rev_bits<R, 3>()], pk[3]);
+        }
+        if constexpr (NP >= 8) {
+            const float2 w4 = cmul(pk[2], pk[2]);
+            pk[0] = w4;
+            v[rev_bits<R, 4>()] = mul(v[rev_bits<R, 4>()], w4);
+            static_for<5, NP>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                pk[k % 4] = cmul(pk[k % 4], w4);
+                v[rev_bits<R, k>()] = mul(v[rev_bits<R, k>()], pk[k % 4]);
+            });
+        }
+    }
 }
 
 // One group of R radix-2 DIF stages on v[0..2^R): the values sit at element
@@ -116,14 +164,7 @@ __device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
             }
         });
     });
-    if constexpr (TWIDDLE) {
-        float2 pw[1 << R];
-        powers<R>(twiddle(tw, logNT, slog, r), pw);
-        static_for<1, (1 << R)>([&](auto pc) {
-            constexpr int p = decltype(pc)::value;
-            v[p] = cmul(v[p], pw[rev_bits<R, p>()]);
-        });
-    }
+    if constexpr (TWIDDLE) apply_powers<R, false>(v, twiddle(tw, logNT, slog, r));
 }
 
 // Inverse of dif_group up to the factor 2^R: conjugate outer twiddles, then
@@ -131,14 +172,7 @@ __device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
 template <int R, bool TWIDDLE = true>
 __device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
                                           const float2 *__restrict__ tw, int logNT) {
-    if constexpr (TWIDDLE) {
-        float2 pw[1 << R];
-        powers<R>(twiddle(tw, logNT, slog, r), pw);
-        static_for<1, (1 << R)>([&](auto pc) {
-            constexpr int p = decltype(pc)::value;
-            v[p] = cmulc(v[p], pw[rev_bits<R, p>()]);
-        });
-    }
+    if constexpr (TWIDDLE) apply_powers<R, true>(v, twiddle(tw, logNT, slog, r));
     static_for<0, R>([&](auto tc) {
         constexpr int t = R - 1 - decltype(tc)::value;
         constexpr int half = (1 << R) >> (t + 1);
@@ -259,6 +293,22 @@ __host__ __device__ inline PairSlot pair_slot(int logn, int e) {
     const int k1 = rbits(logn, p1);
     if (k1 < N / 2) return {p1, p2, k1};
     return {p2, p1, N - k1};
+}
+
+// Transforms of N = 2M points done as two M-point halves.  The first radix-2
+// stage of a decimation in frequency splits the bins by parity: the even bins
+// are the M-point transform of (c_lo + c_hi), the odd bins that of
+// (c_lo - c_hi) W_N^m.  Bin k pairs with N-k, which has the same parity, so
+// each half keeps its own real-spectrum step.  In the even half, bin 2j is
+// bin j of an M-point transform and pairs as in pair_slot (with
+// W_{2N}^{2j} = W_{2M}^j).  In the odd half, bin 2k'+1 pairs with
+// 2(M-1-k')+1, and rev(M-1-k') = M-1-rev(k'): positions p and M-1-p.  Item
+// e in [0, M/2) takes the even position 2e (its bin k' = rev(2e) is below M/2)
+// and its mirror M-1-2e; sixteen consecutive items touch sixteen distinct LDS
+// bank slots.  odd_slot(e).j is the bin 2k'+1 of the N-point transform.
+__host__ __device__ inline PairSlot odd_slot(int logm, int e) {
+    const int M = 1 << logm;
+    return {2 * e, M - 1 - 2 * e, 2 * rbits(logm, 2 * e) + 1};
 }
 
 // Real-spectrum pairing.  C holds the complex transform of c_k = a_{2k} + i a_{2k+1}

@@ -20,5 +20,6 @@ def test_fft_tile_arithmetic_matches_direct_sums(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     print(r.stdout)
     assert r.returncode == 0, r.stdout
-    assert r.stdout.count("rel err") == 13
+    assert r.stdout.count("rel err") == 24
     assert r.stdout.count(" ok") == 15
+    assert r.stdout.count("two halves") == 11
