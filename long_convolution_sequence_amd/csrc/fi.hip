@@ -340,11 +340,11 @@ hipError_t launch_fft(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipE
 }
 
 template <int LOGM>
-hipError_t launch_spectrum2_m(fi_ctx *c, hipStream_t s, float4 *dst) {
+hipError_t launch_spectrum2_m(fi_ctx *c, hipStream_t s, float4 *dst, long long goff, long long stride) {
     using S = FftShape<LOGM>;
     const long long rows = (long long)c->M * c->D;
     const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_spectrum2<LOGM>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst);
+    hipLaunchKernelGGL((k_spectrum2<LOGM>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst, goff, stride);
     return hipGetLastError();
 }
 
@@ -367,9 +367,9 @@ hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
     }
     if (is_pair(q, vlog)) {
         switch (vlog) {
-            case 12: return launch_spectrum2_m<12>(c, s, dst);
-            case 13: return launch_spectrum2_m<13>(c, s, dst);
-            case 14: return launch_spectrum2_m<14>(c, s, dst);
+            case 12: return launch_spectrum2_m<12>(c, s, dst, 0, stride);
+            case 13: return launch_spectrum2_m<13>(c, s, dst, 0, stride);
+            case 14: return launch_spectrum2_m<14>(c, s, dst, 0, stride);
             default: return hipErrorInvalidValue;
         }
     }

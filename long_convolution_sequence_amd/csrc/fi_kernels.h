@@ -395,35 +395,106 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
 }
 
 // ---------------------------------------------------------------------------
-// Gray blocks of U = 2M positions (M = 2^LOGM, the widest one-workgroup
-// transform): the U-point complex transform is carried by its two M-point
-// halves in turn (odd bins, then even bins; see odd_slot), so that only M
-// points are ever in LDS.  Each half multiplies its bins by the matching half
-// of the filter spectrum, transforms back and adds its part of the block's
-// upper half into the accumulators: z = e - W_U^{-m} o for outputs m < M
-// (the accumulators are read and written once per half, in that fixed order).
-//   spec: per (l, c), M float4: M/2 even-half items (pair_slot order, with
-//   item 0 = (G_0, G_U, G_{U/2})), then M/2 odd-half items; scaled by 1/U.
+// Transforms of 2M points (M = 2^LOGM) carried by their two M-point halves
+// in turn (odd bins, then even bins; see odd_slot), so that only M points are
+// ever in LDS.  In the item order of both halves a spectrum takes M float4:
+// M/2 even-half items (pair_slot order, item 0 = (G_0, G_2M, G_M)), then M/2
+// odd-half items.
+// ---------------------------------------------------------------------------
+
+// Forward transform of one half into X (bins bit-reversed, no trailing
+// barrier).  Input: c = lo + hi (HI) or lo; the odd half takes c W_{2M}^m.
+template <int LOGM, bool ODD, bool HI>
+__device__ __forceinline__ void half_forward(const Dev &p, float2 *X, int lt, bool active, const float2 *lo,
+                                             const float2 *hi) {
+    using S = FftShape<LOGM>;
+    constexpr int R0 = S::R0, QLOG0 = S::QLOG0;
+    static_assert(R0 == 4, "two-half transforms have M >= 16");
+    // W_{2M}^i at i = lt + m M/16 is W_{2M}^lt W_32^m
+    const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGM + 1, lt) : make_float2(1.f, 0.f);
+    float2 v[16];
+    static_for<0, 16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const int i = lt + (m << QLOG0);
+        float2 c = active ? lo[i] : make_float2(0.f, 0.f);
+        if constexpr (HI) {
+            const float2 b = active ? hi[i] : make_float2(0.f, 0.f);
+            c = ODD ? csub(c, b) : cadd(c, b);
+        }
+        v[m] = ODD ? mul_w32<m>(cmul(c, wl)) : c;
+    });
+    dif_group<R0>(v, lt, LOGM, p.twid, p.logNT);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    forward_groups<LOGM, 1>(X, lt, p.twid, p.logNT);
+}
+
+// Inverse transform of one half from X (items already re-packed; the caller
+// has synchronised) and its accumulation into dst[0..M): the odd half
+// subtracts W_{2M}^{-m} v, the even half adds v.
+template <int LOGM, bool ODD>
+__device__ __forceinline__ void half_inverse_acc(const Dev &p, float2 *X, int lt, bool active, float2 *dst) {
+    using S = FftShape<LOGM>;
+    constexpr int R0 = S::R0, QLOG0 = S::QLOG0;
+    inverse_groups<LOGM, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    float2 v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = X[lpad(lt + (m << QLOG0))];
+    dit_group<R0>(v, lt, LOGM, p.twid, p.logNT);
+    if (!active) return;
+    const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGM + 1, lt) : make_float2(1.f, 0.f);
+    // in four runs of four, so that the accumulators never all occupy registers
+    static_for<0, 4>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        float2 acc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = dst[lt + ((4 * r + k) << QLOG0)];
+        static_for<0, 4>([&](auto kc) {
+            constexpr int m = 4 * r + decltype(kc)::value;
+            const float2 a = acc[decltype(kc)::value];
+            dst[lt + (m << QLOG0)] = ODD ? csub(a, mul_w32c<m>(cmulc(v[m], wl))) : cadd(a, v[m]);
+        });
+        asm volatile("" ::: "memory");
+    });
+}
+
+template <int LOGM, bool ODD>
+__device__ __forceinline__ PairSlot half_slot(int e) {
+    return ODD ? odd_slot(LOGM, e) : pair_slot(LOGM, e);
+}
+template <int LOGM, bool ODD>
+__device__ __forceinline__ float2 half_w(const Dev &p, int e) {
+    return (ODD ? p.optw : p.ptw)[(1 << (LOGM - 1)) + e];
+}
+
+// Real bins of item e of a forward half in X, unscaled.
+template <int LOGM, bool ODD>
+__device__ __forceinline__ float4 half_bins(const Dev &p, const float2 *X, int e) {
+    if (!ODD && e == 0) {
+        const float2 C0 = X[0];
+        const float2 Ch = X[lpad(1)];
+        return make_float4(C0.x + C0.y, C0.x - C0.y, Ch.x, -Ch.y);
+    }
+    const PairSlot ps = half_slot<LOGM, ODD>(e);
+    float2 A1, A2;
+    real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], half_w<LOGM, ODD>(p, e), A1, A2);
+    return make_float4(A1.x, A1.y, A2.x, A2.y);
+}
+
+// ---------------------------------------------------------------------------
+// Gray blocks of U = 2M positions, M = 2^LOGM the widest one-workgroup
+// transform: each half multiplies its bins by the matching half of the filter
+// spectrum, transforms back and adds its part of the block's upper half into
+// the accumulators, z = e - W_U^{-m} o for outputs m < M (the accumulators
+// are read and written once per half, in that fixed order).
+//   spec: per (l, c), M float4 in the two-half item order, scaled by 1/U.
 // ---------------------------------------------------------------------------
 template <int LOGM, bool ODD>
 __device__ __forceinline__ void tile2_half(const Dev &p, float2 *X, int lt, bool active, const float2 *xsrc,
                                            float2 *adst, const float4 *sp) {
     using S = FftShape<LOGM>;
-    constexpr int M = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0;
-    constexpr int LOGU = LOGM + 1;
-    static_assert(R0 == 4, "two-half blocks have M >= 16");
-    // W_U^i at i = lt + m M/16 is W_U^lt W_32^m
-    const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGU, lt) : make_float2(1.f, 0.f);
-    float2 v[16];
-    static_for<0, 16>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        const float2 x = active ? xsrc[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
-        v[m] = ODD ? mul_w32<m>(cmul(x, wl)) : x;
-    });
-    dif_group<R0>(v, lt, LOGM, p.twid, p.logNT);
-#pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
-    forward_groups<LOGM, 1>(X, lt, p.twid, p.logNT);
+    constexpr int M = S::N, TT = S::TT;
+    half_forward<LOGM, ODD, false>(p, X, lt, active, xsrc, nullptr);
     constexpr int PAIRS = (M / 2 + TT - 1) / TT;
     float4 gs[PAIRS];
 #pragma unroll
@@ -445,9 +516,9 @@ __device__ __forceinline__ void tile2_half(const Dev &p, float2 *X, int lt, bool
             X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
             X[lpad(1)] = cmulc(Ch, make_float2(g.z, g.w));
         } else {
-            const PairSlot ps = ODD ? odd_slot(LOGM, e) : pair_slot(LOGM, e);
+            const PairSlot ps = half_slot<LOGM, ODD>(e);
             const int p1 = lpad(ps.pj), p2 = lpad(ps.pm);
-            const float2 W = (ODD ? p.optw : p.ptw)[M / 2 + e];
+            const float2 W = half_w<LOGM, ODD>(p, e);
             float2 A1, A2, D1, D2;
             real_bins(X[p1], X[p2], W, A1, A2);
             pack_inverse(cmul(A1, make_float2(g.x, g.y)), cmul(A2, make_float2(g.z, g.w)), W, D1, D2);
@@ -456,25 +527,7 @@ __device__ __forceinline__ void tile2_half(const Dev &p, float2 *X, int lt, bool
         }
     }
     __syncthreads();
-    inverse_groups<LOGM, S::NPASS - 1>(X, lt, p.twid, p.logNT);
-#pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_group<R0>(v, lt, LOGM, p.twid, p.logNT);
-    if (active) {
-        // in four runs of four, so that the accumulators never all occupy registers
-        static_for<0, 4>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            float2 acc[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) acc[k] = adst[lt + ((4 * r + k) << QLOG0)];
-            static_for<0, 4>([&](auto kc) {
-                constexpr int m = 4 * r + decltype(kc)::value;
-                const float2 a = acc[decltype(kc)::value];
-                adst[lt + (m << QLOG0)] = ODD ? csub(a, mul_w32c<m>(cmulc(v[m], wl))) : cadd(a, v[m]);
-            });
-            asm volatile("" ::: "memory");
-        });
-    }
+    half_inverse_acc<LOGM, ODD>(p, X, lt, active, adst);
 }
 
 template <int LOGM>
@@ -504,52 +557,31 @@ k_fft_tile2(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
     finish_position(p, n, advance);
 }
 
-// Filter spectra of a two-half class: taps g_r = h[r], r in [0, 2U), packed
-// into U complex points c; even half from c_lo + c_hi, odd half from
-// (c_lo - c_hi) W_U^m, each in its item order, scaled by 1/U.
+// Filter spectra in the two-half item order: for every (l, c) row the taps
+// g_r = h[goff + r], r in [0, 4M), packed into 2M complex points, scaled by
+// 1/(2M), at spec + row * row_stride.
 template <int LOGM>
-__global__ void __launch_bounds__(FftShape<LOGM>::TPB) k_spectrum2(Dev p, float4 *__restrict__ spec) {
+__global__ void __launch_bounds__(FftShape<LOGM>::TPB) k_spectrum2(Dev p, float4 *__restrict__ spec, long long goff,
+                                                                   long long row_stride) {
     using S = FftShape<LOGM>;
-    constexpr int M = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0;
-    constexpr int LOGU = LOGM + 1;
-    static_assert(R0 == 4, "two-half blocks have M >= 16");
+    constexpr int M = S::N, TT = S::TT;
     __shared__ float2 smem[S::LDS];
     const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
     const long long rows = (long long)p.M * p.D;
     const long long rowi = (long long)blockIdx.x * S::PER_BLOCK + team;
     const bool active = rowi < rows;
     float2 *X = smem + team * lds_len(M);
-    const float2 *src = reinterpret_cast<const float2 *>(p.filt + (size_t)rowi * (size_t)p.L);
-    float4 *dst = spec + (size_t)rowi * M;
+    const float2 *src = reinterpret_cast<const float2 *>(p.filt + (size_t)rowi * (size_t)p.L + goff);
+    float4 *dst = spec + (size_t)rowi * (size_t)row_stride;
     const float inv = 1.0f / (float)(2 * M);
     static_for<0, 2>([&](auto hc) {
         constexpr bool ODD = decltype(hc)::value == 0;
-        const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGU, lt) : make_float2(1.f, 0.f);
-        float2 v[16];
-        static_for<0, 16>([&](auto mc) {
-            constexpr int m = decltype(mc)::value;
-            const int i = lt + (m << QLOG0);
-            const float2 lo = active ? src[i] : make_float2(0.f, 0.f);
-            const float2 hi = active ? src[i + M] : make_float2(0.f, 0.f);
-            v[m] = ODD ? mul_w32<m>(cmul(csub(lo, hi), wl)) : cadd(lo, hi);
-        });
         __syncthreads();  // the previous half's reads of X are done
-        dif_group<R0>(v, lt, LOGM, p.twid, p.logNT);
-#pragma unroll
-        for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
-        forward_groups<LOGM, 1>(X, lt, p.twid, p.logNT);
+        half_forward<LOGM, ODD, true>(p, X, lt, active, src, src + M);
         __syncthreads();
         for (int e = lt; e < M / 2 && active; e += TT) {
-            if (!ODD && e == 0) {
-                const float2 C0 = X[0];
-                const float2 Ch = X[lpad(1)];
-                dst[0] = make_float4((C0.x + C0.y) * inv, (C0.x - C0.y) * inv, Ch.x * inv, -Ch.y * inv);
-            } else {
-                const PairSlot ps = ODD ? odd_slot(LOGM, e) : pair_slot(LOGM, e);
-                float2 A1, A2;
-                real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], (ODD ? p.optw : p.ptw)[M / 2 + e], A1, A2);
-                dst[(ODD ? M / 2 : 0) + e] = make_float4(A1.x * inv, A1.y * inv, A2.x * inv, A2.y * inv);
-            }
+            const float4 b = half_bins<LOGM, ODD>(p, X, e);
+            dst[(ODD ? M / 2 : 0) + e] = make_float4(b.x * inv, b.y * inv, b.z * inv, b.w * inv);
         }
     });
 }
