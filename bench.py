@@ -53,10 +53,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(w):
-    """Per-launch HBM traffic of the FFT gray blocks from committed PMC summaries,
-    only if they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "fft_tile_traffic_L131072.json")
+def measured_traffic(w, launches_by_class):
+    """Per-launch HBM traffic (read + write bytes) of the FFT gray blocks, from the
+    committed PMC summary of each class, weighted like the timed launches; only
+    if the summary was taken on the current kernel sources."""
+    path = TRAFFIC_PATH
     if not os.path.exists(path):
         return None
     try:
@@ -65,7 +66,11 @@ def measured_traffic(w):
         return None
     if d.get("kernel_source_hash") != kernel_source_hash() or d.get("workload") != w.name:
         return None
-    return d.get("bytes_per_launch_aggregate")
+    per = {r["q"]: r["read_bytes"] + r["write_bytes"] for r in d.get("per_class", [])}
+    n = sum(launches_by_class.values())
+    if n == 0 or any(q not in per for q in launches_by_class):
+        return None
+    return round(sum(per[q] * k for q, k in launches_by_class.items()) / n)
 
 
 def cpu_baseline(w, h, target_s=12.0):
@@ -107,6 +112,111 @@ def cpu_baseline(w, h, target_s=12.0):
     }
 
 
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "fft_tile_traffic_L131072.json")
+COPY_MIB = 1024
+
+
+def traffic_run(args):
+    """The workload's FFT gray-block classes, each launched once more after a
+    warm-up, then a plain device-to-device copy of COPY_MIB MiB (twice): run
+    under rocprofv3 --pmc FETCH_SIZE and again under --pmc WRITE_SIZE, the copy
+    gives each counter's scale (bytes it reads for known bytes moved)."""
+    import torch
+
+    from long_convolution_sequence_amd import fi, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    h = workloads.filters(w)
+    ctx = fi.Context(torch.from_numpy(h).cuda(), w.B)
+    fft = [q for (q, p, _, _) in ctx.tau_table() if p == fi.PATH_FFT]
+    for q in fft:
+        log(f"traffic run: class {q} (U={1 << q})")
+        ctx.time_block(q, fi.PATH_FFT, reps=1)
+    ctx.close()
+    src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"traffic run: copied {COPY_MIB} MiB twice; FFT classes {fft}")
+
+
+def traffic_summary(args):
+    """Per-launch HBM traffic of the FFT gray blocks from the two PMC runs of
+    --traffic-run (counter_collection CSVs), written to TRAFFIC_PATH."""
+    import csv
+    import re
+
+    from long_convolution_sequence_amd import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    copy_kib = COPY_MIB * 1024
+
+    def load(path, counter):
+        per = {}     # class -> list of KiB per launch (split classes: fwd + inv of one launch)
+        copies = []
+        rows = list(csv.DictReader(open(path)))
+        by_kernel = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            name, v, grid = r["Kernel_Name"], float(r["Counter_Value"]), int(r["Grid_Size"])
+            if "copyBuffer" in name:
+                copies.append((int(r["Dispatch_Id"]), v))
+                continue
+            m = re.search(r"k_fft_(tile2|tile|sub_fwd|sub_inv)<(\d+)>", name)
+            if not m:
+                continue
+            kind, lg = m.group(1), int(m.group(2))
+            if kind == "tile":
+                q = lg
+            elif kind == "tile2":
+                q = lg + 1
+            else:
+                tpb = max(256, (1 << lg) // 16)
+                k = grid // (w.M * w.B * w.D * tpb)
+                q = lg + k.bit_length() - 1
+            by_kernel.setdefault((q, kind), []).append(v)
+        for (q, kind), vs in by_kernel.items():
+            per.setdefault(q, 0.0)
+            per[q] += sum(vs) / len(vs)
+        # the calibration copies are the last two copy dispatches
+        last = [v for _, v in sorted(copies)[-2:]]
+        return per, sum(last) / len(last)
+
+    fetch, fetch_copy = load(args.traffic_summary[0], "FETCH_SIZE")
+    write, write_copy = load(args.traffic_summary[1], "WRITE_SIZE")
+    f_scale = copy_kib / fetch_copy
+    w_scale = copy_kib / write_copy
+    classes = sorted(set(fetch) & set(write))
+    rows = []
+    for q in classes:
+        U = 1 << q
+        rd = fetch[q] * f_scale * 1024
+        wr = write[q] * w_scale * 1024
+        alg = fft_alg_bytes(w, U)
+        rows.append({"q": q, "U": U, "read_bytes": round(rd), "write_bytes": round(wr),
+                     "alg_bytes": alg, "ratio": round((rd + wr) / alg, 3)})
+    out = {
+        "workload": w.name,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "calibration": f"device-to-device copy of {COPY_MIB} MiB: FETCH_SIZE read {fetch_copy:.0f} KiB, "
+                       f"WRITE_SIZE {write_copy:.0f} KiB per dispatch",
+        "per_class": rows,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o pmc -- python3 bench.py --traffic-run",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o pmc -- python3 bench.py --traffic-run",
+            "python3 bench.py --traffic-summary <fetch csv> <write csv>",
+        ],
+    }
+    with open(TRAFFIC_PATH, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,11 +226,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lazy", action="store_true")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="launch each FFT class once and a calibration copy (run under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the FFT traffic summary from the two PMC runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the mixer shards over channels with no communication, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_run:
+        traffic_run(args)
+        return
 
     import torch
 
@@ -185,7 +305,7 @@ def main():
         tot_ms += blk_ms[q]
     launches = int(blk_n.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9 if tot_ms > 0 else 0.0
-    traffic = measured_traffic(w)
+    traffic = measured_traffic(w, {q: int(blk_n[q]) for q in range(w.P) if blk_n[q] > 0})
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
