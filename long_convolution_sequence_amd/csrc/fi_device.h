@@ -105,9 +105,8 @@ __device__ __forceinline__ void finish_position(const Dev &p, long long n, int a
 // Copy helper: every thread of the block moves elements tid, tid+bs, ... of a
 // strided index space; loads are issued in batches of 16 before any store, so a
 // copy costs a few memory round trips instead of one per element.
-template <typename Load, typename Store>
+template <int BATCH = 16, typename Load, typename Store>
 __device__ __forceinline__ void batched_copy(int total, int tid, int bs, Load ld, Store st) {
-    constexpr int BATCH = 16;
     for (int base = tid; base < total; base += BATCH * bs) {
         float v[BATCH];
 #pragma unroll

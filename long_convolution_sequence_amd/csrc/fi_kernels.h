@@ -118,10 +118,11 @@ __global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const flo
                 run_chain(p, n, chain, l0, l1, xext, yext, xw + (U - 1) * kLanes + lane, U * kLanes, rowx != 0);
         } else {
             // waves 1..: stage the input window, the taps and the pending outputs
+            // (eight loads in flight per thread: fewer measured slower, more too)
             const int t2 = threadIdx.x - kLanes, b2 = blockDim.x - kLanes;
             constexpr int KW = CHAIN ? U - 1 : U;     // window entries taken from the ring
             constexpr int KD = KW > 0 ? KW : 1;       // divisor (no entries when KW is 0)
-            batched_copy(nl * KW * kLanes, t2, b2,
+            batched_copy<8>(nl * KW * kLanes, t2, b2,
                 [&](int i) {
                     const int ln = i & (kLanes - 1), k = (i / kLanes) % KD, li = (i / kLanes) / KD;
                     return cb + ln < BD ? p.xr[ring(p, n - U + 1 + k, l0 + li) + cb + ln] : 0.f;
@@ -130,13 +131,13 @@ __global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const flo
                     const int ln = i & (kLanes - 1), k = (i / kLanes) % KD, li = (i / kLanes) / KD;
                     xw[(li * U + k) * kLanes + ln] = v;
                 });
-            batched_copy(nl * TAPS * kLanes, t2, b2,
+            batched_copy<8>(nl * TAPS * kLanes, t2, b2,
                 [&](int i) {
                     const int ln = i & (kLanes - 1), m = (i / kLanes) % TAPS, li = (i / kLanes) / TAPS;
                     return cb + ln < BD ? p.hh[head(p, l0 + li, 1 + m, (cb + ln) % p.D)] : 0.f;
                 },
                 [&](int i, float v) { tp[i] = v; });
-            batched_copy(nl * U * kLanes, t2, b2,
+            batched_copy<8>(nl * U * kLanes, t2, b2,
                 [&](int i) {
                     const int ln = i & (kLanes - 1), j = (i / kLanes) % U, li = (i / kLanes) / U;
                     return cb + ln < BD ? p.ar[ring(p, n + 1 + j, l0 + li) + cb + ln] : 0.f;
