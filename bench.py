@@ -225,6 +225,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lazy", action="store_true")
+    ap.add_argument("--no-defer-leg", action="store_true", help="skip the generation with deferred split blocks")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
     ap.add_argument("--traffic-run", action="store_true",
                     help="launch each FFT class once and a calibration copy (run under rocprofv3 --pmc)")
@@ -305,6 +306,26 @@ def main():
         tot_ms += blk_ms[q]
     launches = int(blk_n.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9 if tot_ms > 0 else 0.0
+
+    # one more generation with the later sub-blocks of split gray blocks
+    # deferred to the context's second stream (large-block latency smoothing)
+    defer = None
+    if not args.no_defer_leg:
+        ctx.set_defer_wide(True)
+        dt = one_step()
+        dl = np.diff(ctx.stamps(1, L).astype(np.float64)) / 100.0
+        ctx.block_times(clear=True)
+        ctx.set_defer_wide(False)
+        top = w.P - 1
+        dcls = cls[:L - 1]
+        defer = {"tokens_per_s": round(L * w.B / dt, 1),
+                 "latency_us": {"p50": round(float(np.percentile(dl, 50)), 2),
+                                "p99": round(float(np.percentile(dl, 99)), 2),
+                                "max": round(float(dl.max()), 1),
+                                f"class_{top}_median": round(float(np.median(dl[dcls == top])), 1)},
+                 "note": "one generation with fi_options.defer_wide on: a split gray block computes its "
+                         "first output sub-block before the next position and the rest on a second "
+                         "stream; not part of the timed steps above"}
     traffic = measured_traffic(w, {q: int(blk_n[q]) for q in range(w.P) if blk_n[q] > 0})
     roofline = {
         "bound": "hbm",
@@ -363,6 +384,7 @@ def main():
                        "max": round(float(lat.max()), 1),
                        "per_class_median": per_class},
         "roofline": roofline,
+        "defer_wide": defer,
         "lazy_gpu": lazy,
         "cpu_baseline": cpu,
     }

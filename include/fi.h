@@ -90,12 +90,20 @@ typedef struct fi_options {
                               multiples of 2^k (default 6; 0 disables) */
     int filters_on_device; /* 1: the filters pointer given to fi_init is device memory */
     int fft_max_log2;      /* widest gray block done as one workgroup transform, as
-                              log2(U) in [12, 14] (default 14: 128 KB of LDS); wider
-                              blocks are split into sub-blocks of that width */
+                              log2(U) in [12, 14] (default 14: 128 KB of LDS); the
+                              next class runs as two halves of that width in one
+                              workgroup, wider blocks are split into sub-blocks of
+                              that width */
     int time_blocks;       /* 1: fi_generate brackets every FFT gray-block launch with
-                              HIP events on the context stream (read with
+                              HIP events stamped by the launches themselves (read with
                               fi_block_times); those positions then bypass graphs */
-    int reserved[6];       /* must be zero */
+    int defer_wide;        /* 1: a split gray block at position n computes only its
+                              first output sub-block (V positions) before position
+                              n+1; the others run on a second stream of the context,
+                              overlapping positions n+1 .. n+V-1, and the context
+                              stream waits for them before position n+V.  Cuts the
+                              latency of that position; default 0 */
+    int reserved[5];       /* must be zero */
 } fi_options;
 
 /* Fill *opt with the defaults listed above. */
@@ -134,6 +142,14 @@ fi_status fi_destroy(fi_ctx *ctx);
 /* Back to position 0 with all activations cleared; filters, spectra and the
  * block-path table are kept. */
 fi_status fi_reset(fi_ctx *ctx);
+
+/* Turn fi_options.defer_wide on (1) or off (0) for the following positions.
+ * Large-block latency (Flash Inference summary page, "Hauptergebnisse": the
+ * per-token time spikes at the positions of the widest blocks): with it on, a
+ * split gray block puts its later output sub-blocks on the context's second
+ * stream.  Any deferred work still running is joined into the context stream
+ * first.  FI_EINVAL for other values. */
+fi_status fi_set_defer_wide(fi_ctx *ctx, int on);
 
 /* Produce the next position n = fi_position()+1 (Algorithm 2 for one i).
  *   x_t: device fp32 [B][D], the layer-0 input x^0_n; NULL = feedback

@@ -124,6 +124,12 @@ struct fi_ctx {
     fi_options opt{};
     hipStream_t stream = nullptr;
     hipStream_t cap = nullptr;  // private stream used only for graph capture
+    // Deferred tails of split gray blocks: output sub-blocks 1..K-1 of a split
+    // block at n run on `side` while positions n+1 .. n+V-1 proceed; the
+    // stream joins `ev_side` before position side_until = n+V.
+    hipStream_t side = nullptr;
+    hipEvent_t ev_split = nullptr, ev_side = nullptr;
+    int64_t side_until = 0;
     bool own_ws = false;
     char *ws = nullptr;
     Layout lay;
@@ -144,6 +150,7 @@ struct fi_ctx {
     // FFT gray-block timing: recorded event pairs not yet read, and the sums
     std::vector<hipEvent_t> ev;
     std::vector<int> ev_class;
+    std::vector<int> ev_count;  // 1: the pair counts as one launch of its class
     size_t ev_used = 0;
     double blk_ms[kMaxP] = {0};
     int64_t blk_count[kMaxP] = {0};
@@ -275,18 +282,38 @@ hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long go
     return hipGetLastError();
 }
 
+// Split class q.  Without `defer`: both kernels on s.  With `defer` (the
+// position n known): the forward kernel and output sub-block 0 on s, output
+// sub-blocks 1..K-1 on the side stream after the forward kernel, timed by
+// dv0/dv1 when given.
 template <int LOGV>
-hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0,
-                            hipEvent_t ev1) {
+hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
+                            int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
     const int K = sub_k(q, LOGV);
-    const unsigned grid = (unsigned)((long long)c->M * c->B * c->D * K);
-    launch_k(k_fft_sub_fwd<LOGV>, dim3(grid), dim3(FftShape<LOGV>::TPB), s, ev0, nullptr, c->dev, rd, c->scratch,
-             K);
+    const long long rows = (long long)c->M * c->B * c->D;
+    const dim3 blk(FftShape<LOGV>::TPB);
+    launch_k(k_fft_sub_fwd<LOGV>, dim3((unsigned)(rows * K)), blk, s, ev0, nullptr, c->dev, rd, c->scratch, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_k(k_fft_sub_inv<LOGV>, dim3(grid), dim3(FftShape<LOGV>::TPB), s, nullptr, ev1, c->dev, rd,
-             (const float4 *)c->scratch, (const float4 *)c->spec[q], K, advance);
-    return hipGetLastError();
+    const float4 *A = c->scratch, *G = c->spec[q];
+    if (!defer) {
+        launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)(rows * K)), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, K,
+                 0LL, advance);
+        return hipGetLastError();
+    }
+    launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)rows), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, 1, 0LL,
+             advance);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the deferred sub-blocks start once sub-block 0 is done, so they never
+    // compete with the position's critical path
+    if ((e = hipEventRecord(c->ev_split, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(c->side, c->ev_split, 0)) != hipSuccess) return e;
+    launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)(rows * (K - 1))), blk, c->side, dv0, dv1, c->dev, rd, A, G, K, 1,
+             K - 1, (long long)defer, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(c->ev_side, c->side)) != hipSuccess) return e;
+    c->side_until = defer + (int64_t(1) << LOGV);
+    return hipSuccess;
 }
 
 template <int LOGM>
@@ -299,11 +326,12 @@ hipError_t launch_fft2_m(fi_ctx *c, int rd, hipStream_t s, int advance, hipEvent
     return hipGetLastError();
 }
 
-hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
+                          int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
     switch (c->opt.fft_max_log2) {
-        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance, ev0, ev1);
-        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance, ev0, ev1);
-        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance, ev0, ev1);
+        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
+        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
+        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -394,13 +422,18 @@ hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
 // All kernels of one position of class q (q == P: the last position, red cells only).
 //   direct class:  [red cells + direct gray block]
 //   FFT class:     [red cells + ring -> history copy] [FFT gray block] [drain]
+// defer > 0 (the position n): a split gray block leaves its later output
+// sub-blocks to the side stream.
 template <bool CHAIN>
 hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
-                             int advance) {
+                             int advance, int64_t defer = 0) {
     if (q >= c->P) return launch_direct<CHAIN>(c, rd, -1, s, xext, yext, advance);
     if (q < c->qd) return launch_direct<CHAIN>(c, rd, q, s, xext, yext, advance);
     hipError_t e = launch_red_fft<CHAIN>(c, rd, s, xext, yext);
-    if (e == hipSuccess) e = launch_fft(c, rd, q, s, 0);
+    if (defer && !c->opt.defer_wide) defer = 0;
+    if (e == hipSuccess)
+        e = defer && is_sub(q, c->opt.fft_max_log2) ? launch_fft_sub(c, rd, q, s, 0, nullptr, nullptr, defer)
+                                                    : launch_fft(c, rd, q, s, 0);
     if (e == hipSuccess) e = launch_drain(c, rd, s, advance);
     return e;
 }
@@ -408,7 +441,7 @@ hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const floa
 // Hyena-style block position: per layer projection + red cell, GELU up,
 // down; then the output / feedback; then every layer's gray block.
 hipError_t launch_hyena_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
-                                 int advance) {
+                                 int advance, int64_t defer = 0) {
     const int B = c->B, D = c->D;
     const size_t lds_d = (size_t)B * D * sizeof(float), lds_4d = 4 * lds_d;
     for (int l = 0; l < c->M; ++l) {
@@ -420,18 +453,18 @@ hipError_t launch_hyena_position(fi_ctx *c, int rd, int q, hipStream_t s, const 
     hipLaunchKernelGGL(k_hy_out, dim3(1), dim3(256), 0, s, c->dev, rd, yext);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, advance);
+    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, advance, defer);
 }
 
 hipError_t launch_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
-                           int advance) {
-    if (c->opt.map == FI_MAP_HYENA) return launch_hyena_position(c, rd, q, s, xext, yext, advance);
-    return launch_position_t<true>(c, rd, q, s, xext, yext, advance);
+                           int advance, int64_t defer = 0) {
+    if (c->opt.map == FI_MAP_HYENA) return launch_hyena_position(c, rd, q, s, xext, yext, advance, defer);
+    return launch_position_t<true>(c, rd, q, s, xext, yext, advance, defer);
 }
 
 // Gray blocks only (external-block mode): the layer inputs at n are in place.
-hipError_t launch_tiles(fi_ctx *c, int rd, int q, hipStream_t s) {
-    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, 1);
+hipError_t launch_tiles(fi_ctx *c, int rd, int q, hipStream_t s, int64_t defer = 0) {
+    return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, 1, defer);
 }
 
 // Parity slot read by the kernels of position n.
@@ -575,11 +608,12 @@ void destroy_graphs(fi_ctx *c) {
 fi_status harvest_events(fi_ctx *c) {
     if (c->ev_used == 0) return FI_OK;
     HIPCK(c, hipStreamSynchronize(c->stream));
+    HIPCK(c, hipStreamSynchronize(c->side));
     for (size_t i = 0; i < c->ev_used; ++i) {
         float ms = 0.f;
         HIPCK(c, hipEventElapsedTime(&ms, c->ev[2 * i], c->ev[2 * i + 1]));
         c->blk_ms[c->ev_class[i]] += ms;
-        c->blk_count[c->ev_class[i]] += 1;
+        c->blk_count[c->ev_class[i]] += c->ev_count[i];
     }
     c->ev_used = 0;
     return FI_OK;
@@ -593,17 +627,38 @@ fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
     if (c->ev.empty()) {
         c->ev.resize(2 * kPairs, nullptr);
         c->ev_class.resize(kPairs, 0);
+        c->ev_count.resize(kPairs, 0);
         for (auto &e : c->ev) HIPCK(c, hipEventCreate(&e));
     }
-    if (c->ev_used == kPairs) {
+    if (c->ev_used + 2 > kPairs) {
         fi_status s = harvest_events(c);
         if (s != FI_OK) return s;
     }
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
+    c->ev_count[i] = 1;
     HIPCK(c, launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr));
-    HIPCK(c, launch_fft(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1]));
+    if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
+        // the deferred sub-blocks' kernel time adds to this launch
+        const size_t j = c->ev_used++;
+        c->ev_class[j] = q;
+        c->ev_count[j] = 0;
+        HIPCK(c, launch_fft_sub(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1], n, c->ev[2 * j],
+                                c->ev[2 * j + 1]));
+    } else {
+        HIPCK(c, launch_fft(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1]));
+    }
     HIPCK(c, launch_drain(c, rd, c->stream, 1));
+    return FI_OK;
+}
+
+// Before launching positions up to `upto`: join the side stream if deferred
+// sub-blocks it still computes are due by then (upto < 0: join in any case).
+fi_status join_side(fi_ctx *c, int64_t upto) {
+    if (c->side_until && (upto < 0 || upto >= c->side_until)) {
+        HIPCK(c, hipStreamWaitEvent(c->stream, c->ev_side, 0));
+        c->side_until = 0;
+    }
     return FI_OK;
 }
 
@@ -657,6 +712,9 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         fi_default_options(&o);
     if (o.map < FI_MAP_TANH || o.map > FI_MAP_HYENA) return FI_EINVAL;
     if (o.feedback < FI_FEEDBACK_TANH || o.feedback > FI_FEEDBACK_IDENTITY) return FI_EINVAL;
+    if (o.defer_wide != 0 && o.defer_wide != 1) return FI_EINVAL;
+    for (int r : o.reserved)
+        if (r != 0) return FI_EINVAL;
     if (o.tau_mode < FI_TAU_AUTO || o.tau_mode > FI_TAU_FFT) return FI_EINVAL;
     if ((uintptr_t)workspace % 256 != 0) return FI_EINVAL;
     Layout lay;
@@ -688,6 +746,10 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         c->own_ws = true;
     }
     if (hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess) return bail(FI_EDEVICE);
+    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_split, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_side, hipEventDisableTiming) != hipSuccess)
+        return bail(FI_EDEVICE);
 
     Dev &d = c->dev;
     d.filt = (const float *)(c->ws + lay.filt);
@@ -823,8 +885,12 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
 fi_status fi_destroy(fi_ctx *c) {
     if (!c) return FI_OK;
     if (c->ws) (void)hipStreamSynchronize(c->stream);
+    if (c->side) (void)hipStreamSynchronize(c->side);
     destroy_graphs(c);
     if (c->cap) (void)hipStreamDestroy(c->cap);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->ev_split) (void)hipEventDestroy(c->ev_split);
+    if (c->ev_side) (void)hipEventDestroy(c->ev_side);
     if (c->own_ws && c->ws) (void)hipFree(c->ws);
     delete c;
     return FI_OK;
@@ -833,7 +899,17 @@ fi_status fi_destroy(fi_ctx *c) {
 fi_status fi_reset(fi_ctx *c) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
     return clear_state(c);
+}
+
+fi_status fi_set_defer_wide(fi_ctx *c, int on) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (on != 0 && on != 1) return FI_EINVAL;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
+    c->opt.defer_wide = on;
+    return FI_OK;
 }
 
 int64_t fi_position(const fi_ctx *c) { return c ? c->pos : -1; }
@@ -859,7 +935,8 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const int64_t n = c->pos + 1;
-    HIPCK(c, launch_position(c, rd_of(n), class_of(c, n), c->stream, x_t, y_t, 1));
+    if ((s = join_side(c, n)) != FI_OK) return s;
+    HIPCK(c, launch_position(c, rd_of(n), class_of(c, n), c->stream, x_t, y_t, 1, n));
     c->pos = n;
     return FI_OK;
 }
@@ -891,18 +968,22 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
     while (c->pos < end) {
         const int64_t n = c->pos + 1;
         if (graphs && bsize && ((n - 1) & (bsize - 1)) == 0 && n + bsize - 2 <= end) {
+            if ((s = join_side(c, n + bsize - 2)) != FI_OK) return s;
             HIPCK(c, hipGraphLaunch(c->gblock, c->stream));
             c->pos += bsize - 1;
             continue;
         }
+        if ((s = join_side(c, n)) != FI_OK) return s;
         const int q = class_of(c, n);
-        if (c->opt.time_blocks && q < c->P && c->path[q] == FI_PATH_FFT) {
+        if (c->opt.time_blocks && q < c->P && c->path[q] == FI_PATH_FFT && c->opt.map != FI_MAP_HYENA) {
             s = launch_timed_position(c, n, q);
             if (s != FI_OK) return s;
-        } else if (graphs) {
+        } else if (graphs && !(c->opt.defer_wide && q < c->P && c->path[q] == FI_PATH_FFT &&
+                               is_sub(q, c->opt.fft_max_log2))) {
             HIPCK(c, hipGraphLaunch(c->gclass[q], c->stream));
         } else {
-            HIPCK(c, launch_position(c, rd_of(n), q, c->stream, nullptr, nullptr, 1));
+            // split gray blocks launch directly, leaving their later sub-blocks to the side stream
+            HIPCK(c, launch_position(c, rd_of(n), q, c->stream, nullptr, nullptr, 1, n));
         }
         c->pos = n;
     }
@@ -1013,7 +1094,8 @@ fi_status fi_tiles(fi_ctx *c) {
     if (c->opt.map != FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_tiles needs FI_MAP_EXTERNAL");
     if (c->pos >= c->L) return FI_ERANGE;
     const int64_t n = c->pos + 1;
-    HIPCK(c, launch_tiles(c, rd_of(n), class_of(c, n), c->stream));
+    if ((s = join_side(c, n)) != FI_OK) return s;
+    HIPCK(c, launch_tiles(c, rd_of(n), class_of(c, n), c->stream, n));
     c->pos = n;
     return FI_OK;
 }
@@ -1053,6 +1135,7 @@ fi_status fi_block_times(fi_ctx *c, int clear, double *ms, int64_t *count) {
 fi_status fi_time_block(fi_ctx *c, int q, int path, int reps, double *us) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
     if (q < 0 || q >= c->P || reps < 1 || !us) return FI_EINVAL;
     if (path == FI_PATH_DIRECT ? !direct_exists(q) : path == FI_PATH_FFT ? !fft_exists(q, c->P) : true)
         return FI_EINVAL;
@@ -1083,6 +1166,7 @@ fi_status fi_time_block(fi_ctx *c, int q, int path, int reps, double *us) {
 fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
     if (n < 1 || n > c->L || reps < 1 || !us) return FI_EINVAL;
     if (c->opt.map == FI_MAP_EXTERNAL || c->opt.map == FI_MAP_HYENA)
         return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");

@@ -662,21 +662,25 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
 
 // k_fft_sub_inv: per (l, b, c, o), Z = sum_i A_i * G_{K+o-i}, then the inverse
 // transform and accumulation of its exact upper half into output sub-block o.
+// One launch covers output sub-blocks o0 .. o0+nO-1.  nfix > 0 names the
+// position directly (a launch that runs after later positions have already
+// overwritten the position slots).
 template <int LOGV>
 __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int rd, const float4 *__restrict__ scratch,
                                                                      const float4 *__restrict__ spec, int K,
-                                                                     int advance) {
+                                                                     int o0, int nO, long long nfix, int advance) {
     using S = FftShape<LOGV>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
     __shared__ float2 smem[S::LDS];
     const int lt = threadIdx.x;
     const long long U = (long long)K * N;
-    const long long n = position_of(p, rd);
+    const long long n = nfix > 0 ? nfix : position_of(p, rd);
     const long long t = n - 1;
     if (n > p.L || n % U != 0 || n + U > p.L) return;  // uniform guard
     long long tile;
     int o;
-    xcd_tile(blockIdx.x, (long long)p.M * p.B * p.D, K, tile, o);
+    xcd_tile(blockIdx.x, (long long)p.M * p.B * p.D, nO, tile, o);
+    o += o0;
     const int c = (int)(tile % p.D);
     const int l = (int)(tile / ((long long)p.D * p.B));
     const size_t row = (size_t)tile * (size_t)p.L;

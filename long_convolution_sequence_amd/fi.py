@@ -35,7 +35,7 @@ class Options(ctypes.Structure):
                 ("tau_split", ctypes.c_int), ("record", ctypes.c_int), ("use_graphs", ctypes.c_int),
                 ("block_graph_log2", ctypes.c_int), ("filters_on_device", ctypes.c_int),
                 ("fft_max_log2", ctypes.c_int), ("time_blocks", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6)]
+                ("defer_wide", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
 
 
 _lib = None
@@ -62,6 +62,7 @@ def load_library():
         "fi_init": (I, [ctypes.POINTER(P), I, I, I, I64, P, OP, P, P]),
         "fi_destroy": (I, [P]),
         "fi_reset": (I, [P]),
+        "fi_set_defer_wide": (I, [P, I]),
         "fi_step": (I, [P, P, P]),
         "fi_set_input": (I, [P, P]),
         "fi_prefill": (I, [P, P, I64, P]),
@@ -116,7 +117,7 @@ class Context:
 
     def __init__(self, filters, batch, *, map=MAP_TANH, feedback=FEEDBACK_TANH, tau_mode=TAU_AUTO,
                  tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, fft_max_log2=14,
-                 time_blocks=False, device=None):
+                 time_blocks=False, defer_wide=False, device=None):
         import torch
         if not torch.cuda.is_available():
             raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
@@ -128,6 +129,7 @@ class Context:
         opt.record, opt.use_graphs, opt.block_graph_log2 = int(record), int(use_graphs), block_graph_log2
         opt.fft_max_log2 = fft_max_log2
         opt.time_blocks = int(time_blocks)
+        opt.defer_wide = int(defer_wide)
         if isinstance(filters, np.ndarray):
             f = np.ascontiguousarray(filters, dtype=np.float32)
             fptr = f.ctypes.data_as(ctypes.c_void_p)
@@ -173,6 +175,10 @@ class Context:
 
     def set_input(self, x0):
         self._check(self._lib.fi_set_input(self._h, _dptr(x0)))
+
+    def set_defer_wide(self, on):
+        """Defer the later sub-blocks of split gray blocks to a second stream (or not)."""
+        self._check(self._lib.fi_set_defer_wide(self._h, int(bool(on))))
 
     def step(self, x=None, y=None):
         """One position; x: [B][D] device tensor or None (feedback). Returns y [B][D]."""

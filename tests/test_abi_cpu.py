@@ -36,6 +36,8 @@ def test_default_options(lib):
     o = fi.default_options()
     assert (o.map, o.feedback, o.tau_mode, o.tau_split) == (fi.MAP_TANH, fi.FEEDBACK_TANH, fi.TAU_AUTO, -1)
     assert (o.record, o.use_graphs, o.block_graph_log2, o.filters_on_device) == (0, 1, 6, 0)
+    assert (o.fft_max_log2, o.time_blocks, o.defer_wide) == (14, 0, 0)
+    assert ctypes.sizeof(o) == 16 * 4
     assert lib.fi_version().decode().startswith("fi ")
 
 
@@ -69,9 +71,15 @@ def test_init_rejects_bad_arguments_without_a_device(lib):
     assert lib.fi_init(None, 1, 1, 1, 8, f, None, None, None) == fi.FI_EINVAL
     # misaligned workspace
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, None, ctypes.c_void_p(0x1001), None) == fi.FI_EINVAL
-    # invalid option value
+    # invalid option values
     o = fi.default_options()
     o.map = 7
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
+    o = fi.default_options()
+    o.defer_wide = 2
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
+    o = fi.default_options()
+    o.reserved[0] = 1
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
 
 
@@ -81,3 +89,4 @@ def test_null_context_calls_are_rejected(lib):
     assert lib.fi_position(None) == -1
     assert lib.fi_destroy(None) == fi.FI_OK
     assert lib.fi_debug_schedule(None, 1, None, None) == fi.FI_EINVAL
+    assert lib.fi_set_defer_wide(None, 1) == fi.FI_EINVAL

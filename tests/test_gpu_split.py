@@ -1,6 +1,8 @@
-"""GPU parity of gray blocks wider than one workgroup transform (split into
-K sub-blocks with offset-tap spectra), against the CPU oracle at sampled
-positions of full-length rows."""
+"""GPU parity of gray blocks wider than one workgroup transform: the class of
+twice that width (two halves in one workgroup) and the wider classes (split
+into K sub-blocks with offset-tap spectra), against the CPU oracle at sampled
+positions of full-length rows; and the deferred later sub-blocks of split
+blocks (defer_wide), which must change no bit of any output."""
 import numpy as np
 import pytest
 import torch
@@ -43,7 +45,7 @@ def _run_teacher_forced(M, B, D, L, vlog, seed):
 
 def test_split_blocks_k2_k4_k8():
     M, B, D, L = 1, 2, 3, 65536
-    say(f"case split blocks width 2^12 (K=2,4,8) M={M} B={B} D={D} L={L}")
+    say(f"case two-half block 2^13, split blocks 2^14, 2^15 (K=4, 8) M={M} B={B} D={D} L={L}")
     worst = _run_teacher_forced(M, B, D, L, 12, 21)
     say(f"  worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
@@ -51,7 +53,30 @@ def test_split_blocks_k2_k4_k8():
 
 def test_split_blocks_default_width_full_length():
     M, B, D, L = 1, 1, 2, 131072
-    say(f"case split blocks width 2^14 (K=2,4) M={M} B={B} D={D} L={L}")
+    say(f"case two-half block 2^15, split block 2^16 (K=4) M={M} B={B} D={D} L={L}")
     worst = _run_teacher_forced(M, B, D, L, 14, 22)
     say(f"  worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("graphs", [True, False])
+def test_deferred_split_sub_blocks_change_nothing(graphs):
+    """Feedback stack with split classes 2^14 and 2^15 (width 2^12): generation
+    and single steps with the later sub-blocks deferred to the side stream equal
+    the undeferred run bit for bit, also when a run stops inside a deferral."""
+    M, B, D, L = 2, 2, 5, 32768
+    say(f"case deferred split sub-blocks M={M} B={B} D={D} L={L} graphs={graphs}")
+    rng = np.random.default_rng(31)
+    h = (rng.standard_normal((M, D, L)) * np.exp(-np.arange(L) / 4096.0) / np.sqrt(L)).astype(np.float32)
+    x1 = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).cuda()
+    outs = []
+    for defer in (False, True):
+        with fi.Context(torch.from_numpy(h).cuda(), B, tau_split=6, fft_max_log2=12, use_graphs=graphs,
+                        defer_wide=defer) as ctx:
+            ctx.set_input(x1)
+            a = ctx.generate(16384 + 100)          # stops 100 positions into the first deferral
+            b = torch.stack([ctx.step() for _ in range(200)])
+            c = ctx.generate(L - 16384 - 300)
+            outs.append(torch.cat([a, b, c]).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    assert np.abs(outs[0]).max() > 0
