@@ -177,9 +177,11 @@ fi_status fail(fi_ctx *c, fi_status s, const std::string &msg) {
 // Layers per block of a direct position: enough blocks to spread the U x U
 // products, few enough that the red cells are not recomputed needlessly.
 int direct_lg(int M, int U) {
-    const int lg = U <= 2 ? M : U == 4 ? 6 : U == 8 ? 3 : U == 16 ? 2 : 1;
+    const int lg = U <= 1 ? M : U == 2 ? 9 : U == 4 ? 3 : U == 8 ? 2 : 1;
     return std::min(M, lg);
 }
+// U = 1 waits on the red cells, not on staging: a small block suffices
+int direct_threads(int U) { return U >= 2 ? kDirectThreads : 256; }
 // inputs (U) + taps (2U-1) + pending outputs (U) per layer and lane
 size_t direct_lds(int LG, int U) { return U > 0 ? (size_t)LG * (4 * U - 1) * 64 * sizeof(float) : 0; }
 size_t ring_lds(int LG, int G) { return (size_t)LG * G * 65 * sizeof(float); }
@@ -189,8 +191,8 @@ hipError_t launch_direct_u(fi_ctx *c, int rd, hipStream_t s, const float *xext, 
                            int rowx) {
     const int LG = direct_lg(c->M, U);
     const dim3 grid((c->B * c->D + 63) / 64, (c->M + LG - 1) / LG);
-    hipLaunchKernelGGL((k_direct<U, CHAIN>), grid, dim3(256), direct_lds(LG, U), s, c->dev, rd, LG, xext, yext,
-                       advance, rowx);
+    hipLaunchKernelGGL((k_direct<U, CHAIN>), grid, dim3(direct_threads(U)), direct_lds(LG, U), s, c->dev, rd, LG,
+                       xext, yext, advance, rowx);
     return hipGetLastError();
 }
 
@@ -242,13 +244,13 @@ hipError_t launch_direct(fi_ctx *c, int rd, int q, hipStream_t s, const float *x
 template <bool CHAIN>
 hipError_t launch_red_fft(fi_ctx *c, int rd, hipStream_t s, const float *xext, float *yext) {
     const dim3 grid((c->B * c->D + 63) / 64, c->M);
-    hipLaunchKernelGGL((k_red_fft<CHAIN>), grid, dim3(256), ring_lds(1, c->dev.G), s, c->dev, rd, 1, xext, yext);
+    hipLaunchKernelGGL((k_red_fft<CHAIN>), grid, dim3(kRingThreads), ring_lds(1, c->dev.G), s, c->dev, rd, 1, xext, yext);
     return hipGetLastError();
 }
 
 hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
     const dim3 grid((c->B * c->D + 63) / 64, c->M);
-    hipLaunchKernelGGL(k_drain, grid, dim3(256), (size_t)c->dev.G * 65 * sizeof(float), s, c->dev, rd, advance);
+    hipLaunchKernelGGL(k_drain, grid, dim3(kRingThreads), (size_t)c->dev.G * 65 * sizeof(float), s, c->dev, rd, advance);
     return hipGetLastError();
 }
 

@@ -14,6 +14,12 @@
 namespace fi {
 
 constexpr int kLanes = 64;  // chains per block: one per lane, so every access is coalesced
+// Threads of a direct-block workgroup (one wave runs the red cells, the rest
+// stage rows from memory: the staging is the critical path from U = 2 on, and
+// sixteen waves measured 25-50% faster than four there) and of the
+// ring <-> history copies at FFT positions.
+constexpr int kDirectThreads = 1024;
+constexpr int kRingThreads = 1024;
 
 // ---------------------------------------------------------------------------
 // Red cells of one (b, c) chain at position n, layers 0..l1-1, from the ring.
@@ -90,7 +96,7 @@ __device__ __forceinline__ void clear_ahead(const Dev &p, long long n, int chain
 // at n are already in the ring (external block mode).
 // ---------------------------------------------------------------------------
 template <int U, bool CHAIN>
-__global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const float *xext, float *yext,
+__global__ void __launch_bounds__(kDirectThreads) k_direct(Dev p, int rd, int LG, const float *xext, float *yext,
                                                 int advance, int rowx) {
     extern __shared__ float sm[];
     const long long n = position_of(p, rd);
@@ -186,7 +192,7 @@ __global__ void __launch_bounds__(256) k_direct(Dev p, int rd, int LG, const flo
 // both sides are coalesced).  CHAIN = false: external block mode.
 // ---------------------------------------------------------------------------
 template <bool CHAIN>
-__global__ void __launch_bounds__(256) k_red_fft(Dev p, int rd, int LG, const float *xext, float *yext) {
+__global__ void __launch_bounds__(kRingThreads) k_red_fft(Dev p, int rd, int LG, const float *xext, float *yext) {
     extern __shared__ float sm[];                 // [LG][G][65]
     const long long n = position_of(p, rd);
     const int G = p.G;
@@ -224,7 +230,7 @@ __global__ void __launch_bounds__(256) k_red_fft(Dev p, int rd, int LG, const fl
 // Last kernel of an FFT position: the FFT gray blocks' pending sums for
 // positions n+1 .. n+G are final (the next FFT block starts at n+G); add them
 // from the row-major history into the ring.  Grid = chain blocks x layers.
-__global__ void __launch_bounds__(256) k_drain(Dev p, int rd, int advance) {
+__global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advance) {
     extern __shared__ float sm[];                 // [G][65]
     const long long n = position_of(p, rd);
     const int G = p.G;
