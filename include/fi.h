@@ -103,7 +103,17 @@ typedef struct fi_options {
                               overlapping positions n+1 .. n+V-1, and the context
                               stream waits for them before position n+V.  Cuts the
                               latency of that position; default 0 */
-    int reserved[5];       /* must be zero */
+    int chunk_direct;      /* 1 (default): for maps that act channel by channel
+                              (FI_MAP_TANH, FI_MAP_IDENTITY), fi_generate and
+                              fi_prefill run the G = 2^q positions between two
+                              FFT positions (q: the first FFT class) as one
+                              launch, each workgroup owning whole chains.  The
+                              direct gray blocks of a chunk then sum, target by
+                              target, the same pairs the tiling assigns them
+                              (summary page, "Kachelung-Strategie"; the blocks
+                              below G never leave a chunk).  0: one launch (or
+                              graph node) per position */
+    int reserved[4];       /* must be zero */
 } fi_options;
 
 /* Fill *opt with the defaults listed above. */

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
+#include <utility>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -154,6 +156,13 @@ struct fi_ctx {
     size_t ev_used = 0;
     double blk_ms[kMaxP] = {0};
     int64_t blk_count[kMaxP] = {0};
+    // Chunked direct positions (maps that act channel by channel): chunks of
+    // 2^chunk_log positions, chunk_ch chains per workgroup; -1: not available.
+    int chunk_log = -1;
+    int chunk_ch = 0;
+    // The ring holds no valid pending sums after a chunk: the next per-position
+    // launch rebuilds it (cleared, then the FFT sums drained into it).
+    bool ring_stale = false;
 };
 
 namespace {
@@ -252,6 +261,47 @@ hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
     const dim3 grid((c->B * c->D + 63) / 64, c->M);
     hipLaunchKernelGGL(k_drain, grid, dim3(kRingThreads), (size_t)c->dev.G * 65 * sizeof(float), s, c->dev, rd, advance);
     return hipGetLastError();
+}
+
+// ---- chunked direct positions ----------------------------------------------
+
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kChunkLanes = 8;       // helper lanes per row
+// heads [R] float2, slots [G][R | 1], teacher-forced inputs [G][CH]; R = CH * M
+size_t chunk_lds(int CH, int M, int logg) {
+    const size_t G = (size_t)1 << logg, R = (size_t)CH * M;
+    return G * (R | 1) * sizeof(float) + R * sizeof(float2) + G * CH * sizeof(float);
+}
+int chunk_threads(int R) { return kLanes + (R * kChunkLanes + kLanes - 1) / kLanes * kLanes; }
+
+// Chains per workgroup: about one workgroup per CU, within the helper lanes,
+// the LDS and the 64 lanes of wave 0.
+int choose_chunk_ch(int M, int BD, int logg, int cus) {
+    int ch = std::max(1, (BD + cus - 1) / cus);
+    ch = std::min(ch, (kChunkThreads - kLanes) / (M * kChunkLanes));
+    while (ch > 1 && chunk_lds(ch, M, logg) > (size_t)kLdsBytes) --ch;
+    return std::max(1, std::min(ch, kLanes));
+}
+
+// k_chunk<MT>: MT = M up to kChunkRegLayers (layers in registers), else 0
+using ChunkKernel = void (*)(Dev, long long, int, int, const float *);
+template <int... I>
+constexpr std::array<ChunkKernel, sizeof...(I)> chunk_table(std::integer_sequence<int, I...>) {
+    return {{&k_chunk<I>...}};
+}
+constexpr auto kChunkKernels = chunk_table(std::make_integer_sequence<int, kChunkRegLayers + 1>{});
+ChunkKernel chunk_kernel(int M) { return kChunkKernels[M <= kChunkRegLayers ? M : 0]; }
+
+hipError_t launch_chunk(fi_ctx *c, int64_t cb, const float *xseq, hipStream_t s) {
+    const int CH = c->chunk_ch, R = CH * c->M, BD = c->B * c->D;
+    hipLaunchKernelGGL(chunk_kernel(c->M), dim3((unsigned)((BD + CH - 1) / CH)), dim3(chunk_threads(R)),
+                       chunk_lds(CH, c->M, c->chunk_log), s, c->dev, (long long)cb, 1 << c->chunk_log, CH, xseq);
+    return hipGetLastError();
+}
+
+hipError_t allow_chunk_lds(fi_ctx *c) {
+    return hipFuncSetAttribute((const void *)chunk_kernel(c->M), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)chunk_lds(c->chunk_ch, c->M, c->chunk_log));
 }
 
 // Kernel launch that, given events, has the dispatch itself stamp them at the
@@ -511,6 +561,7 @@ fi_status clear_state(fi_ctx *c) {
         c->blk_count[q] = 0;
     }
     c->ev_used = 0;
+    c->ring_stale = false;
     return FI_OK;
 }
 
@@ -621,9 +672,9 @@ fi_status harvest_events(fi_ctx *c) {
     return FI_OK;
 }
 
-// One FFT-class position launched directly, its gray-block kernels timed by
-// events that their dispatch stamps.
-fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
+// The FFT gray blocks of position n (class q), timed by events that their
+// dispatch stamps.
+fi_status launch_timed_fft(fi_ctx *c, int64_t n, int q, int advance) {
     const int rd = rd_of(n);
     constexpr size_t kPairs = 4096;
     if (c->ev.empty()) {
@@ -639,18 +690,71 @@ fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
     c->ev_count[i] = 1;
-    HIPCK(c, launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr));
     if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
         // the deferred sub-blocks' kernel time adds to this launch
         const size_t j = c->ev_used++;
         c->ev_class[j] = q;
         c->ev_count[j] = 0;
-        HIPCK(c, launch_fft_sub(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1], n, c->ev[2 * j],
+        HIPCK(c, launch_fft_sub(c, rd, q, c->stream, advance, c->ev[2 * i], c->ev[2 * i + 1], n, c->ev[2 * j],
                                 c->ev[2 * j + 1]));
     } else {
-        HIPCK(c, launch_fft(c, rd, q, c->stream, 0, c->ev[2 * i], c->ev[2 * i + 1]));
+        HIPCK(c, launch_fft(c, rd, q, c->stream, advance, c->ev[2 * i], c->ev[2 * i + 1]));
     }
+    return FI_OK;
+}
+
+// One FFT-class position launched directly, its gray-block kernels timed.
+fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
+    const int rd = rd_of(n);
+    HIPCK(c, launch_red_fft<true>(c, rd, c->stream, nullptr, nullptr));
+    fi_status s = launch_timed_fft(c, n, q, 0);
+    if (s != FI_OK) return s;
     HIPCK(c, launch_drain(c, rd, c->stream, 1));
+    return FI_OK;
+}
+
+// Positions cb+1 .. cb+G as one chunk launch, then the FFT gray blocks of
+// position cb+G (none at L).  xseq: teacher-forced inputs [G][B][D] or NULL.
+fi_status run_chunk(fi_ctx *c, int64_t cb, const float *xseq) {
+    const int64_t n = cb + (int64_t(1) << c->chunk_log);
+    HIPCK(c, launch_chunk(c, cb, xseq, c->stream));
+    c->ring_stale = true;
+    if (n >= c->L) return FI_OK;
+    const int q = class_of(c, n);
+    if (c->opt.time_blocks) {
+        fi_status s = launch_timed_fft(c, n, q, 0);
+        if (s != FI_OK) return s;
+    } else if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
+        HIPCK(c, launch_fft_sub(c, rd_of(n), q, c->stream, 0, nullptr, nullptr, n));
+    } else {
+        HIPCK(c, launch_fft(c, rd_of(n), q, c->stream, 0));
+    }
+    // stamped after the whole gray block (an FFT kernel's own stamp is its
+    // block 0's end, which for the widest blocks is far from the kernel's end)
+    hipLaunchKernelGGL(k_publish, dim3(1), dim3(64), 0, c->stream, c->dev, (long long)n);
+    HIPCK(c, hipGetLastError());
+    return FI_OK;
+}
+
+// True when the positions pos+1 .. pos+G form a whole chunk inside the run.
+bool chunk_fits(const fi_ctx *c, int64_t pos, int64_t end) {
+    if (c->chunk_log < 0 || !c->opt.chunk_direct) return false;
+    const int64_t G = int64_t(1) << c->chunk_log;
+    return (pos & (G - 1)) == 0 && pos + G <= end;
+}
+
+// Before a per-position launch after chunks: clear the ring's pending sums and
+// drain the FFT sums of the next G positions into it (the chunk kernel kept
+// them in the row-major history only).  Direct gray blocks never cross a
+// multiple of G, so nothing else is pending there.
+fi_status resume_ring(fi_ctx *c) {
+    if (!c->ring_stale) return FI_OK;
+    const size_t rows = (size_t)c->M * c->B * c->D;
+    HIPCK(c, hipMemsetAsync(c->dev.ar, 0, (size_t)kRing * rows * sizeof(float), c->stream));
+    const int64_t G = c->dev.G;
+    if (G && c->pos > 0 && c->pos % G == 0 && c->pos + G <= c->L)
+        HIPCK(c, launch_drain(c, rd_of(c->pos), c->stream, 0));
+    c->ring_stale = false;
     return FI_OK;
 }
 
@@ -687,6 +791,7 @@ void fi_default_options(fi_options *o) {
     o->block_graph_log2 = 6;
     o->filters_on_device = 0;
     o->fft_max_log2 = kMaxLdsFftLog;
+    o->chunk_direct = 1;
 }
 
 const char *fi_version(void) { return "fi 0.1 gfx950"; }
@@ -715,6 +820,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     if (o.map < FI_MAP_TANH || o.map > FI_MAP_HYENA) return FI_EINVAL;
     if (o.feedback < FI_FEEDBACK_TANH || o.feedback > FI_FEEDBACK_IDENTITY) return FI_EINVAL;
     if (o.defer_wide != 0 && o.defer_wide != 1) return FI_EINVAL;
+    if (o.chunk_direct != 0 && o.chunk_direct != 1) return FI_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return FI_EINVAL;
     if (o.tau_mode < FI_TAU_AUTO || o.tau_mode > FI_TAU_FFT) return FI_EINVAL;
@@ -876,6 +982,16 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     c->qd = qd;
     for (int q = 0; q < c->P; ++q) c->path[q] = q < qd ? FI_PATH_DIRECT : FI_PATH_FFT;
     c->dev.G = qd < c->P ? (1 << qd) : 0;
+    if (o.map == FI_MAP_TANH || o.map == FI_MAP_IDENTITY) {
+        // chunks end at the FFT positions (or at L when every class is direct)
+        c->chunk_log = std::min(qd, c->P);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return bail(fail(c, FI_EDEVICE, "device query"));
+        c->chunk_ch = choose_chunk_ch(c->M, c->B * c->D, c->chunk_log, cus);
+        if (allow_chunk_lds(c) != hipSuccess) return bail(fail(c, FI_EDEVICE, "chunk kernel LDS attribute"));
+    }
     if (o.use_graphs && o.map != FI_MAP_EXTERNAL) {
         if (build_graphs(c) != FI_OK) return bail(FI_EDEVICE);
     }
@@ -938,6 +1054,7 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const int64_t n = c->pos + 1;
     if ((s = join_side(c, n)) != FI_OK) return s;
+    if ((s = resume_ring(c)) != FI_OK) return s;
     HIPCK(c, launch_position(c, rd_of(n), class_of(c, n), c->stream, x_t, y_t, 1, n));
     c->pos = n;
     return FI_OK;
@@ -948,8 +1065,23 @@ fi_status fi_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
     if (s != FI_OK) return s;
     if (!x || P < 0) return FI_EINVAL;
     if (c->pos + P > c->L) return FI_ERANGE;
+    if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_prefill in external-block mode");
+    if (c->opt.map == FI_MAP_HYENA && !c->weights_set) return fail(c, FI_ESTATE, "block weights not set");
+    if ((s = enter_mode(c, 1)) != FI_OK) return s;
     const size_t BD = (size_t)c->B * c->D;
-    for (int64_t i = 0; i < P; ++i) {
+    const int64_t pos0 = c->pos, end = c->pos + P;
+    while (c->pos < end) {
+        const int64_t i = c->pos - pos0;
+        if (chunk_fits(c, c->pos, end)) {
+            const int64_t G = int64_t(1) << c->chunk_log;
+            if ((s = join_side(c, c->pos + G - 1)) != FI_OK) return s;
+            if ((s = run_chunk(c, c->pos, x + i * BD)) != FI_OK) return s;
+            if (y)
+                HIPCK(c, hipMemcpyAsync(y + i * BD, c->dev.ylast + c->pos * BD, G * BD * sizeof(float),
+                                        hipMemcpyDeviceToDevice, c->stream));
+            c->pos += G;
+            continue;
+        }
         s = fi_step(c, x + i * BD, y ? y + i * BD : nullptr);
         if (s != FI_OK) return s;
     }
@@ -969,6 +1101,16 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
     const bool graphs = c->opt.use_graphs != 0;
     while (c->pos < end) {
         const int64_t n = c->pos + 1;
+        if (chunk_fits(c, c->pos, end)) {
+            // a split gray block deferred earlier feeds targets past side_until
+            const int64_t G = int64_t(1) << c->chunk_log;
+            if ((s = join_side(c, c->pos + G - 1)) != FI_OK) return s;
+            if ((s = run_chunk(c, c->pos, nullptr)) != FI_OK) return s;
+            c->pos += G;
+            continue;
+        }
+        if ((s = join_side(c, n)) != FI_OK) return s;
+        if ((s = resume_ring(c)) != FI_OK) return s;
         if (graphs && bsize && ((n - 1) & (bsize - 1)) == 0 && n + bsize - 2 <= end) {
             if ((s = join_side(c, n + bsize - 2)) != FI_OK) return s;
             HIPCK(c, hipGraphLaunch(c->gblock, c->stream));

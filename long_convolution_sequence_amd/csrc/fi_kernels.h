@@ -20,6 +20,7 @@ constexpr int kLanes = 64;  // chains per block: one per lane, so every access i
 // ring <-> history copies at FFT positions.
 constexpr int kDirectThreads = 1024;
 constexpr int kRingThreads = 1024;
+constexpr int kChunkThreads = 1024;  // chunk workgroups: wave 0 + up to 15 helper waves
 
 // ---------------------------------------------------------------------------
 // Red cells of one (b, c) chain at position n, layers 0..l1-1, from the ring.
@@ -257,6 +258,194 @@ __global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advan
             if (cb + ln < BD) p.ar[ring(p, n + 1 + k, l) + cb + ln] = v;
         });
     finish_position(p, n, advance);
+}
+
+// ---------------------------------------------------------------------------
+// All positions of one chunk (cb, cb + G] (cb a multiple of G, the edge of
+// the first FFT class, G <= 256) for maps that act channel by channel.  Then
+// every (b, c) chain is independent through all layers, and so is every gray
+// block below G: their sources and targets lie in the same chunk (a block
+// after n has U = lowbit(n) < G, so n + U never passes the next multiple of
+// G).  One workgroup owns CH chains and all M layers and runs the chunk's G
+// positions back to back, with a barrier between positions and no launch.
+//
+// The gray blocks of edge U < G inside a chunk cover every pair s < t of the
+// chunk exactly once, so their sum into target t is the causal dot product
+// over the chunk.  It is formed here target by target:
+//   pend(t) = fft(t) + sum_{k=2..} h[k] x_{t-k}  (helpers, during position t-1)
+//           + h[1] x_{t-1}                       (chain lane, at position t)
+// so only the last term waits for the position before.  One LDS slot per
+// (position, row) holds the FFT pending sum (loaded from the row-major
+// history), then the finished sum, then the input x_t (the pages' activation
+// reuse); at the end the slots are the inputs the next FFT block reads.
+//
+// LDS: heads h01[R] (h[0], h[1]), then xp[G][RP], position-major (RP = R
+// rounded up to odd): a chain's layers at one position are adjacent.
+// Rows rho = j * M + l for chain c0 + j, layer l.
+// ---------------------------------------------------------------------------
+constexpr int kChunkTaps = 32;       // taps per helper lane: h[seg + 8m], m < 32 (G <= 256)
+constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's layers in registers
+
+// Red cells of the chunk's positions for one chain per lane of wave 0, all
+// layers.  MT = M layers: heads, pending sums and the previous position's
+// inputs in registers, straight-line code with no branch between layers; the
+// pending sums of a position are read from LDS in one batch, so the chain
+// then waits only on its own arithmetic.  MT = 0: any depth, one layer at a
+// time from LDS.  One barrier per position, as in the helper waves.
+template <int MT>
+__device__ __forceinline__ void chain_run(const Dev &p, float *xp, int RP, int G, const float2 *hz, long long cb,
+                                          int j, int chain, bool on, const float *xs, int CH) {
+    const int BD = p.B * p.D, M = p.M;
+    constexpr int NR = MT > 0 ? MT : 1;
+    float h0[NR], h1[NR], xq[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const float2 v = on && MT > 0 ? hz[j * M + k] : make_float2(0.f, 0.f);
+        h0[k] = v.x;
+        h1[k] = v.y;
+        xq[k] = 0.f;                           // slot -1: its tap-1 term is in the FFT sums
+    }
+    float xf = on ? p.xin[(size_t)((cb + 1) & 1) * BD + chain] : 0.f;   // feedback input
+    const bool map_id = p.map != 0, fb_id = p.fb != 0, rec = p.recx != nullptr;
+    for (int i = 0; i < G; ++i) {
+        const long long t = cb + 1 + i;        // position
+        if (on) {
+            float x = xs ? xs[i * CH + j] : xf;   // teacher-forced inputs, staged in LDS
+            float *cur = xp + (size_t)i * RP + j * M;   // this chain's layers at slot i
+            float y = 0.f;
+            if constexpr (MT > 0) {
+                float a[MT];
+#pragma unroll
+                for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
+#pragma unroll
+                for (int k = 0; k < MT; ++k) {
+                    y = fmaf(h0[k], x, a[k]);
+                    cur[k] = x;
+                    xq[k] = x;
+                    if (rec) {
+                        const size_t r = ((size_t)(t - 1) * MT + k) * BD + chain;
+                        p.recx[r] = x;
+                        p.recy[r] = y;
+                    }
+                    const float th = tanh_chain(y);  // both maps are evaluated, then one is selected
+                    x = (k + 1 < MT ? map_id : fb_id) ? y : th;
+                }
+            } else {
+                for (int l = 0; l < M; ++l) {
+                    const float2 h = hz[j * M + l];
+                    const float pend = i > 0 ? fmaf(h.y, cur[l - RP], cur[l]) : cur[l];
+                    y = fmaf(h.x, x, pend);
+                    cur[l] = x;
+                    if (rec) {
+                        const size_t r = ((size_t)(t - 1) * M + l) * BD + chain;
+                        p.recx[r] = x;
+                        p.recy[r] = y;
+                    }
+                    x = apply_map(l + 1 < M ? p.map : p.fb, y);
+                }
+            }
+            p.ylast[(size_t)(t - 1) * BD + chain] = y;
+            xf = x;
+        }
+        if (on && threadIdx.x == 0)
+            atomicMax((unsigned long long *)&p.stamps[t], (unsigned long long)wall_clock64());
+        __syncthreads();
+    }
+    if (on) p.xin[(size_t)((cb + G + 1) & 1) * BD + chain] = xf;
+}
+
+template <int MT>
+__global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, int G, int CH, const float *xseq) {
+    constexpr int S = 8;                       // helper lanes per row
+    extern __shared__ float sm[];
+    const int M = p.M, BD = p.B * p.D, R = CH * M, RP = R | 1;
+    float2 *h01 = (float2 *)sm;                            // [R]
+    float *xp = sm + 2 * R;                                // [G][RP]
+    float *xs = xp + (size_t)G * RP;                       // [G][CH] teacher-forced inputs
+    const int c0 = blockIdx.x * CH;
+    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
+    const int logG = 31 - __clz(G);
+    auto grow = [&](int rho) {                             // history row of local row rho
+        return ((size_t)(rho % M) * BD + c0 + rho / M) * (size_t)p.L;
+    };
+    auto frow = [&](int rho) {                             // filter row
+        return ((size_t)(rho % M) * p.D + (c0 + rho / M) % p.D) * (size_t)p.L;
+    };
+    auto live = [&](int rho) { return c0 + rho / M < BD; };
+
+    // pending sums of the chunk's positions (rows of the history, G slots
+    // each: coalesced reads, LDS writes at the odd stride RP), and the heads
+    batched_copy<8>(R * G, threadIdx.x, blockDim.x,
+        [&](int e) {
+            const int rho = e >> logG;
+            return live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
+        },
+        [&](int e, float v) { xp[(size_t)(e & (G - 1)) * RP + (e >> logG)] = v; });
+    for (int rho = threadIdx.x; rho < R; rho += blockDim.x)
+        h01[rho] = live(rho) ? make_float2(p.filt[frow(rho)], p.L > 1 ? p.filt[frow(rho) + 1] : 0.f)
+                             : make_float2(0.f, 0.f);
+    if (xseq)
+        for (int e = threadIdx.x; e < G * CH; e += blockDim.x) {
+            const int i = e / CH, j = e % CH;
+            xs[e] = c0 + j < BD ? xseq[(size_t)i * BD + c0 + j] : 0.f;
+        }
+    __syncthreads();
+
+    if (wave == 0) {
+        // ---- red cells, one chain per lane; the helpers must not delay them
+        __builtin_amdgcn_s_setprio(3);
+        chain_run<MT>(p, xp, RP, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr,
+                      CH);
+    } else {
+        // ---- helpers: during position t, the pending sum of t + 1 but for
+        // its tap-1 term: fft(t+1) + sum_{k>=2} h[k] x_{t+1-k}
+        const int hid = threadIdx.x - kLanes;
+        const int hrho = hid / S, seg = hid & (S - 1);
+        const bool helper = hrho < R && live(hrho);
+        float hreg[kChunkTaps];
+#pragma unroll
+        for (int m = 0; m < kChunkTaps; ++m)
+            hreg[m] = helper && seg + S * m < G ? p.filt[frow(hrho) + seg + S * m] : 0.f;
+        for (int i = 0; i < G; ++i) {
+            if (i + 1 < G) {
+                float acc = 0.f;
+                if (helper) {
+                    const float *col = xp + (size_t)(i + 1 - seg) * RP + hrho;   // slot i+1-k, k = seg + 8m
+#pragma unroll
+                    for (int m = 0; m < kChunkTaps; ++m) {
+                        if (S * m > i + 1) break;
+                        const int k = seg + S * m;
+                        if (k >= 2 && k <= i + 1) acc = fmaf(hreg[m], col[-(long)S * m * RP], acc);
+                    }
+                }
+#pragma unroll
+                for (int off = S / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+                if (helper && seg == 0) xp[(size_t)(i + 1) * RP + hrho] += acc;
+            }
+            __syncthreads();
+        }
+    }
+
+    // inputs of the chunk into the history (the next FFT block reads them)
+    for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
+        const int rho = e >> logG;
+        if (live(rho)) p.buf[grow(rho) + cb + (e & (G - 1))] = xp[(size_t)(e & (G - 1)) * RP + rho];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const long long n = cb + G;           // published: the FFT block of n reads slot (n-1)&1
+        p.st->pos[(n - 1) & 1] = n - 1;
+        p.st->pos[n & 1] = n;
+    }
+}
+
+// End of an FFT position reached from a chunk: n is published and stamped
+// once every gray-block kernel of n has finished (one thread).
+__global__ void __launch_bounds__(64) k_publish(Dev p, long long n) {
+    if (threadIdx.x == 0) {
+        p.stamps[n] = (long long)wall_clock64();
+        p.st->pos[(n - 1) & 1] = n - 1;
+        p.st->pos[n & 1] = n;
+    }
 }
 
 // Filter heads h^l[c][0..HK-1], channel innermost.

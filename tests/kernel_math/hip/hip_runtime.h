@@ -1,6 +1,7 @@
 // host shim for tests/kernel_math: the few HIP names fi_fft.h uses, for a CPU build
 // host shim: just enough of the HIP vector types to compile the FFT header on the CPU
 #pragma once
+#include <cmath>
 #include <cstdint>
 #include <cstddef>
 #define __device__
@@ -18,3 +19,6 @@ inline unsigned atomicAdd(unsigned* p, unsigned v) { unsigned o = *p; *p += v; r
 inline void __syncthreads() {}
 struct dim3_ { unsigned x = 0, y = 0, z = 0; };
 static dim3_ threadIdx, blockIdx, blockDim, gridDim;
+// hardware base-2 exponential and reciprocal: the C library's stand-ins
+#define __builtin_amdgcn_exp2f(x) std::exp2((float)(x))
+#define __builtin_amdgcn_rcpf(x) (1.0f / (float)(x))

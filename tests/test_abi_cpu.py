@@ -36,7 +36,7 @@ def test_default_options(lib):
     o = fi.default_options()
     assert (o.map, o.feedback, o.tau_mode, o.tau_split) == (fi.MAP_TANH, fi.FEEDBACK_TANH, fi.TAU_AUTO, -1)
     assert (o.record, o.use_graphs, o.block_graph_log2, o.filters_on_device) == (0, 1, 6, 0)
-    assert (o.fft_max_log2, o.time_blocks, o.defer_wide) == (14, 0, 0)
+    assert (o.fft_max_log2, o.time_blocks, o.defer_wide, o.chunk_direct) == (14, 0, 0, 1)
     assert ctypes.sizeof(o) == 16 * 4
     assert lib.fi_version().decode().startswith("fi ")
 
@@ -77,6 +77,9 @@ def test_init_rejects_bad_arguments_without_a_device(lib):
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
     o = fi.default_options()
     o.defer_wide = 2
+    assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
+    o = fi.default_options()
+    o.chunk_direct = 2
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
     o = fi.default_options()
     o.reserved[0] = 1

@@ -52,13 +52,14 @@ def test_single_layer_teacher_forced_matches_definition(tau):
     assert worst <= 0.05
 
 
+@pytest.mark.parametrize("chunk", [True, False])
 @pytest.mark.parametrize("tau", list(TAUS))
-def test_stack_teacher_forced_per_layer_replay(tau):
+def test_stack_teacher_forced_per_layer_replay(tau, chunk):
     M, B, D, L = 3, 2, 6, 512
-    say(f"case stack teacher-forced replay tau={tau} M={M} B={B} D={D} L={L}")
+    say(f"case stack teacher-forced replay tau={tau} chunk={chunk} M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 3, decay=128.0)
     x = np.random.default_rng(4).standard_normal((L, B, D)).astype(np.float32)
-    with fi.Context(_cuda(h), B, tau_mode=TAUS[tau], record=True) as ctx:
+    with fi.Context(_cuda(h), B, tau_mode=TAUS[tau], record=True, chunk_direct=chunk) as ctx:
         y = ctx.prefill(_cuda(x)).cpu().numpy()
         x0 = ctx.history(0, 0).cpu().numpy()
         assert np.array_equal(x0, x)                                 # inputs land in their slots
@@ -72,13 +73,14 @@ def test_stack_teacher_forced_per_layer_replay(tau):
     assert worst <= 1.0
 
 
-def test_feedback_small_config_replay_and_horizon():
+@pytest.mark.parametrize("chunk", [True, False])
+def test_feedback_small_config_replay_and_horizon(chunk):
     """1 layer, B=1, D=4, L=1024, h ~ N(0,1) exp(-k/256), x_1 ~ N(0,1), x_{t+1} = tanh(y_t)."""
     w = workloads.WORKLOADS[1]
-    say(f"case feedback {w.name}")
+    say(f"case feedback {w.name} chunk={chunk}")
     h = workloads.filters(w)
     x1 = workloads.x_first(w)
-    with fi.Context(_cuda(h), w.B, record=True) as ctx:
+    with fi.Context(_cuda(h), w.B, record=True, chunk_direct=chunk) as ctx:
         ctx.set_input(_cuda(x1))
         y = ctx.generate(w.L).cpu().numpy()            # [L][B][D]
         xs = ctx.history(0, 0).cpu().numpy()           # [L][B][D]
@@ -102,15 +104,16 @@ def test_feedback_small_config_replay_and_horizon():
     assert dgpu[:horizon // 2].max() <= 1e-3
 
 
-def test_paths_agree_and_runs_are_deterministic():
+@pytest.mark.parametrize("chunk", [True, False])
+def test_paths_agree_and_runs_are_deterministic(chunk):
     M, B, D, L = 2, 3, 7, 1024
-    say(f"case path agreement M={M} B={B} D={D} L={L}")
+    say(f"case path agreement chunk={chunk} M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 5, decay=300.0) * 0.05
     x1 = np.random.default_rng(6).standard_normal((B, D)).astype(np.float32)
     outs = {}
     for name, tau in TAUS.items():
         for graphs in (True, False):
-            with fi.Context(_cuda(h), B, tau_mode=tau, use_graphs=graphs) as ctx:
+            with fi.Context(_cuda(h), B, tau_mode=tau, use_graphs=graphs, chunk_direct=chunk) as ctx:
                 ctx.set_input(_cuda(x1))
                 outs[(name, graphs)] = ctx.generate(L).cpu().numpy()
     for name in TAUS:
@@ -120,7 +123,7 @@ def test_paths_agree_and_runs_are_deterministic():
         rel = np.abs(outs[(name, True)] - ref).max() / np.abs(ref).max()
         say(f"  {name} vs direct rel diff {rel:.2e}")
         assert rel <= 1e-3
-    with fi.Context(_cuda(h), B, tau_mode=fi.TAU_FFT) as ctx:
+    with fi.Context(_cuda(h), B, tau_mode=fi.TAU_FFT, chunk_direct=chunk) as ctx:
         ctx.set_input(_cuda(x1))
         again = ctx.generate(L).cpu().numpy()
     assert np.array_equal(again, outs[("fft", True)])
@@ -132,8 +135,9 @@ def test_prefill_equals_steps_then_generation_continues():
     h = _filters(M, D, L, 7, decay=64.0)
     x = np.random.default_rng(8).standard_normal((P, B, D)).astype(np.float32)
     # one fixed split for both contexts: two calibrations may pick different
-    # paths, which agree only to rounding
-    with fi.Context(_cuda(h), B, tau_split=4) as a, fi.Context(_cuda(h), B, tau_split=4) as b:
+    # paths, which agree only to rounding; one launch per position in both
+    with fi.Context(_cuda(h), B, tau_split=4, chunk_direct=False) as a, \
+            fi.Context(_cuda(h), B, tau_split=4, chunk_direct=False) as b:
         ya = a.prefill(_cuda(x))
         yb = torch.stack([b.step(_cuda(x[i])) for i in range(P)])
         assert torch.equal(ya, yb)
@@ -173,7 +177,7 @@ def test_external_block_mode_equals_identity_map():
     say(f"case external block mode M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 11, decay=32.0) * 0.3
     x = np.random.default_rng(12).standard_normal((L, B, D)).astype(np.float32)
-    with fi.Context(_cuda(h), B, map=fi.MAP_IDENTITY, tau_mode=fi.TAU_FFT) as ref:
+    with fi.Context(_cuda(h), B, map=fi.MAP_IDENTITY, tau_mode=fi.TAU_FFT, chunk_direct=False) as ref:
         yref = ref.prefill(_cuda(x))
     with fi.Context(_cuda(h), B, map=fi.MAP_EXTERNAL, tau_mode=fi.TAU_FFT) as ext:
         ys = []
@@ -185,6 +189,48 @@ def test_external_block_mode_equals_identity_map():
             ext.tiles()
         yext = torch.stack(ys)
     assert torch.equal(yext, yref)
+
+
+def test_chunks_and_single_positions_interleave():
+    """Prefill and generation switch between whole chunks (one launch for the
+    G positions between FFT positions) and single positions at every kind of
+    boundary; every recorded output replays against the oracle, and the run
+    agrees with one launch per position to rounding."""
+    M, B, D, L = 3, 2, 5, 1024
+    say(f"case chunk / position interleave M={M} B={B} D={D} L={L} G=32")
+    h = _filters(M, D, L, 17, decay=128.0) * 0.3
+    x = np.random.default_rng(18).standard_normal((45, B, D)).astype(np.float32)
+    outs = []
+    for chunk in (True, False):
+        with fi.Context(_cuda(h), B, tau_split=5, record=True, chunk_direct=chunk) as ctx:
+            ys = [ctx.prefill(_cuda(x))]                 # chunk 1..32, then 33..45 one by one
+            ys.append(ctx.generate(100))                 # 46..64, chunks 65..128, 129..145
+            ys.append(torch.stack([ctx.step() for _ in range(10)]))
+            ys.append(ctx.generate(L - 155))             # ... up to L, the last chunk ends at L
+            assert ctx.position == L
+            outs.append(torch.cat(ys).cpu().numpy())
+            worst = check_replay(h, ctx)
+            say(f"  chunk={chunk} replay worst error/tolerance {worst:.3e}")
+            assert worst <= 1.0
+    rel = np.abs(outs[0] - outs[1]).max() / np.abs(outs[1]).max()
+    say(f"  chunked vs per-position rel diff {rel:.2e}")
+    assert rel <= 1e-3
+
+
+@pytest.mark.parametrize("D", [515, 1103])
+def test_chunk_workgroups_with_ragged_chain_counts(D):
+    """More chains than CUs: several chains per chunk workgroup, the last
+    workgroup short; 256-position chunks (taps h[2..255] in the helpers)."""
+    M, B, L = 2, 1, 1024
+    say(f"case chunk ragged M={M} B={B} D={D} L={L} G=256")
+    h = _filters(M, D, L, 19, decay=200.0) * 0.1
+    x = np.random.default_rng(20).standard_normal((L, B, D)).astype(np.float32)
+    with fi.Context(_cuda(h), B, tau_split=8, record=True) as ctx:
+        ctx.prefill(_cuda(x))
+        chans = sorted(set([0, 1, 2, 3, D // 2, D - 4, D - 3, D - 2, D - 1]))
+        worst = check_replay(h, ctx, chans=chans)
+    say(f"  replay worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
 
 
 @pytest.mark.parametrize("L", [1, 2, 4, 8, 32])
