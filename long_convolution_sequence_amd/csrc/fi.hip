@@ -266,21 +266,19 @@ hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
 // ---- chunked direct positions ----------------------------------------------
 
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kChunkLanes = 8;       // helper lanes per row
-// heads [R] float2, slots [G][R | 1], teacher-forced inputs [G][CH]; R = CH * M
+// heads [R] float2, slots [G][kChunkSlot], teacher-forced inputs [G][CH]; R = CH * M
 size_t chunk_lds(int CH, int M, int logg) {
-    const size_t G = (size_t)1 << logg, R = (size_t)CH * M;
-    return G * (R | 1) * sizeof(float) + R * sizeof(float2) + G * CH * sizeof(float);
+    const size_t G = (size_t)1 << logg;
+    return G * kChunkSlot * sizeof(float) + (size_t)CH * M * sizeof(float2) + G * CH * sizeof(float);
 }
-int chunk_threads(int R) { return kLanes + (R * kChunkLanes + kLanes - 1) / kLanes * kLanes; }
 
-// Chains per workgroup: about one workgroup per CU, within the helper lanes,
-// the LDS and the 64 lanes of wave 0.
+// Chains per workgroup: about one workgroup per CU, within the helper rows,
+// the LDS and the 64 lanes of wave 0.  0: the stack is too deep for one chain.
 int choose_chunk_ch(int M, int BD, int logg, int cus) {
     int ch = std::max(1, (BD + cus - 1) / cus);
-    ch = std::min(ch, (kChunkThreads - kLanes) / (M * kChunkLanes));
+    ch = std::min(ch, kChunkMaxRows / M);
     while (ch > 1 && chunk_lds(ch, M, logg) > (size_t)kLdsBytes) --ch;
-    return std::max(1, std::min(ch, kLanes));
+    return std::min(ch, kLanes);
 }
 
 // k_chunk<MT>: MT = M up to kChunkRegLayers (layers in registers), else 0
@@ -294,7 +292,7 @@ ChunkKernel chunk_kernel(int M) { return kChunkKernels[M <= kChunkRegLayers ? M 
 
 hipError_t launch_chunk(fi_ctx *c, int64_t cb, const float *xseq, hipStream_t s) {
     const int CH = c->chunk_ch, R = CH * c->M, BD = c->B * c->D;
-    hipLaunchKernelGGL(chunk_kernel(c->M), dim3((unsigned)((BD + CH - 1) / CH)), dim3(chunk_threads(R)),
+    hipLaunchKernelGGL(chunk_kernel(c->M), dim3((unsigned)((BD + CH - 1) / CH)), dim3(kChunkThreads),
                        chunk_lds(CH, c->M, c->chunk_log), s, c->dev, (long long)cb, 1 << c->chunk_log, CH, xseq);
     return hipGetLastError();
 }
@@ -990,7 +988,9 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             return bail(fail(c, FI_EDEVICE, "device query"));
         c->chunk_ch = choose_chunk_ch(c->M, c->B * c->D, c->chunk_log, cus);
-        if (allow_chunk_lds(c) != hipSuccess) return bail(fail(c, FI_EDEVICE, "chunk kernel LDS attribute"));
+        if (c->chunk_ch < 1) c->chunk_log = -1;   // deeper than the helper rows of one workgroup
+        else if (allow_chunk_lds(c) != hipSuccess)
+            return bail(fail(c, FI_EDEVICE, "chunk kernel LDS attribute"));
     }
     if (o.use_graphs && o.map != FI_MAP_EXTERNAL) {
         if (build_graphs(c) != FI_OK) return bail(FI_EDEVICE);

@@ -279,22 +279,33 @@ __global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advan
 // history), then the finished sum, then the input x_t (the pages' activation
 // reuse); at the end the slots are the inputs the next FFT block reads.
 //
-// LDS: heads h01[R] (h[0], h[1]), then xp[G][RP], position-major (RP = R
-// rounded up to odd): a chain's layers at one position are adjacent.
-// Rows rho = j * M + l for chain c0 + j, layer l.
+// Waves (16): wave 0 runs the red cells, one chain per lane; the other waves
+// of its SIMD (4, 8, 12: waves go to the four SIMDs in turn) stay off the
+// arithmetic, and wave 4 stamps each position once its barrier has passed;
+// the twelve remaining waves are helpers, eight lanes per row.
+//
+// LDS: heads h01[R] (h[0], h[1]); slots xp[G][kChunkSlot], slot s at row
+// G-1-s (reversed, so that the taps of a helper lie at increasing addresses:
+// immediate offsets, read in pairs); teacher-forced inputs xs[G][CH].  Rows
+// rho = j * M + l for chain c0 + j, layer l.
 // ---------------------------------------------------------------------------
 constexpr int kChunkTaps = 32;       // taps per helper lane: h[seg + 8m], m < 32 (G <= 256)
 constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's layers in registers
+constexpr int kChunkHelperWaves = 12;
+constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
+// floats per slot: >= the rows, and 8 slots apart = 15 x 256 bytes (one
+// read2st64 reaches two taps); the eight lanes of a row then hit distinct banks
+constexpr int kChunkSlot = 120;
 
 // Red cells of the chunk's positions for one chain per lane of wave 0, all
 // layers.  MT = M layers: heads, pending sums and the previous position's
 // inputs in registers, straight-line code with no branch between layers; the
 // pending sums of a position are read from LDS in one batch, so the chain
 // then waits only on its own arithmetic.  MT = 0: any depth, one layer at a
-// time from LDS.  One barrier per position, as in the helper waves.
+// time from LDS.  One barrier per position, as in the other waves.
 template <int MT>
-__device__ __forceinline__ void chain_run(const Dev &p, float *xp, int RP, int G, const float2 *hz, long long cb,
-                                          int j, int chain, bool on, const float *xs, int CH) {
+__device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
+                                          int chain, bool on, const float *xs, int CH) {
     const int BD = p.B * p.D, M = p.M;
     constexpr int NR = MT > 0 ? MT : 1;
     float h0[NR], h1[NR], xq[NR];
@@ -311,7 +322,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int RP, int G
         const long long t = cb + 1 + i;        // position
         if (on) {
             float x = xs ? xs[i * CH + j] : xf;   // teacher-forced inputs, staged in LDS
-            float *cur = xp + (size_t)i * RP + j * M;   // this chain's layers at slot i
+            float *cur = xp + (size_t)(G - 1 - i) * kChunkSlot + j * M;   // this chain's layers at slot i
             float y = 0.f;
             if constexpr (MT > 0) {
                 float a[MT];
@@ -333,7 +344,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int RP, int G
             } else {
                 for (int l = 0; l < M; ++l) {
                     const float2 h = hz[j * M + l];
-                    const float pend = i > 0 ? fmaf(h.y, cur[l - RP], cur[l]) : cur[l];
+                    const float pend = i > 0 ? fmaf(h.y, cur[l + kChunkSlot], cur[l]) : cur[l];
                     y = fmaf(h.x, x, pend);
                     cur[l] = x;
                     if (rec) {
@@ -347,21 +358,33 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int RP, int G
             p.ylast[(size_t)(t - 1) * BD + chain] = y;
             xf = x;
         }
-        if (on && threadIdx.x == 0)
-            atomicMax((unsigned long long *)&p.stamps[t], (unsigned long long)wall_clock64());
         __syncthreads();
     }
     if (on) p.xin[(size_t)((cb + G + 1) & 1) * BD + chain] = xf;
 }
 
+// Sum over each aligned group of eight lanes, in every lane of the group:
+// swaps within quads (lane ^ 1, lane ^ 2), then the mirror within the group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);   // row_half_mirror
+    return v;
+}
+
 template <int MT>
 __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, int G, int CH, const float *xseq) {
     constexpr int S = 8;                       // helper lanes per row
+    constexpr int SP = kChunkSlot;
     extern __shared__ float sm[];
-    const int M = p.M, BD = p.B * p.D, R = CH * M, RP = R | 1;
+    const int M = p.M, BD = p.B * p.D, R = CH * M;
     float2 *h01 = (float2 *)sm;                            // [R]
-    float *xp = sm + 2 * R;                                // [G][RP]
-    float *xs = xp + (size_t)G * RP;                       // [G][CH] teacher-forced inputs
+    float *xp = sm + 2 * R;                                // [G][SP], slot s at row G-1-s
+    float *xs = xp + (size_t)G * SP;                       // [G][CH] teacher-forced inputs
     const int c0 = blockIdx.x * CH;
     const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
     const int logG = 31 - __clz(G);
@@ -373,14 +396,27 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     };
     auto live = [&](int rho) { return c0 + rho / M < BD; };
 
+    // helper lanes: row hrho, taps h[seg + 8m] (zero for k < 2: the chain
+    // adds tap 1, tap 0 is the red cell's own term); loads issued first
+    const int hw = (wave & 3) ? wave - 1 - wave / 4 : -1;
+    const int hid = hw * kLanes + lane;
+    const int hrho = hid / S, seg = hid & (S - 1);
+    const bool helper = hw >= 0 && hrho < R && live(hrho);
+    float hreg[kChunkTaps];
+#pragma unroll
+    for (int m = 0; m < kChunkTaps; ++m) {
+        const int k = seg + S * m;
+        hreg[m] = helper && k >= 2 && k < G ? p.filt[frow(hrho) + k] : 0.f;
+    }
+
     // pending sums of the chunk's positions (rows of the history, G slots
-    // each: coalesced reads, LDS writes at the odd stride RP), and the heads
+    // each: coalesced reads), the heads, the teacher-forced inputs
     batched_copy<8>(R * G, threadIdx.x, blockDim.x,
         [&](int e) {
             const int rho = e >> logG;
             return live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
         },
-        [&](int e, float v) { xp[(size_t)(e & (G - 1)) * RP + (e >> logG)] = v; });
+        [&](int e, float v) { xp[(size_t)(G - 1 - (e & (G - 1))) * SP + (e >> logG)] = v; });
     for (int rho = threadIdx.x; rho < R; rho += blockDim.x)
         h01[rho] = live(rho) ? make_float2(p.filt[frow(rho)], p.L > 1 ? p.filt[frow(rho) + 1] : 0.f)
                              : make_float2(0.f, 0.f);
@@ -392,35 +428,53 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     __syncthreads();
 
     if (wave == 0) {
-        // ---- red cells, one chain per lane; the helpers must not delay them
+        // ---- red cells; the helpers do not share this wave's SIMD
         __builtin_amdgcn_s_setprio(3);
-        chain_run<MT>(p, xp, RP, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr,
-                      CH);
+        chain_run<MT>(p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH);
+    } else if (hw < 0) {
+        // ---- waves 4, 8, 12: barriers only; wave 4 stamps each position's end
+        for (int i = 0; i < G; ++i) {
+            __syncthreads();
+            if (wave == 4 && lane == 0)
+                atomicMax((unsigned long long *)&p.stamps[cb + 1 + i], (unsigned long long)wall_clock64());
+        }
     } else {
         // ---- helpers: during position t, the pending sum of t + 1 but for
         // its tap-1 term: fft(t+1) + sum_{k>=2} h[k] x_{t+1-k}
-        const int hid = threadIdx.x - kLanes;
-        const int hrho = hid / S, seg = hid & (S - 1);
-        const bool helper = hrho < R && live(hrho);
-        float hreg[kChunkTaps];
-#pragma unroll
-        for (int m = 0; m < kChunkTaps; ++m)
-            hreg[m] = helper && seg + S * m < G ? p.filt[frow(hrho) + seg + S * m] : 0.f;
         for (int i = 0; i < G; ++i) {
             if (i + 1 < G) {
+                // tap m reads slot i+1-seg-8m, at row G-2-i+seg+8m.  Taps m < nu
+                // exist in every lane (nu uniform); groups of eight such taps
+                // read in one batch; the group holding nu (where some lanes'
+                // slots do not exist yet) reads clamped rows and drops them.
+                const int row0 = G - 2 - i + seg;
+                const float *base = xp + row0 * SP + hrho;
+                const int nu = (i + 2) >> 3, gfull = nu >> 3;
                 float acc = 0.f;
-                if (helper) {
-                    const float *col = xp + (size_t)(i + 1 - seg) * RP + hrho;   // slot i+1-k, k = seg + 8m
 #pragma unroll
-                    for (int m = 0; m < kChunkTaps; ++m) {
-                        if (S * m > i + 1) break;
-                        const int k = seg + S * m;
-                        if (k >= 2 && k <= i + 1) acc = fmaf(hreg[m], col[-(long)S * m * RP], acc);
+                for (int g = 0; g < kChunkTaps / 8; ++g) {
+                    if (g < gfull) {
+                        float v[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) v[q] = base[(8 * g + q) * S * SP];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) acc = fmaf(hreg[8 * g + q], v[q], acc);
+                    } else if (g == gfull) {
+                        float v[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int r = min(row0 + S * (8 * g + q), G - 1);
+                            v[q] = xp[r * SP + hrho];
+                        }
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const bool ok = S * (8 * g + q) <= i + 1 - seg;
+                            acc = fmaf(ok ? hreg[8 * g + q] : 0.f, v[q], acc);
+                        }
                     }
                 }
-#pragma unroll
-                for (int off = S / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-                if (helper && seg == 0) xp[(size_t)(i + 1) * RP + hrho] += acc;
+                acc = sum8(acc);
+                if (helper && seg == 0) atomicAdd(&xp[(size_t)(G - 2 - i) * SP + hrho], acc);
             }
             __syncthreads();
         }
@@ -429,7 +483,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     // inputs of the chunk into the history (the next FFT block reads them)
     for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
         const int rho = e >> logG;
-        if (live(rho)) p.buf[grow(rho) + cb + (e & (G - 1))] = xp[(size_t)(e & (G - 1)) * RP + rho];
+        if (live(rho)) p.buf[grow(rho) + cb + (e & (G - 1))] = xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho];
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const long long n = cb + G;           // published: the FFT block of n reads slot (n-1)&1
