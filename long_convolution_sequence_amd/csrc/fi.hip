@@ -51,7 +51,7 @@ int ctz64(int64_t n) {
 }
 
 struct Layout {
-    size_t filt = 0, hh = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
+    size_t filt = 0, hh = 0, htap = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
            stamps = 0, state = 0, scratch = 0, wt = 0, w1t = 0, w2t = 0, zb = 0, mb = 0, hb = 0, reca = 0;
     int HK = 0;
     size_t spec[kMaxP] = {0};
@@ -89,6 +89,7 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.HK = (int)std::min<int64_t>(kHeadTaps, L);
     lay.filt = take(rowsMD * L * sizeof(float));
     lay.hh = take(rowsMD * lay.HK * sizeof(float));
+    lay.htap = take(rowsMD * kChunkTapRow * sizeof(float));
     lay.buf = take(rowsMBD * L * sizeof(float));
     lay.xr = take((size_t)kRing * rowsMBD * sizeof(float));
     lay.ar = take((size_t)kRing * rowsMBD * sizeof(float));
@@ -266,10 +267,12 @@ hipError_t launch_drain(fi_ctx *c, int rd, hipStream_t s, int advance) {
 // ---- chunked direct positions ----------------------------------------------
 
 constexpr int kLdsBytes = 160 * 1024;
-// heads [R] float2, slots [G][kChunkSlot], teacher-forced inputs [G][CH]; R = CH * M
+// heads [R] float2, slots [G][kChunkSlot], zero rows [kChunkZeroRows][kChunkSlot],
+// teacher-forced inputs [G][CH]; R = CH * M
 size_t chunk_lds(int CH, int M, int logg) {
     const size_t G = (size_t)1 << logg;
-    return G * kChunkSlot * sizeof(float) + (size_t)CH * M * sizeof(float2) + G * CH * sizeof(float);
+    return (G + kChunkZeroRows) * kChunkSlot * sizeof(float) + (size_t)CH * M * sizeof(float2) +
+           G * CH * sizeof(float);
 }
 
 // Chains per workgroup: about one workgroup per CU, within the helper rows,
@@ -281,24 +284,29 @@ int choose_chunk_ch(int M, int BD, int logg, int cus) {
     return std::min(ch, kLanes);
 }
 
-// k_chunk<MT>: MT = M up to kChunkRegLayers (layers in registers), else 0
+// k_chunk<MT, MODE>: MT = M up to kChunkRegLayers (layers in registers), else
+// 0; MODE = kChunkRec (records kept) | kChunkTanh (tanh map and feedback)
 using ChunkKernel = void (*)(Dev, long long, int, int, const float *);
 template <int... I>
-constexpr std::array<ChunkKernel, sizeof...(I)> chunk_table(std::integer_sequence<int, I...>) {
-    return {{&k_chunk<I>...}};
+constexpr std::array<ChunkKernel, 4 * sizeof...(I)> chunk_table(std::integer_sequence<int, I...>) {
+    return {{&k_chunk<I / 4, I % 4>...}};
 }
-constexpr auto kChunkKernels = chunk_table(std::make_integer_sequence<int, kChunkRegLayers + 1>{});
-ChunkKernel chunk_kernel(int M) { return kChunkKernels[M <= kChunkRegLayers ? M : 0]; }
+constexpr auto kChunkKernels = chunk_table(std::make_integer_sequence<int, 4 * (kChunkRegLayers + 1)>{});
+ChunkKernel chunk_kernel(const fi_ctx *c) {
+    const int mode = (c->opt.record ? kChunkRec : 0) |
+                     (c->opt.map == FI_MAP_TANH && c->opt.feedback == FI_FEEDBACK_TANH ? kChunkTanh : 0);
+    return kChunkKernels[4 * (c->M <= kChunkRegLayers ? c->M : 0) + mode];
+}
 
 hipError_t launch_chunk(fi_ctx *c, int64_t cb, const float *xseq, hipStream_t s) {
     const int CH = c->chunk_ch, R = CH * c->M, BD = c->B * c->D;
-    hipLaunchKernelGGL(chunk_kernel(c->M), dim3((unsigned)((BD + CH - 1) / CH)), dim3(kChunkThreads),
+    hipLaunchKernelGGL(chunk_kernel(c), dim3((unsigned)((BD + CH - 1) / CH)), dim3(kChunkThreads),
                        chunk_lds(CH, c->M, c->chunk_log), s, c->dev, (long long)cb, 1 << c->chunk_log, CH, xseq);
     return hipGetLastError();
 }
 
 hipError_t allow_chunk_lds(fi_ctx *c) {
-    return hipFuncSetAttribute((const void *)chunk_kernel(c->M), hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute((const void *)chunk_kernel(c), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)chunk_lds(c->chunk_ch, c->M, c->chunk_log));
 }
 
@@ -860,6 +868,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     Dev &d = c->dev;
     d.filt = (const float *)(c->ws + lay.filt);
     d.hh = (const float *)(c->ws + lay.hh);
+    d.htap = (const float *)(c->ws + lay.htap);
     d.buf = (float *)(c->ws + lay.buf);
     d.xr = (float *)(c->ws + lay.xr);
     d.ar = (float *)(c->ws + lay.ar);
@@ -940,6 +949,10 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         hipLaunchKernelGGL(k_heads, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, c->stream, c->dev,
                            (float *)(c->ws + lay.hh));
         if (hipGetLastError() != hipSuccess) return bail(fail(c, FI_EDEVICE, "filter heads"));
+        const size_t nt = (size_t)layers * channels * kChunkTapRow;
+        hipLaunchKernelGGL(k_taps, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, c->stream, c->dev,
+                           (float *)(c->ws + lay.htap));
+        if (hipGetLastError() != hipSuccess) return bail(fail(c, FI_EDEVICE, "chunk tap table"));
     }
     if (clear_state(c) != FI_OK) return bail(FI_EDEVICE);
 

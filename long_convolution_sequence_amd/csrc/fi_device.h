@@ -5,6 +5,8 @@
 //   filt  [M][D][L]      filter taps h^l[c][k] (spectra, Lazy baseline)
 //   hh    [M][HK][D]     filter heads h^l[c][0..HK-1], channel innermost (red
 //                        cells and direct gray blocks: coalesced over channels)
+//   htap  [M][D][256]    taps 0..255 per (l, c) in runs s = 0..7 of h[s + 8m],
+//                        m < 32: one helper lane's taps of a chunk kernel
 //   xr    [W][M][B][D]   ring of recent layer inputs x^l_p, slot p mod W
 //   ar    [W][M][B][D]   ring of pending sums for positions p in (n, n+W/2]
 //   buf   [M][B][D][L]   row-major history: the inputs of every position up to
@@ -38,6 +40,7 @@ struct State {
 struct Dev {
     const float *filt;
     const float *hh;
+    const float *htap;   // [M][D][256] chunk helper taps, permuted (k_taps)
     float *buf;
     float *xr;
     float *ar;

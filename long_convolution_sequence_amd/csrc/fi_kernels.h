@@ -286,78 +286,109 @@ __global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advan
 //
 // LDS: heads h01[R] (h[0], h[1]); slots xp[G][kChunkSlot], slot s at row
 // G-1-s (reversed, so that the taps of a helper lie at increasing addresses:
-// immediate offsets, read in pairs); teacher-forced inputs xs[G][CH].  Rows
-// rho = j * M + l for chain c0 + j, layer l.
+// immediate offsets, read in pairs); a zero row G; teacher-forced inputs
+// xs[G][CH].  Rows rho = j * M + l for chain c0 + j, layer l.
+//
+// Global memory inside the position loop: the chain's last-layer output, the
+// helpers' history stores (one 128-byte line per row every 32 positions, for
+// the FFT block at the chunk's end) and wave 4's stamps.
 // ---------------------------------------------------------------------------
 constexpr int kChunkTaps = 32;       // taps per helper lane: h[seg + 8m], m < 32 (G <= 256)
+constexpr int kChunkTapRow = 8 * kChunkTaps;   // tap-table floats per (l, c): taps 0..255
 constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's layers in registers
 constexpr int kChunkHelperWaves = 12;
 constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
 // floats per slot: >= the rows, and 8 slots apart = 15 x 256 bytes (one
 // read2st64 reaches two taps); the eight lanes of a row then hit distinct banks
 constexpr int kChunkSlot = 120;
+// zero row after the slots: a helper tap that lies before the chunk reads it
+constexpr int kChunkZeroRows = 1;
+// chunk kernel variants: records every layer's input and output; both maps tanh
+constexpr int kChunkRec = 1, kChunkTanh = 2;
+// 0: the chain reads a position's pending sums when it starts (one barrier per
+// position); q > 0: a second barrier after layer q M / 4, where the chain
+// reads the next position's sums while its remaining layers run
+constexpr int kChunkMidQ = 0; 
 
 // Red cells of the chunk's positions for one chain per lane of wave 0, all
-// layers.  MT = M layers: heads, pending sums and the previous position's
-// inputs in registers, straight-line code with no branch between layers; the
-// pending sums of a position are read from LDS in one batch, so the chain
-// then waits only on its own arithmetic.  MT = 0: any depth, one layer at a
-// time from LDS.  One barrier per position, as in the other waves.
-template <int MT>
+// layers; one barrier per position, as in the other waves.  MT = M layers:
+// heads and the previous position's inputs in registers, the pending sums of
+// the position read from LDS in one batch, then straight-line code with no
+// branch between layers.  Lanes without a chain run the same code on chain
+// 0's data and store nothing.  MT = 0: any depth, one layer at a time from LDS.
+template <int MT, bool REC, bool TANH_ALL>
 __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
                                           int chain, bool on, const float *xs, int CH) {
     const int BD = p.B * p.D, M = p.M;
+    const int jr = on ? j : 0;                 // the chain whose LDS data this lane reads
     constexpr int NR = MT > 0 ? MT : 1;
-    float h0[NR], h1[NR], xq[NR];
+    constexpr int MID = kChunkMidQ > 0 && MT > 0 ? MT * kChunkMidQ / 4 : -1;
+    float h0[NR], h1[NR], xq[NR], pn[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-        const float2 v = on && MT > 0 ? hz[j * M + k] : make_float2(0.f, 0.f);
+        const float2 v = MT > 0 ? hz[jr * M + k] : make_float2(0.f, 0.f);
         h0[k] = v.x;
         h1[k] = v.y;
         xq[k] = 0.f;                           // slot -1: its tap-1 term is in the FFT sums
+        pn[k] = MID >= 0 ? xp[(size_t)(G - 1) * kChunkSlot + jr * M + k] : 0.f;   // slot 0
     }
     float xf = on ? p.xin[(size_t)((cb + 1) & 1) * BD + chain] : 0.f;   // feedback input
-    const bool map_id = p.map != 0, fb_id = p.fb != 0, rec = p.recx != nullptr;
+    const bool map_id = !TANH_ALL && p.map != 0, fb_id = !TANH_ALL && p.fb != 0;
     for (int i = 0; i < G; ++i) {
         const long long t = cb + 1 + i;        // position
-        if (on) {
-            float x = xs ? xs[i * CH + j] : xf;   // teacher-forced inputs, staged in LDS
-            float *cur = xp + (size_t)(G - 1 - i) * kChunkSlot + j * M;   // this chain's layers at slot i
-            float y = 0.f;
-            if constexpr (MT > 0) {
-                float a[MT];
+        float x = xs ? xs[i * CH + jr] : xf;   // teacher-forced inputs, staged in LDS
+        float *cur = xp + (size_t)(G - 1 - i) * kChunkSlot + jr * M;   // this chain's layers at slot i
+        float y = 0.f;
+        if constexpr (MT > 0) {
+            float a[MT];
 #pragma unroll
-                for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
+            for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], MID >= 0 ? pn[k] : cur[k]);   // + tap 1 of slot i-1
 #pragma unroll
-                for (int k = 0; k < MT; ++k) {
-                    y = fmaf(h0[k], x, a[k]);
-                    cur[k] = x;
-                    xq[k] = x;
-                    if (rec) {
+            for (int k = 0; k < MT; ++k) {
+                if (k == MID) {
+                    __syncthreads();           // the helper sums of slot i+1 are complete
+                    if (i + 1 < G) {
+#pragma unroll
+                        for (int kk = 0; kk < MT; ++kk) pn[kk] = cur[kk - kChunkSlot];   // slot i+1
+                    }
+                }
+                y = fmaf(h0[k], x, a[k]);
+                xq[k] = x;
+                if constexpr (REC) {
+                    if (on) {
                         const size_t r = ((size_t)(t - 1) * MT + k) * BD + chain;
                         p.recx[r] = x;
                         p.recy[r] = y;
                     }
-                    const float th = tanh_chain(y);  // both maps are evaluated, then one is selected
-                    x = (k + 1 < MT ? map_id : fb_id) ? y : th;
                 }
-            } else {
-                for (int l = 0; l < M; ++l) {
-                    const float2 h = hz[j * M + l];
-                    const float pend = i > 0 ? fmaf(h.y, cur[l + kChunkSlot], cur[l]) : cur[l];
-                    y = fmaf(h.x, x, pend);
-                    cur[l] = x;
-                    if (rec) {
-                        const size_t r = ((size_t)(t - 1) * M + l) * BD + chain;
-                        p.recx[r] = x;
-                        p.recy[r] = y;
-                    }
-                    x = apply_map(l + 1 < M ? p.map : p.fb, y);
+                const float th = tanh_chain(y);
+                if constexpr (TANH_ALL) {
+                    x = th;
+                } else {
+                    x = (k + 1 < MT ? map_id : fb_id) ? y : th;   // both maps evaluated, one selected
                 }
             }
-            p.ylast[(size_t)(t - 1) * BD + chain] = y;
-            xf = x;
+            if (on) {
+#pragma unroll
+                for (int k = 0; k < MT; ++k) cur[k] = xq[k];
+            }
+        } else {
+            for (int l = 0; l < M; ++l) {
+                const float2 h = hz[jr * M + l];
+                const float pend = i > 0 ? fmaf(h.y, cur[l + kChunkSlot], cur[l]) : cur[l];
+                y = fmaf(h.x, x, pend);
+                if (on) cur[l] = x;
+                if (REC && on) {
+                    const size_t r = ((size_t)(t - 1) * M + l) * BD + chain;
+                    p.recx[r] = x;
+                    p.recy[r] = y;
+                }
+                x = apply_map(l + 1 < M ? p.map : p.fb, y);
+            }
+            if (kChunkMidQ > 0) __syncthreads();
         }
+        if (on) p.ylast[(size_t)(t - 1) * BD + chain] = y;
+        xf = x;
         __syncthreads();
     }
     if (on) p.xin[(size_t)((cb + G + 1) & 1) * BD + chain] = xf;
@@ -376,7 +407,23 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
-template <int MT>
+template <int NF>
+__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho, int G) {
+    constexpr int S = 8, SP = kChunkSlot;
+    constexpr int NT = NF < 4 ? 8 * (NF + 1) : 32;
+    float v[NT];
+    const float *base = xp + (size_t)row0 * SP + hrho;
+#pragma unroll
+    for (int m = 0; m < 8 * NF && m < NT; ++m) v[m] = base[(size_t)m * S * SP];
+#pragma unroll
+    for (int m = 8 * NF; m < NT; ++m) v[m] = xp[(size_t)min(row0 + S * m, G) * SP + hrho];
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m & 3] = fmaf(hreg[m], v[m], acc[m & 3]);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <int MT, int MODE>
 __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, int G, int CH, const float *xseq) {
     constexpr int S = 8;                       // helper lanes per row
     constexpr int SP = kChunkSlot;
@@ -384,7 +431,8 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     const int M = p.M, BD = p.B * p.D, R = CH * M;
     float2 *h01 = (float2 *)sm;                            // [R]
     float *xp = sm + 2 * R;                                // [G][SP], slot s at row G-1-s
-    float *xs = xp + (size_t)G * SP;                       // [G][CH] teacher-forced inputs
+    float *xz = xp + (size_t)G * SP;                       // [kChunkZeroRows][SP] zeros: row G
+    float *xs = xz + kChunkZeroRows * SP;                  // [G][CH] teacher-forced inputs
     const int c0 = blockIdx.x * CH;
     const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
     const int logG = 31 - __clz(G);
@@ -393,6 +441,9 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     };
     auto frow = [&](int rho) {                             // filter row
         return ((size_t)(rho % M) * p.D + (c0 + rho / M) % p.D) * (size_t)p.L;
+    };
+    auto trow = [&](int rho) {                             // tap-table row
+        return (size_t)(rho % M) * p.D + (c0 + rho / M) % p.D;
     };
     auto live = [&](int rho) { return c0 + rho / M < BD; };
 
@@ -403,20 +454,46 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     const int hrho = hid / S, seg = hid & (S - 1);
     const bool helper = hw >= 0 && hrho < R && live(hrho);
     float hreg[kChunkTaps];
+    {
+        // the lane's 32 taps lie together in the tap table: eight 16-byte loads
+        const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
+                                            seg * kChunkTaps);
 #pragma unroll
-    for (int m = 0; m < kChunkTaps; ++m) {
-        const int k = seg + S * m;
-        hreg[m] = helper && k >= 2 && k < G ? p.filt[frow(hrho) + k] : 0.f;
+        for (int q = 0; q < kChunkTaps / 4; ++q) {
+            const float4 v = tp[q];
+            hreg[4 * q] = v.x;
+            hreg[4 * q + 1] = v.y;
+            hreg[4 * q + 2] = v.z;
+            hreg[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int m = 0; m < kChunkTaps; ++m) {
+            const int k = seg + S * m;
+            if (!(helper && k >= 2 && k < G)) hreg[m] = 0.f;
+        }
     }
 
     // pending sums of the chunk's positions (rows of the history, G slots
     // each: coalesced reads), the heads, the teacher-forced inputs
-    batched_copy<8>(R * G, threadIdx.x, blockDim.x,
-        [&](int e) {
+    if (G >= 4) {
+        const int g4 = logG - 2;                           // float4 per row: G / 4
+        for (int e = threadIdx.x; e < (R * G) >> 2; e += blockDim.x) {
+            const int rho = e >> g4, s0 = (e & ((G >> 2) - 1)) * 4;
+            const float4 v = live(rho) ? *(const float4 *)(p.buf + grow(rho) + cb + s0)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+            float *d = xp + (size_t)(G - 1 - s0) * SP + rho;
+            d[0] = v.x;
+            d[-SP] = v.y;
+            d[-2 * SP] = v.z;
+            d[-3 * SP] = v.w;
+        }
+    } else {
+        for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
             const int rho = e >> logG;
-            return live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
-        },
-        [&](int e, float v) { xp[(size_t)(G - 1 - (e & (G - 1))) * SP + (e >> logG)] = v; });
+            xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho] = live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
+        }
+    }
+    for (int e = threadIdx.x; e < kChunkZeroRows * SP; e += blockDim.x) xz[e] = 0.f;
     for (int rho = threadIdx.x; rho < R; rho += blockDim.x)
         h01[rho] = live(rho) ? make_float2(p.filt[frow(rho)], p.L > 1 ? p.filt[frow(rho) + 1] : 0.f)
                              : make_float2(0.f, 0.f);
@@ -427,63 +504,63 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
         }
     __syncthreads();
 
+    float *hist = p.buf + (helper ? grow(hrho) + cb : 0);   // a helper row's positions of the chunk
     if (wave == 0) {
         // ---- red cells; the helpers do not share this wave's SIMD
         __builtin_amdgcn_s_setprio(3);
-        chain_run<MT>(p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH);
+        chain_run<MT, (MODE & kChunkRec) != 0, (MODE & kChunkTanh) != 0>(
+            p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH);
     } else if (hw < 0) {
         // ---- waves 4, 8, 12: barriers only; wave 4 stamps each position's end
         for (int i = 0; i < G; ++i) {
+            if (kChunkMidQ > 0) __syncthreads();
             __syncthreads();
             if (wave == 4 && lane == 0)
                 atomicMax((unsigned long long *)&p.stamps[cb + 1 + i], (unsigned long long)wall_clock64());
         }
     } else {
-        // ---- helpers: during position t, the pending sum of t + 1 but for
-        // its tap-1 term: fft(t+1) + sum_{k>=2} h[k] x_{t+1-k}
+        // ---- helpers: during position i, the pending sum of slot i+1 but for
+        // its tap-1 term: fft + sum_{k>=2} h[k] x_{i+1-k}.  Tap m of a lane
+        // (k = seg + 8m) reads slot i+1-k at row row0 + 8m.  Taps come in four
+        // groups of eight m; the first nf = (i+2)/64 groups exist in every
+        // lane, the next one in some (its other lanes read the zero rows past
+        // the chunk's first slot), the rest in none.  nf is uniform and picks
+        // a branch-free body, so all of a position's reads are in flight.
         for (int i = 0; i < G; ++i) {
+            // every 32 positions, the inputs of the last 32 into the history,
+            // for the FFT block at the chunk's end: one whole 128-byte line per
+            // row, 16 bytes per lane (slots i-32+4seg .. +3, from row G-i+31-4seg down)
+            if (helper && i >= 32 && (i & 31) == 0) {
+                const float *src = xp + (size_t)(G - i + 31 - 4 * seg) * SP + hrho;
+                *(float4 *)(hist + i - 32 + 4 * seg) = make_float4(src[0], src[-SP], src[-2 * SP], src[-3 * SP]);
+            }
             if (i + 1 < G) {
-                // tap m reads slot i+1-seg-8m, at row G-2-i+seg+8m.  Taps m < nu
-                // exist in every lane (nu uniform); groups of eight such taps
-                // read in one batch; the group holding nu (where some lanes'
-                // slots do not exist yet) reads clamped rows and drops them.
                 const int row0 = G - 2 - i + seg;
-                const float *base = xp + row0 * SP + hrho;
-                const int nu = (i + 2) >> 3, gfull = nu >> 3;
-                float acc = 0.f;
-#pragma unroll
-                for (int g = 0; g < kChunkTaps / 8; ++g) {
-                    if (g < gfull) {
-                        float v[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) v[q] = base[(8 * g + q) * S * SP];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) acc = fmaf(hreg[8 * g + q], v[q], acc);
-                    } else if (g == gfull) {
-                        float v[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const int r = min(row0 + S * (8 * g + q), G - 1);
-                            v[q] = xp[r * SP + hrho];
-                        }
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const bool ok = S * (8 * g + q) <= i + 1 - seg;
-                            acc = fmaf(ok ? hreg[8 * g + q] : 0.f, v[q], acc);
-                        }
-                    }
+                float acc;
+                switch ((i + 2) >> 6) {
+                    case 0: acc = helper_sum<0>(xp, hreg, row0, hrho, G); break;
+                    case 1: acc = helper_sum<1>(xp, hreg, row0, hrho, G); break;
+                    case 2: acc = helper_sum<2>(xp, hreg, row0, hrho, G); break;
+                    case 3: acc = helper_sum<3>(xp, hreg, row0, hrho, G); break;
+                    default: acc = helper_sum<4>(xp, hreg, row0, hrho, G); break;
                 }
                 acc = sum8(acc);
-                if (helper && seg == 0) atomicAdd(&xp[(size_t)(G - 2 - i) * SP + hrho], acc);
+                if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
             }
-            __syncthreads();
+            if (kChunkMidQ > 0) __syncthreads();   // the chain reads slot i+1
+            __syncthreads();                   // the chain has written slot i
         }
     }
 
-    // inputs of the chunk into the history (the next FFT block reads them)
-    for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
-        const int rho = e >> logG;
-        if (live(rho)) p.buf[grow(rho) + cb + (e & (G - 1))] = xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho];
+    // the remaining inputs into the history: the last 32 slots as above, or
+    // all of a chunk shorter than 32
+    if (helper) {
+        if (G >= 32) {
+            const float *src = xp + (size_t)(31 - 4 * seg) * SP + hrho;   // slot G-32+4seg at row 31-4seg
+            *(float4 *)(hist + G - 32 + 4 * seg) = make_float4(src[0], src[-SP], src[-2 * SP], src[-3 * SP]);
+        } else {
+            for (int sl = seg; sl < G; sl += S) hist[sl] = xp[(size_t)(G - 1 - sl) * SP + hrho];
+        }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const long long n = cb + G;           // published: the FFT block of n reads slot (n-1)&1
@@ -500,6 +577,16 @@ __global__ void __launch_bounds__(64) k_publish(Dev p, long long n) {
         p.st->pos[(n - 1) & 1] = n - 1;
         p.st->pos[n & 1] = n;
     }
+}
+
+// Tap table of the chunk kernels' helper lanes: per (l, c), 8 runs of 32
+// floats, run s holding taps s, s+8, .., s+248 (zero past L).
+__global__ void __launch_bounds__(256) k_taps(Dev p, float *htap) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)p.M * p.D * kChunkTapRow) return;
+    const size_t row = i / kChunkTapRow;
+    const int e = (int)(i % kChunkTapRow), k = (e / kChunkTaps) + 8 * (e % kChunkTaps);
+    htap[i] = k < p.L ? p.filt[row * (size_t)p.L + k] : 0.f;
 }
 
 // Filter heads h^l[c][0..HK-1], channel innermost.
