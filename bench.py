@@ -46,8 +46,9 @@ def fft_alg_bytes(w, U):
 
 
 def kernel_source_hash():
+    """Hash of the FFT gray-block kernel sources (the kernels the traffic summary covers)."""
     h = hashlib.sha256()
-    for f in ("fi_kernels.h", "fi_fft.h", "fi_device.h"):
+    for f in ("fi_fft_kernels.h", "fi_fft.h"):
         with open(os.path.join(ROOT, "long_convolution_sequence_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -271,7 +272,9 @@ def main():
         dt = one_step()
         log(f"bench: warmup {i + 1}/{args.warmup}: {dt:.3f}s")
     ctx.block_times(clear=True)
+    ctx.chunk_times(clear=True)
     times, lat = [], []
+    chunk_ms, chunk_n = 0.0, 0
     blk_ms = np.zeros(w.P)
     blk_n = np.zeros(w.P, dtype=np.int64)
     for i in range(args.steps):
@@ -282,6 +285,9 @@ def main():
         for q, ms, cnt in ctx.block_times(clear=True):
             blk_ms[q] += ms
             blk_n[q] += cnt
+        cms, cn = ctx.chunk_times(clear=True)
+        chunk_ms += cms
+        chunk_n += cn
         log(f"bench: step {i + 1}/{args.steps}: {dt:.3f}s ({L * w.B / dt:,.0f} tokens/s)")
     total = float(np.sum(times))
     value = L * w.B * args.steps / total
@@ -306,6 +312,17 @@ def main():
         tot_ms += blk_ms[q]
     launches = int(blk_n.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9 if tot_ms > 0 else 0.0
+    G = next((1 << q for (q, pth, _, _) in tau if pth == fi.PATH_FFT), L)   # chunks end at FFT positions
+    chunk = None
+    if chunk_n:
+        avg_us = chunk_ms * 1e3 / chunk_n
+        chunk = {"kernel": "k_chunk (red cells and direct gray blocks of a chunk of positions)",
+                 "launches": int(chunk_n), "positions_per_launch": G,
+                 "avg_launch_us": round(avg_us, 2), "us_per_position": round(avg_us / G, 4),
+                 "share_of_step_time": round(chunk_ms * 1e-3 / total, 4),
+                 "fft_share_of_step_time": round(tot_ms * 1e-3 / total, 4),
+                 "bound": "latency: the serial red-cell chain (M layers of fma + tanh per position) "
+                          "and one workgroup barrier per position, not bytes or flops"}
 
     # one more generation with the later sub-blocks of split gray blocks
     # deferred to the context's second stream (large-block latency smoothing)
@@ -384,6 +401,7 @@ def main():
                        "max": round(float(lat.max()), 1),
                        "per_class_median": per_class},
         "roofline": roofline,
+        "chunk_kernel": chunk,
         "defer_wide": defer,
         "lazy_gpu": lazy,
         "cpu_baseline": cpu,

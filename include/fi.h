@@ -246,6 +246,13 @@ fi_status fi_lazy_generate(fi_ctx *ctx, int64_t steps, float *y);
  * at least P entries; either may be NULL. */
 fi_status fi_block_times(fi_ctx *ctx, int clear, double *ms, int64_t *count);
 
+/* Chunk-kernel timing (needs time_blocks = 1): *ms = summed event-measured
+ * milliseconds of the chunk kernels fi_generate / fi_step launched (each runs
+ * the red cells and direct gray blocks of 2^k consecutive positions, see
+ * fi_options.chunk_direct), *count = their number.  Synchronises the stream;
+ * clear = 1 zeroes both afterwards.  Either pointer may be NULL. */
+fi_status fi_chunk_times(fi_ctx *ctx, int clear, double *ms, int64_t *count);
+
 /* Per-size runtime of one gray-block path (the pages' runtime-per-tile-size
  * comparison, "Pareto-Optimalitaetskurve"): the mean device time in
  * microseconds of the gray-block kernels of class q (U = 2^q) over `reps`

@@ -21,6 +21,7 @@
 #include "../../include/fi.h"
 #include "fi_block.h"
 #include "fi_kernels.h"
+#include "fi_fft_kernels.h"
 
 using namespace fi;
 
@@ -34,6 +35,7 @@ constexpr int kMaxLayers = 64;
 constexpr int kMaxP = 24;
 constexpr int kRing = 512;        // ring slots: pending sums reach at most W/2 = 256 ahead
 constexpr int kHeadTaps = 256;    // taps h[0..255] serve direct blocks up to U = 128
+constexpr int kChunkEv = -1;      // event-pair class of a timed chunk kernel
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -157,6 +159,8 @@ struct fi_ctx {
     size_t ev_used = 0;
     double blk_ms[kMaxP] = {0};
     int64_t blk_count[kMaxP] = {0};
+    double chunk_ms = 0.0;           // event-timed chunk kernels (time_blocks)
+    int64_t chunk_count = 0;
     // Chunked direct positions (maps that act channel by channel): chunks of
     // 2^chunk_log positions, chunk_ch chains per workgroup; -1: not available.
     int chunk_log = -1;
@@ -298,10 +302,18 @@ ChunkKernel chunk_kernel(const fi_ctx *c) {
     return kChunkKernels[4 * (c->M <= kChunkRegLayers ? c->M : 0) + mode];
 }
 
-hipError_t launch_chunk(fi_ctx *c, int64_t cb, const float *xseq, hipStream_t s) {
-    const int CH = c->chunk_ch, R = CH * c->M, BD = c->B * c->D;
-    hipLaunchKernelGGL(chunk_kernel(c), dim3((unsigned)((BD + CH - 1) / CH)), dim3(kChunkThreads),
-                       chunk_lds(CH, c->M, c->chunk_log), s, c->dev, (long long)cb, 1 << c->chunk_log, CH, xseq);
+// ev0/ev1 (optional) are stamped by the dispatch at the kernel's start and end
+hipError_t launch_chunk(fi_ctx *c, int64_t cb, const float *xseq, hipStream_t s, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr) {
+    const int CH = c->chunk_ch, BD = c->B * c->D;
+    const dim3 grid((unsigned)((BD + CH - 1) / CH)), block(kChunkThreads);
+    const size_t lds = chunk_lds(CH, c->M, c->chunk_log);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(chunk_kernel(c), grid, block, lds, s, ev0, ev1, 0, c->dev, (long long)cb,
+                              1 << c->chunk_log, CH, xseq);
+    else
+        hipLaunchKernelGGL(chunk_kernel(c), grid, block, lds, s, c->dev, (long long)cb, 1 << c->chunk_log, CH,
+                           xseq);
     return hipGetLastError();
 }
 
@@ -671,17 +683,20 @@ fi_status harvest_events(fi_ctx *c) {
     for (size_t i = 0; i < c->ev_used; ++i) {
         float ms = 0.f;
         HIPCK(c, hipEventElapsedTime(&ms, c->ev[2 * i], c->ev[2 * i + 1]));
-        c->blk_ms[c->ev_class[i]] += ms;
-        c->blk_count[c->ev_class[i]] += c->ev_count[i];
+        if (c->ev_class[i] == kChunkEv) {
+            c->chunk_ms += ms;
+            c->chunk_count += c->ev_count[i];
+        } else {
+            c->blk_ms[c->ev_class[i]] += ms;
+            c->blk_count[c->ev_class[i]] += c->ev_count[i];
+        }
     }
     c->ev_used = 0;
     return FI_OK;
 }
 
-// The FFT gray blocks of position n (class q), timed by events that their
-// dispatch stamps.
-fi_status launch_timed_fft(fi_ctx *c, int64_t n, int q, int advance) {
-    const int rd = rd_of(n);
+// Room for two more event pairs (harvesting the pool when it is full).
+fi_status reserve_events(fi_ctx *c) {
     constexpr size_t kPairs = 4096;
     if (c->ev.empty()) {
         c->ev.resize(2 * kPairs, nullptr);
@@ -689,10 +704,16 @@ fi_status launch_timed_fft(fi_ctx *c, int64_t n, int q, int advance) {
         c->ev_count.resize(kPairs, 0);
         for (auto &e : c->ev) HIPCK(c, hipEventCreate(&e));
     }
-    if (c->ev_used + 2 > kPairs) {
-        fi_status s = harvest_events(c);
-        if (s != FI_OK) return s;
-    }
+    if (c->ev_used + 2 > kPairs) return harvest_events(c);
+    return FI_OK;
+}
+
+// The FFT gray blocks of position n (class q), timed by events that their
+// dispatch stamps.
+fi_status launch_timed_fft(fi_ctx *c, int64_t n, int q, int advance) {
+    const int rd = rd_of(n);
+    fi_status s0 = reserve_events(c);
+    if (s0 != FI_OK) return s0;
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
     c->ev_count[i] = 1;
@@ -723,7 +744,16 @@ fi_status launch_timed_position(fi_ctx *c, int64_t n, int q) {
 // position cb+G (none at L).  xseq: teacher-forced inputs [G][B][D] or NULL.
 fi_status run_chunk(fi_ctx *c, int64_t cb, const float *xseq) {
     const int64_t n = cb + (int64_t(1) << c->chunk_log);
-    HIPCK(c, launch_chunk(c, cb, xseq, c->stream));
+    if (c->opt.time_blocks) {
+        fi_status s = reserve_events(c);
+        if (s != FI_OK) return s;
+        const size_t i = c->ev_used++;
+        c->ev_class[i] = kChunkEv;
+        c->ev_count[i] = 1;
+        HIPCK(c, launch_chunk(c, cb, xseq, c->stream, c->ev[2 * i], c->ev[2 * i + 1]));
+    } else {
+        HIPCK(c, launch_chunk(c, cb, xseq, c->stream));
+    }
     c->ring_stale = true;
     if (n >= c->L) return FI_OK;
     const int q = class_of(c, n);
@@ -1285,6 +1315,19 @@ fi_status fi_block_times(fi_ctx *c, int clear, double *ms, int64_t *count) {
             c->blk_ms[q] = 0.0;
             c->blk_count[q] = 0;
         }
+    }
+    return FI_OK;
+}
+
+fi_status fi_chunk_times(fi_ctx *c, int clear, double *ms, int64_t *count) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if ((s = harvest_events(c)) != FI_OK) return s;
+    if (ms) *ms = c->chunk_ms;
+    if (count) *count = c->chunk_count;
+    if (clear) {
+        c->chunk_ms = 0.0;
+        c->chunk_count = 0;
     }
     return FI_OK;
 }

@@ -78,6 +78,7 @@ def load_library():
         "fi_lazy_step": (I, [P, P, P]),
         "fi_lazy_generate": (I, [P, I64, P]),
         "fi_block_times": (I, [P, I, P, P]),
+        "fi_chunk_times": (I, [P, I, P, P]),
         "fi_set_block_weights": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
@@ -262,6 +263,13 @@ class Context:
         cnt = (ctypes.c_int64 * P)()
         self._check(self._lib.fi_block_times(self._h, int(clear), ms, cnt))
         return [(q, ms[q], cnt[q]) for q in range(self.P)]
+
+    def chunk_times(self, clear=False):
+        """(summed chunk-kernel ms, launches) measured with HIP events (time_blocks contexts)."""
+        ms = ctypes.c_double()
+        cnt = ctypes.c_int64()
+        self._check(self._lib.fi_chunk_times(self._h, int(clear), ctypes.byref(ms), ctypes.byref(cnt)))
+        return ms.value, cnt.value
 
     def time_block(self, q, path, reps=10):
         """Mean microseconds of class q's gray-block kernels on one path (needs reset after)."""
