@@ -360,24 +360,54 @@ def main():
     del ctx
     torch.cuda.empty_cache()
 
-    lazy = None
+    lazy = ablations = None
     if not args.no_lazy:
-        # the Lazy path uses no gray blocks: skip calibration and graphs
-        lz = fi.Context(torch.from_numpy(h).cuda(), w.B, use_graphs=False, tau_split=0)
+        # the baselines use no gray blocks: skip calibration and graphs
+        bl = fi.Context(torch.from_numpy(h).cuda(), w.B, use_graphs=False, tau_split=0)
         pts = sorted({max(1, int(w.L * k / 8)) for k in range(1, 9)} | {1, 64})
-        tus = []
-        for n in pts:
-            tus.append(lz.lazy_time(n, reps=3 if n > 1024 else 20))
-        lz.close()
-        A = np.vstack([np.ones(len(pts)), np.array(pts, dtype=np.float64)]).T
-        a, b = np.linalg.lstsq(A, np.array(tus), rcond=None)[0]
-        lazy_total_s = (a * w.L + b * w.L * (w.L + 1) / 2) * 1e-6
-        lazy = {"tokens_per_s": w.L * w.B / lazy_total_s, "total_s_extrapolated": round(lazy_total_s, 2),
-                "sample": {str(n): round(t, 2) for n, t in zip(pts, tus)},
-                "fit_us": [round(float(a), 3), float(b)],
-                "speedup_vs_lazy": round(value / (w.L * w.B / lazy_total_s), 1),
-                "note": "Lazy per-position device time measured at the sampled positions with HIP "
-                        "events and integrated over n = 1..L with an affine fit"}
+        fits = {}
+        for name, kind in (("lazy", fi.BASE_LAZY), ("lazy_np", fi.BASE_LAZY_NP), ("eager", fi.BASE_EAGER),
+                           ("eager_np", fi.BASE_EAGER_NP)):
+            tus = [bl.baseline_time(kind, n, reps=3 if (n > 1024) == name.startswith("lazy") else 10)
+                   for n in pts]
+            # per-position cost is affine in the work: n for Lazy, L - n for Eager
+            work = np.array([n if name.startswith("lazy") else w.L - n for n in pts], dtype=np.float64)
+            A = np.vstack([np.ones(len(pts)), work]).T
+            a, b = np.linalg.lstsq(A, np.array(tus), rcond=None)[0]
+            total_s = (a * w.L + b * w.L * (w.L + 1) / 2 - (0 if name.startswith("lazy") else b * w.L)) * 1e-6
+            fits[name] = {"tokens_per_s": w.L * w.B / total_s, "total_s_extrapolated": round(total_s, 2),
+                          "sample_us": {str(n): round(t, 2) for n, t in zip(pts, tus)},
+                          "fit_us": [round(float(a), 3), float(b)]}
+        bl.close()
+        del bl
+        lazy = dict(fits["lazy"])
+        lazy["speedup_vs_lazy"] = round(value / lazy["tokens_per_s"], 1)
+        lazy["note"] = ("Lazy per-position device time measured at the sampled positions with HIP events "
+                        "and integrated over n = 1..L with an affine fit")
+        ablations = {k: {"tokens_per_s": round(v["tokens_per_s"], 2),
+                         "total_s_extrapolated": v["total_s_extrapolated"], "fit_us": v["fit_us"]}
+                     for k, v in fits.items()}
+        # the tiled path without chunks (one position per launch), with and without graphs
+        for name, graphs in (("tiled_per_position_graphs", True), ("tiled_per_position_no_graphs", False)):
+            pc = fi.Context(torch.from_numpy(h).cuda(), w.B, chunk_direct=False, use_graphs=graphs)
+            pc.set_input(x1)
+            pc.generate(min(L, 4096), want_y=False)          # warm-up (graphs, caches)
+            pc.reset()
+            pc.set_input(x1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            pc.generate(L, want_y=False)
+            torch.cuda.synchronize()
+            ablations[name] = {"tokens_per_s": round(L * w.B / (time.perf_counter() - t0), 1)}
+            pc.close()
+            del pc
+        ablations["note"] = ("the pages' ablations on this workload: Lazy / Eager and their non-layer-"
+                             "parallel forms (NP: the per-row work launched layer by layer), each timed at "
+                             "sampled positions and integrated with an affine fit in its per-position work; "
+                             "the tiled path with one launch (or graph) per position instead of chunks, "
+                             "with and without graphs, one timed generation each")
+        log("bench: ablations " + ", ".join(f"{k} {v['tokens_per_s']:,.0f}" for k, v in ablations.items()
+                                            if isinstance(v, dict)))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, h)
 
@@ -404,6 +434,7 @@ def main():
         "chunk_kernel": chunk,
         "defer_wide": defer,
         "lazy_gpu": lazy,
+        "ablations": ablations,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

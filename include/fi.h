@@ -239,6 +239,33 @@ fi_status fi_tiles(fi_ctx *ctx);
 fi_status fi_lazy_step(fi_ctx *ctx, const float *x_t, float *y_t);
 fi_status fi_lazy_generate(fi_ctx *ctx, int64_t steps, float *y);
 
+/* The pages' baselines and their ablations ("Vergleichsmethoden": Lazy,
+ * Eager, Lazy NP, Eager NP; "Ablationsstudien", cross-layer parallelism):
+ *   FI_BASE_LAZY      position n computes its full O(n) sum, all layers in
+ *                     one launch, then the red cells (= fi_lazy_step);
+ *   FI_BASE_EAGER     the red cells of n, then x_n is pushed into the pending
+ *                     sums of every later position (O(L - n)), all layers in
+ *                     one launch;
+ *   FI_BASE_LAZY_NP,
+ *   FI_BASE_EAGER_NP  the same with the per-row work launched layer by layer
+ *                     (no cross-layer parallelism).
+ * fi_baseline_step / fi_baseline_generate have the semantics of fi_step /
+ * fi_generate (x_t device [B][D] or NULL for internal feedback; y_t device
+ * [B][D] or NULL; y device [steps][B][D] or NULL).  A context steps one
+ * family at a time: Lazy kinds and Eager kinds, and either with tiled calls,
+ * cannot be mixed without fi_reset (FI_ESTATE).  kind outside the list:
+ * FI_EINVAL; external-block and Hyena-style maps: FI_ESTATE. */
+enum { FI_BASE_LAZY = 0, FI_BASE_EAGER = 1, FI_BASE_LAZY_NP = 2, FI_BASE_EAGER_NP = 3 };
+fi_status fi_baseline_step(fi_ctx *ctx, int kind, const float *x_t, float *y_t);
+fi_status fi_baseline_generate(fi_ctx *ctx, int kind, int64_t steps, float *y);
+
+/* Benchmark support for the baselines: the mean device time in microseconds
+ * of one baseline position n of the given kind (its sums or pushes plus the
+ * red cells), over `reps` launches timed with HIP events, without advancing.
+ * Overwrites activation rows: fi_reset is required before further stepping
+ * (FI_ESTATE otherwise). */
+fi_status fi_baseline_time(fi_ctx *ctx, int kind, int64_t n, int reps, double *us);
+
 /* Per-class FFT gray-block timing (needs time_blocks = 1): for q = 0..P-1,
  * ms[q] = summed event-measured milliseconds of the FFT gray-block kernels of
  * class q launched by fi_generate, count[q] = number of such launches.

@@ -804,9 +804,38 @@ fi_status join_side(fi_ctx *c, int64_t upto) {
     return FI_OK;
 }
 
+// The kernels of one baseline position n (rd its parity slot).  Lazy: the
+// full sum of every row, then the red cells.  Eager: the red cells, then every
+// row's push into the later pending sums.  _NP: the per-row work launched
+// layer by layer instead of for all layers at once ([S] "Vergleichsmethoden",
+// Lazy NP / Eager NP).  advance = 0 leaves the position unpublished (timing).
+hipError_t launch_baseline(fi_ctx *c, int kind, int rd, int64_t n, const float *x_t, float *y_t, int advance) {
+    const long long BD = (long long)c->B * c->D, rows = BD * c->M;
+    const bool np = kind == FI_BASE_LAZY_NP || kind == FI_BASE_EAGER_NP;
+    const int parts = np ? c->M : 1;
+    const long long per = np ? BD : rows;
+    hipError_t e;
+    if (kind == FI_BASE_LAZY || kind == FI_BASE_LAZY_NP) {
+        for (int k = 0; k < parts; ++k) {
+            hipLaunchKernelGGL(k_lazy_dot, dim3((unsigned)per), dim3(256), 0, c->stream, c->dev, rd, k * per);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        // red cells; the inputs also go to the row-major history the next sums read
+        return launch_direct<true>(c, rd, -1, c->stream, x_t, y_t, advance, 1);
+    }
+    if ((e = launch_direct<true>(c, rd, -1, c->stream, x_t, y_t, advance, 1)) != hipSuccess) return e;
+    if (n >= c->L) return hipSuccess;
+    const unsigned spans = (unsigned)((c->L - n + kEagerSpan - 1) / kEagerSpan);
+    for (int k = 0; k < parts; ++k) {
+        hipLaunchKernelGGL(k_eager_push, dim3(spans, (unsigned)per), dim3(256), 0, c->stream, c->dev, rd, k * per);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 fi_status enter_mode(fi_ctx *c, int mode) {
     if (c->mode != 0 && c->mode != mode)
-        return fail(c, FI_ESTATE, "tiled and Lazy calls cannot be mixed without fi_reset");
+        return fail(c, FI_ESTATE, "tiled, Lazy and Eager calls cannot be mixed without fi_reset");
     c->mode = mode;
     return FI_OK;
 }
@@ -1294,13 +1323,69 @@ fi_status fi_lazy_step(fi_ctx *c, const float *x_t, float *y_t) {
         return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
     if (c->pos >= c->L) return FI_ERANGE;
     if ((s = enter_mode(c, 2)) != FI_OK) return s;
-    const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
     const int rd = rd_of(c->pos + 1);
-    hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev, rd);
-    HIPCK(c, hipGetLastError());
-    // red cells; the inputs also go to the row-major history the next sums read
-    HIPCK(c, launch_direct<true>(c, rd, -1, c->stream, x_t, y_t, 1, 1));
+    HIPCK(c, launch_baseline(c, FI_BASE_LAZY, rd, c->pos + 1, x_t, y_t, 1));
     c->pos += 1;
+    return FI_OK;
+}
+
+fi_status fi_baseline_step(fi_ctx *c, int kind, const float *x_t, float *y_t) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (kind < FI_BASE_LAZY || kind > FI_BASE_EAGER_NP) return FI_EINVAL;
+    if (c->opt.map == FI_MAP_EXTERNAL || c->opt.map == FI_MAP_HYENA)
+        return fail(c, FI_ESTATE, "the baselines need an elementwise map");
+    if (c->pos >= c->L) return FI_ERANGE;
+    const bool eager = kind == FI_BASE_EAGER || kind == FI_BASE_EAGER_NP;
+    if ((s = enter_mode(c, eager ? 4 : 2)) != FI_OK) return s;
+    const int rd = rd_of(c->pos + 1);
+    HIPCK(c, launch_baseline(c, kind, rd, c->pos + 1, x_t, y_t, 1));
+    c->pos += 1;
+    return FI_OK;
+}
+
+fi_status fi_baseline_generate(fi_ctx *c, int kind, int64_t steps, float *y) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (steps < 0) return FI_EINVAL;
+    if (c->pos + steps > c->L) return FI_ERANGE;
+    const int64_t pos0 = c->pos;
+    for (int64_t i = 0; i < steps; ++i) {
+        s = fi_baseline_step(c, kind, nullptr, nullptr);
+        if (s != FI_OK) return s;
+    }
+    if (y && steps > 0) {
+        const size_t BD = (size_t)c->B * c->D;
+        HIPCK(c, hipMemcpyAsync(y, c->dev.ylast + pos0 * BD, steps * BD * sizeof(float),
+                                hipMemcpyDeviceToDevice, c->stream));
+    }
+    return FI_OK;
+}
+
+fi_status fi_baseline_time(fi_ctx *c, int kind, int64_t n, int reps, double *us) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
+    if (kind < FI_BASE_LAZY || kind > FI_BASE_EAGER_NP) return FI_EINVAL;
+    if (n < 1 || n > c->L || reps < 1 || !us) return FI_EINVAL;
+    if (c->opt.map == FI_MAP_EXTERNAL || c->opt.map == FI_MAP_HYENA)
+        return fail(c, FI_ESTATE, "the baselines need an elementwise map");
+    if ((s = set_state_pos(c, n - 1)) != FI_OK) return s;
+    c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    const int rd = rd_of(n);
+    HIPCK(c, launch_baseline(c, kind, rd, n, nullptr, nullptr, 0));  // warm-up
+    HIPCK(c, hipEventRecord(a, c->stream));
+    for (int r = 0; r < reps; ++r) HIPCK(c, launch_baseline(c, kind, rd, n, nullptr, nullptr, 0));
+    HIPCK(c, hipEventRecord(b, c->stream));
+    HIPCK(c, hipEventSynchronize(b));
+    float ms = 0.f;
+    HIPCK(c, hipEventElapsedTime(&ms, a, b));
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    *us = ms * 1000.0 / reps;
     return FI_OK;
 }
 
@@ -1372,16 +1457,11 @@ fi_status fi_lazy_time(fi_ctx *c, int64_t n, int reps, double *us) {
         return fail(c, FI_ESTATE, "Lazy path needs an elementwise map");
     if ((s = set_state_pos(c, n - 1)) != FI_OK) return s;
     c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
-    const unsigned rows = (unsigned)((size_t)c->M * c->B * c->D);
     hipEvent_t a, b;
     HIPCK(c, hipEventCreate(&a));
     HIPCK(c, hipEventCreate(&b));
     const int rd = rd_of(n);
-    auto once = [&]() -> hipError_t {
-        hipLaunchKernelGGL(k_lazy_dot, dim3(rows), dim3(256), 0, c->stream, c->dev, rd);
-        hipError_t e = hipGetLastError();
-        return e != hipSuccess ? e : launch_direct<true>(c, rd, -1, c->stream, nullptr, nullptr, 0, 1);
-    };
+    auto once = [&]() -> hipError_t { return launch_baseline(c, FI_BASE_LAZY, rd, n, nullptr, nullptr, 0); };
     HIPCK(c, once());  // warm-up
     HIPCK(c, hipEventRecord(a, c->stream));
     for (int r = 0; r < reps; ++r) HIPCK(c, once());

@@ -587,11 +587,11 @@ __global__ void __launch_bounds__(256) k_heads(Dev p, float *hh) {
 // whole history term sum_{s=1..n-1} h[n-s] x_s, written into slot n-1; the
 // red cells (k_red) then add h[0] x_n.  One workgroup per row.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_lazy_dot(Dev p, int rd) {
+__global__ void __launch_bounds__(256) k_lazy_dot(Dev p, int rd, long long row0) {
     const long long n = position_of(p, rd);
     const long long t = n - 1;
     if (n > p.L) return;
-    const long long rowi = blockIdx.x;
+    const long long rowi = row0 + blockIdx.x;
     const int b = (int)((rowi / p.D) % p.B), c = (int)(rowi % p.D);
     const int l = (int)(rowi / ((long long)p.D * p.B));
     const float *x = p.buf + act_row(p, l, b, c);
@@ -607,6 +607,36 @@ __global__ void __launch_bounds__(256) k_lazy_dot(Dev p, int rd) {
         float tot = 0.f;
         for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += part[w];
         p.ar[ring(p, n, l) + (size_t)b * p.D + c] = tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Eager baseline ([S] "Vergleichsmethoden", Eager: every future contribution
+// computed at once): after the red cells of position n have put x_n into the
+// history, x_n is pushed into the pending sum of every later position of its
+// row, t = n+1 .. L: h[t-n] x_n.  The sum of n+1 is then complete and goes to
+// the ring slot the next red cells read; later ones stay in the history row
+// (slot t-1, overwritten by x_t when t is reached).  Rows row0 + blockIdx.y,
+// 2048 targets per workgroup along x.
+// ---------------------------------------------------------------------------
+constexpr int kEagerSpan = 2048;
+__global__ void __launch_bounds__(256) k_eager_push(Dev p, int rd, long long row0) {
+    const long long n = position_of(p, rd);
+    if (n >= p.L) return;
+    const long long rowi = row0 + blockIdx.y;
+    const int b = (int)((rowi / p.D) % p.B), c = (int)(rowi % p.D);
+    const int l = (int)(rowi / ((long long)p.D * p.B));
+    float *row = p.buf + act_row(p, l, b, c);
+    const float *h = p.filt + filt_row(p, l, c);
+    const float xn = row[n - 1];
+    const long long t0 = n + 1 + (long long)blockIdx.x * kEagerSpan;
+    const long long t1 = min(p.L, t0 + kEagerSpan - 1);
+    for (long long t = t0 + threadIdx.x; t <= t1; t += blockDim.x) {
+        const float v = h[t - n] * xn;
+        if (t == n + 1)
+            p.ar[ring(p, n + 1, l) + (size_t)b * p.D + c] = row[n] + v;
+        else
+            row[t - 1] += v;
     }
 }
 

@@ -20,6 +20,7 @@ MAP_TANH, MAP_IDENTITY, MAP_EXTERNAL, MAP_HYENA = 0, 1, 2, 3
 FEEDBACK_TANH, FEEDBACK_IDENTITY = 0, 1
 TAU_AUTO, TAU_DIRECT, TAU_FFT = 0, 1, 2
 PATH_NONE, PATH_DIRECT, PATH_FFT = 0, 1, 2
+BASE_LAZY, BASE_EAGER, BASE_LAZY_NP, BASE_EAGER_NP = 0, 1, 2, 3
 _STATUS = {0: "FI_OK", -1: "FI_EINVAL", -2: "FI_ENOMEM", -3: "FI_EDEVICE", -4: "FI_ERANGE",
            -5: "FI_ESTATE"}
 
@@ -79,6 +80,9 @@ def load_library():
         "fi_lazy_generate": (I, [P, I64, P]),
         "fi_block_times": (I, [P, I, P, P]),
         "fi_chunk_times": (I, [P, I, P, P]),
+        "fi_baseline_step": (I, [P, I, P, P]),
+        "fi_baseline_generate": (I, [P, I, I64, P]),
+        "fi_baseline_time": (I, [P, I, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_set_block_weights": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
@@ -212,6 +216,17 @@ class Context:
         self._check(self._lib.fi_lazy_generate(self._h, int(steps), _dptr(y)))
         return y
 
+    def baseline_step(self, kind, x=None, y=None):
+        y = self._bd() if y is None else y
+        self._check(self._lib.fi_baseline_step(self._h, int(kind), _dptr(x), _dptr(y)))
+        return y
+
+    def baseline_generate(self, kind, steps, y=None, want_y=True):
+        if want_y and y is None:
+            y = self._bd((steps,))
+        self._check(self._lib.fi_baseline_generate(self._h, int(kind), int(steps), _dptr(y)))
+        return y
+
     def layer_red(self, layer, q, y=None):
         y = self._bd() if y is None else y
         self._check(self._lib.fi_layer_red(self._h, int(layer), _dptr(q), _dptr(y)))
@@ -281,6 +296,12 @@ class Context:
         """Mean microseconds of the Lazy baseline's work at position n (needs reset after)."""
         us = ctypes.c_double()
         self._check(self._lib.fi_lazy_time(self._h, int(n), int(reps), ctypes.byref(us)))
+        return us.value
+
+    def baseline_time(self, kind, n, reps=3):
+        """Mean microseconds of one baseline position n of the given kind (needs reset after)."""
+        us = ctypes.c_double()
+        self._check(self._lib.fi_baseline_time(self._h, int(kind), int(n), int(reps), ctypes.byref(us)))
         return us.value
 
     def schedule(self, n):
