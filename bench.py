@@ -227,6 +227,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lazy", action="store_true")
     ap.add_argument("--no-defer-leg", action="store_true", help="skip the generation with deferred split blocks")
+    ap.add_argument("--no-prefill-leg", action="store_true", help="skip the prefill timing")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
     ap.add_argument("--traffic-run", action="store_true",
                     help="launch each FFT class once and a calibration copy (run under rocprofv3 --pmc)")
@@ -409,6 +410,33 @@ def main():
         log("bench: ablations " + ", ".join(f"{k} {v['tokens_per_s']:,.0f}" for k, v in ablations.items()
                                             if isinstance(v, dict)))
 
+    prefill = None
+    if not args.no_prefill_leg:
+        # a prompt of P positions: eager (all positions of a layer at once) against P
+        # teacher-forced positions; each timed warm, on device events
+        P = min(16384, w.L // 8)
+        xp = torch.from_numpy(np.random.default_rng(5).standard_normal((P, w.B, w.D)).astype(np.float32)).cuda()
+        prefill = {"P": P}
+        for name, eager in (("eager", True), ("steps", False)):
+            pf = fi.Context(torch.from_numpy(h).cuda(), w.B, eager_prefill=eager)
+            ms = []
+            for _ in range(3):
+                pf.reset()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pf.prefill(xp, want_y=False)
+                b.record()
+                torch.cuda.synchronize()
+                ms.append(a.elapsed_time(b))
+            pf.close()
+            del pf
+            prefill[f"{name}_ms"] = round(float(np.median(ms[1:])), 3)
+            prefill[f"{name}_tokens_per_s"] = round(P * w.B / (np.median(ms[1:]) * 1e-3), 1)
+        prefill["note"] = ("fi_prefill of a seeded N(0,1) prompt at position 0, eager (layer by layer, "
+                           "all positions at once) against P teacher-forced positions (chunks); median of "
+                           "two warm runs, HIP events on the stream")
+        log(f"bench: prefill P={P}: eager {prefill['eager_ms']} ms, steps {prefill['steps_ms']} ms")
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, h)
 
     out = {
@@ -435,6 +463,7 @@ def main():
         "defer_wide": defer,
         "lazy_gpu": lazy,
         "ablations": ablations,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

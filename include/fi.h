@@ -113,7 +113,15 @@ typedef struct fi_options {
                               (summary page, "Kachelung-Strategie"; the blocks
                               below G never leave a chunk).  0: one launch (or
                               graph node) per position */
-    int reserved[4];       /* must be zero */
+    int eager_prefill;     /* 1 (default): fi_prefill at position 0 computes the
+                              prompt layer by layer with all of a layer's
+                              positions at once (direct sums inside blocks of G,
+                              FFT blocks above), when the map acts channel by
+                              channel, P is a multiple of G and every gray block
+                              after n <= P fits one workgroup transform
+                              (P < 2^(fft_max_log2+1)); otherwise, or with 0, P
+                              teacher-forced positions */
+    int reserved[3];       /* must be zero */
 } fi_options;
 
 /* Fill *opt with the defaults listed above. */

@@ -53,9 +53,10 @@ int ctz64(int64_t n) {
 }
 
 struct Layout {
-    size_t filt = 0, hh = 0, htap = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
+    size_t filt = 0, hh = 0, htap = 0, pre = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
            stamps = 0, state = 0, scratch = 0, wt = 0, w1t = 0, w2t = 0, zb = 0, mb = 0, hb = 0, reca = 0;
     int HK = 0;
+    int pre_stride = 0;              // prefill sums per (b, c): positions below 2^(fft_max_log2+1)
     size_t spec[kMaxP] = {0};
     size_t total = 0;
     int logNT = 0;
@@ -92,6 +93,8 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.filt = take(rowsMD * L * sizeof(float));
     lay.hh = take(rowsMD * lay.HK * sizeof(float));
     lay.htap = take(rowsMD * kChunkTapRow * sizeof(float));
+    lay.pre_stride = (int)std::min<int64_t>(L, int64_t(1) << (vlog + 1));
+    lay.pre = take((size_t)B * D * lay.pre_stride * sizeof(float));
     lay.buf = take(rowsMBD * L * sizeof(float));
     lay.xr = take((size_t)kRing * rowsMBD * sizeof(float));
     lay.ar = take((size_t)kRing * rowsMBD * sizeof(float));
@@ -141,6 +144,8 @@ struct fi_ctx {
     Dev dev{};
     float4 *spec[kMaxP] = {nullptr};
     float4 *scratch = nullptr;
+    float *pre = nullptr;            // eager prefill sums [B*D][pre_stride]
+    int pre_stride = 0;
     int path[kMaxP] = {0};
     double us_direct[kMaxP], us_fft[kMaxP];
     int64_t pos = 0;
@@ -857,6 +862,7 @@ void fi_default_options(fi_options *o) {
     o->filters_on_device = 0;
     o->fft_max_log2 = kMaxLdsFftLog;
     o->chunk_direct = 1;
+    o->eager_prefill = 1;
 }
 
 const char *fi_version(void) { return "fi 0.1 gfx950"; }
@@ -966,6 +972,8 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     for (int q = 0; q < c->P; ++q)
         c->spec[q] = fft_exists(q, c->P) ? (float4 *)(c->ws + lay.spec[q]) : nullptr;
     c->scratch = lay.scratch ? (float4 *)(c->ws + lay.scratch) : nullptr;
+    c->pre = (float *)(c->ws + lay.pre);
+    c->pre_stride = lay.pre_stride;
 
     // filters
     const size_t fbytes = (size_t)layers * channels * L * sizeof(float);
@@ -1132,6 +1140,77 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
     return FI_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Whether fi_prefill may take the eager path (see fi_options.eager_prefill).
+bool eager_prefill_ok(const fi_ctx *c, int64_t P) {
+    const int64_t G = c->dev.G;
+    return c->opt.eager_prefill && c->pos == 0 && P > 0 && P < c->L && G >= 4 && G <= kPreNearMax && P % G == 0 &&
+           (c->opt.map == FI_MAP_TANH || c->opt.map == FI_MAP_IDENTITY) &&
+           P < (int64_t(1) << (c->opt.fft_max_log2 + 1)) && P <= c->pre_stride;
+}
+
+template <int LOGN>
+hipError_t launch_pre_fft_n(fi_ctx *c, int l, int64_t P) {
+    using S = FftShape<LOGN>;
+    const long long BD = (long long)c->B * c->D;
+    const unsigned nb = (unsigned)(((P >> LOGN) + 1) >> 1);   // odd multiples of 2^LOGN up to P
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pre_fft<LOGN>, dim3((unsigned)((BD + S::PER_BLOCK - 1) / S::PER_BLOCK), nb), dim3(S::TPB),
+                       0, c->stream, c->dev, (const float4 *)c->spec[LOGN], l, (long long)P, c->pre,
+                       c->pre_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_pre_fft(fi_ctx *c, int q, int l, int64_t P) {
+    switch (q) {
+        case 2: return launch_pre_fft_n<2>(c, l, P);
+        case 3: return launch_pre_fft_n<3>(c, l, P);
+        case 4: return launch_pre_fft_n<4>(c, l, P);
+        case 5: return launch_pre_fft_n<5>(c, l, P);
+        case 6: return launch_pre_fft_n<6>(c, l, P);
+        case 7: return launch_pre_fft_n<7>(c, l, P);
+        case 8: return launch_pre_fft_n<8>(c, l, P);
+        case 9: return launch_pre_fft_n<9>(c, l, P);
+        case 10: return launch_pre_fft_n<10>(c, l, P);
+        case 11: return launch_pre_fft_n<11>(c, l, P);
+        case 12: return launch_pre_fft_n<12>(c, l, P);
+        case 13: return launch_pre_fft_n<13>(c, l, P);
+        case 14: return launch_pre_fft_n<14>(c, l, P);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// The prompt x[P][B][D] at position 0, layer by layer with all positions at
+// once; leaves the state of P teacher-forced positions (ring rebuilt lazily).
+fi_status eager_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
+    const long long BD = (long long)c->B * c->D;
+    const unsigned cells = (unsigned)((BD * P + 255) / 256);
+    const int G = (int)c->dev.G, qg = ilog2_exact(G);
+    hipLaunchKernelGGL(k_pre_in, dim3(cells), dim3(256), 0, c->stream, c->dev, x, (long long)P);
+    HIPCK(c, hipGetLastError());
+    for (int l = 0; l < c->M; ++l) {
+        hipLaunchKernelGGL(k_pre_near, dim3((unsigned)(BD * (P / G))), dim3(kPreNearMax), 0, c->stream, c->dev, l,
+                           (long long)P, G, c->pre, c->pre_stride);
+        HIPCK(c, hipGetLastError());
+        for (int q = qg; (int64_t(1) << q) <= P; ++q) HIPCK(c, launch_pre_fft(c, q, l, P));
+        hipLaunchKernelGGL(k_pre_red, dim3(cells), dim3(256), 0, c->stream, c->dev, l, (long long)P,
+                           (const float *)c->pre, c->pre_stride, y);
+        HIPCK(c, hipGetLastError());
+    }
+    fi_status s = set_state_pos(c, P);
+    if (s != FI_OK) return s;
+    c->pos = P;
+    c->ring_stale = true;          // the next per-position launch rebuilds the ring
+    return FI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 fi_status fi_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
@@ -1140,6 +1219,7 @@ fi_status fi_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
     if (c->opt.map == FI_MAP_EXTERNAL) return fail(c, FI_ESTATE, "fi_prefill in external-block mode");
     if (c->opt.map == FI_MAP_HYENA && !c->weights_set) return fail(c, FI_ESTATE, "block weights not set");
     if ((s = enter_mode(c, 1)) != FI_OK) return s;
+    if (eager_prefill_ok(c, P)) return eager_prefill(c, x, P, y);
     const size_t BD = (size_t)c->B * c->D;
     const int64_t pos0 = c->pos, end = c->pos + P;
     while (c->pos < end) {

@@ -18,30 +18,18 @@ namespace fi {
 // (l, b, c) block; the red cells at n have already run.
 //   spec: per (l, c), U/2 float4 in pair order (see k_spectrum), scaled by 1/U.
 // ---------------------------------------------------------------------------
-// Four waves per SIMD is what the LDS allows at every size from 2^8 on; the
-// register budget is held to that.
+// One gray block of edge N = 2^LOGN for the calling team (TT threads, lt
+// its thread): the block's N inputs at xsrc (N/2 float2), times the filter
+// spectrum sp (N/2 float4 in pair order), transformed back.  On return this
+// thread holds in v[HALF0 + m] the outputs at float2 index lt + (m << QLOG0)
+// of the exact upper half (targets n+1 .. n+N of the block after n).  Every
+// thread of the workgroup calls it (it synchronises); inactive teams compute
+// on zeros.  X: the team's LDS.
 template <int LOGN>
-__global__ void __launch_bounds__(FftShape<LOGN>::TPB) __attribute__((amdgpu_waves_per_eu(LOGN >= 8 ? 4 : 1)))
-k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
+__device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool active, const float2 *xsrc,
+                                          const float4 *sp, float2 (&v)[1 << FftShape<LOGN>::R0]) {
     using S = FftShape<LOGN>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
-    __shared__ float2 smem[S::LDS];
-    const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
-    const long long n = position_of(p, rd);
-    const long long t = n - 1;
-    if (n > p.L || n % N != 0 || n + N > p.L) return;  // uniform guard, as in k_direct
-    const long long ntiles = (long long)p.M * p.B * p.D;
-    const long long tile = (long long)blockIdx.x * S::PER_BLOCK + team;
-    const bool active = tile < ntiles;
-    float2 *X = smem + team * lds_len(N);
-    const int c = (int)(tile % p.D);
-    const int l = (int)(tile / ((long long)p.D * p.B));
-    const size_t row = (size_t)tile * (size_t)p.L;
-    const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + t - N + 1);
-    float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1);
-    const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
-
-    float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) {
         v[m] = active ? xsrc[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
@@ -91,6 +79,32 @@ k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
     dit_group<R0>(v, lt, LOGN, p.twid, p.logNT);
+}
+
+// Four waves per SIMD is what the LDS allows at every size from 2^8 on; the
+// register budget is held to that.
+template <int LOGN>
+__global__ void __launch_bounds__(FftShape<LOGN>::TPB) __attribute__((amdgpu_waves_per_eu(LOGN >= 8 ? 4 : 1)))
+k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
+    using S = FftShape<LOGN>;
+    constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
+    __shared__ float2 smem[S::LDS];
+    const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
+    const long long n = position_of(p, rd);
+    const long long t = n - 1;
+    if (n > p.L || n % N != 0 || n + N > p.L) return;  // uniform guard, as in k_direct
+    const long long ntiles = (long long)p.M * p.B * p.D;
+    const long long tile = (long long)blockIdx.x * S::PER_BLOCK + team;
+    const bool active = tile < ntiles;
+    float2 *X = smem + team * lds_len(N);
+    const int c = (int)(tile % p.D);
+    const int l = (int)(tile / ((long long)p.D * p.B));
+    const size_t row = (size_t)tile * (size_t)p.L;
+    const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + t - N + 1);
+    float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1);
+    const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
+    float2 v[1 << R0];
+    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v);
     if (active) {  // the accumulators, like the spectrum, are read late
         float2 acc[HALF0];
 #pragma unroll
@@ -99,6 +113,43 @@ k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
         for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
     }
     finish_position(p, n, advance);
+}
+
+// ---------------------------------------------------------------------------
+// Eager prefill, far part (the pages' prefill: the prompt's inputs of a layer
+// are all known at once).  Every gray block of edge N = 2^LOGN after a
+// position n <= P, n = (2j+1) N with j = blockIdx.y, for the B*D rows of layer
+// l: the same transform as k_fft_tile; targets t <= P add into the prefill
+// sums pre[(b, c)][t-1] (row stride pstride), later ones into the pending sums
+// of the history.  P is even, so no float2 of outputs straddles it.
+// ---------------------------------------------------------------------------
+template <int LOGN>
+__global__ void __launch_bounds__(FftShape<LOGN>::TPB) __attribute__((amdgpu_waves_per_eu(LOGN >= 8 ? 4 : 1)))
+k_pre_fft(Dev p, const float4 *__restrict__ spec, int l, long long P, float *pre, int pstride) {
+    using S = FftShape<LOGN>;
+    constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
+    __shared__ float2 smem[S::LDS];
+    const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
+    const long long n = (2LL * blockIdx.y + 1) * N;
+    const long long BD = (long long)p.B * p.D;
+    const long long k = (long long)blockIdx.x * S::PER_BLOCK + team;   // (b, c) of layer l
+    const bool active = k < BD && n <= P && n + N <= p.L;
+    float2 *X = smem + team * lds_len(N);
+    const long long kk = active ? k : 0;
+    const int c = (int)(kk % p.D);
+    const size_t row = ((size_t)l * BD + kk) * (size_t)p.L;
+    const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + n - N);
+    const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
+    float2 v[1 << R0];
+    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v);
+    if (active) {
+#pragma unroll
+        for (int m = 0; m < HALF0; ++m) {
+            const long long s0 = n + 2LL * (lt + (m << QLOG0));   // slot of target s0 + 1
+            float2 *dst = reinterpret_cast<float2 *>(s0 < P ? pre + (size_t)kk * pstride + s0 : p.buf + row + s0);
+            *dst = cadd(*dst, v[m + HALF0]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -641,6 +641,71 @@ __global__ void __launch_bounds__(256) k_eager_push(Dev p, int rd, long long row
 }
 
 // ---------------------------------------------------------------------------
+// Eager prefill ([R] prefill is eager, so the prompt's activations can be
+// dropped; [S] "Einschraenkungen": prefill dominates long prompts).  The state
+// it leaves is that of P teacher-forced positions: every gray block after
+// n <= P done, so later positions run the same schedule.  Per layer l, with all
+// of the layer's prompt inputs in the history:
+//   k_pre_near  pairs inside one aligned block of G positions (the gray blocks
+//               below G): pre[(b,c)][t-1] = sum h[t-s] x_s, t <= P;
+//   k_pre_fft   the FFT blocks of edge >= G (fi_fft_kernels.h), adding to pre;
+//   k_pre_red   the red cells of every t <= P, then the next layer's inputs.
+// 1-D grids over (b, c) x positions; P is a multiple of G.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_pre_in(Dev p, const float *x, long long P) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long BD = (long long)p.B * p.D;
+    if (i >= (size_t)(BD * P)) return;
+    const long long k = (long long)(i / P), t = (long long)(i % P);
+    p.buf[(size_t)k * p.L + t] = x[(size_t)t * BD + k];   // layer 0 rows come first
+}
+
+// One workgroup per (b, c) and aligned block of G <= 256 positions: the
+// block's inputs and taps 0..G-1 staged in LDS, one target per thread.
+constexpr int kPreNearMax = 256;
+__global__ void __launch_bounds__(kPreNearMax) k_pre_near(Dev p, int l, long long P, int G, float *pre,
+                                                          int pstride) {
+    __shared__ float xs[kPreNearMax], hs[kPreNearMax];
+    const long long nblk = P / G;
+    const long long k = blockIdx.x / nblk;                   // (b, c) of layer l
+    const long long s0 = (blockIdx.x % nblk) * G;            // the block's first slot
+    const int c = (int)(k % p.D), i = threadIdx.x;
+    const float *x = p.buf + ((size_t)l * p.B * p.D + k) * (size_t)p.L + s0;
+    if (i < G) {
+        xs[i] = x[i];
+        hs[i] = p.filt[filt_row(p, l, c) + i];
+    }
+    __syncthreads();
+    if (i >= G) return;
+    float acc = 0.f;                                         // target slot s0 + i: inputs s0 .. s0+i-1
+    for (int j = 0; j < i; ++j) acc = fmaf(hs[i - j], xs[j], acc);
+    pre[(size_t)k * pstride + s0 + i] = acc;
+}
+
+__global__ void __launch_bounds__(256) k_pre_red(Dev p, int l, long long P, const float *pre, int pstride,
+                                                 float *yout) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long BD = (long long)p.B * p.D;
+    if (i >= (size_t)(BD * P)) return;
+    const long long k = (long long)(i / P), t = (long long)(i % P) + 1;
+    const int c = (int)(k % p.D);
+    const float x = p.buf[((size_t)l * BD + k) * p.L + t - 1];
+    const float y = fmaf(p.filt[filt_row(p, l, c)], x, pre[(size_t)k * pstride + t - 1]);
+    if (p.recx) {
+        const size_t r = ((size_t)(t - 1) * p.M + l) * BD + k;
+        p.recx[r] = x;
+        p.recy[r] = y;
+    }
+    if (l + 1 < p.M) {
+        p.buf[((size_t)(l + 1) * BD + k) * p.L + t - 1] = apply_map(p.map, y);
+    } else {
+        p.ylast[(size_t)(t - 1) * BD + k] = y;
+        if (yout) yout[(size_t)(t - 1) * BD + k] = y;
+        if (t == P) p.xin[(size_t)((P + 1) & 1) * BD + k] = apply_map(p.fb, y);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // External-block mode: the red cell of one layer at position n for all (b, c):
 // y = pending + h0 * q, and q becomes the layer input at n.
 // ---------------------------------------------------------------------------

@@ -36,7 +36,8 @@ class Options(ctypes.Structure):
                 ("tau_split", ctypes.c_int), ("record", ctypes.c_int), ("use_graphs", ctypes.c_int),
                 ("block_graph_log2", ctypes.c_int), ("filters_on_device", ctypes.c_int),
                 ("fft_max_log2", ctypes.c_int), ("time_blocks", ctypes.c_int),
-                ("defer_wide", ctypes.c_int), ("chunk_direct", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+                ("defer_wide", ctypes.c_int), ("chunk_direct", ctypes.c_int), ("eager_prefill", ctypes.c_int),
+                ("reserved", ctypes.c_int * 3)]
 
 
 _lib = None
@@ -122,7 +123,7 @@ class Context:
 
     def __init__(self, filters, batch, *, map=MAP_TANH, feedback=FEEDBACK_TANH, tau_mode=TAU_AUTO,
                  tau_split=-1, record=False, use_graphs=True, block_graph_log2=6, fft_max_log2=14,
-                 time_blocks=False, defer_wide=False, chunk_direct=True, device=None):
+                 time_blocks=False, defer_wide=False, chunk_direct=True, eager_prefill=True, device=None):
         import torch
         if not torch.cuda.is_available():
             raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
@@ -136,6 +137,7 @@ class Context:
         opt.time_blocks = int(time_blocks)
         opt.defer_wide = int(defer_wide)
         opt.chunk_direct = int(chunk_direct)
+        opt.eager_prefill = int(eager_prefill)
         if isinstance(filters, np.ndarray):
             f = np.ascontiguousarray(filters, dtype=np.float32)
             fptr = f.ctypes.data_as(ctypes.c_void_p)
