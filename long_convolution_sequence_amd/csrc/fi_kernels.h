@@ -393,6 +393,9 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
+// A helper lane's partial sum over its taps m < 8 (NF + 1) (tap m: slot row
+// row0 + 8m, register hreg[m]): groups below NF read their rows as they are,
+// group NF clamps its rows to G, the zero row (taps that lie before the chunk).
 template <int NF>
 __device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho, int G) {
     constexpr int S = 8, SP = kChunkSlot;
@@ -508,7 +511,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
         // its tap-1 term: fft + sum_{k>=2} h[k] x_{i+1-k}.  Tap m of a lane
         // (k = seg + 8m) reads slot i+1-k at row row0 + 8m.  Taps come in four
         // groups of eight m; the first nf = (i+2)/64 groups exist in every
-        // lane, the next one in some (its other lanes read the zero rows past
+        // lane, the next one in some (its other lanes read the zero row past
         // the chunk's first slot), the rest in none.  nf is uniform and picks
         // a branch-free body, so all of a position's reads are in flight.
         for (int i = 0; i < G; ++i) {
