@@ -762,18 +762,16 @@ fi_status run_chunk(fi_ctx *c, int64_t cb, const float *xseq) {
     c->ring_stale = true;
     if (n >= c->L) return FI_OK;
     const int q = class_of(c, n);
+    // the gray block's last kernel is stamped and published by its last
+    // workgroup (for the widest blocks block 0 ends far earlier)
     if (c->opt.time_blocks) {
-        fi_status s = launch_timed_fft(c, n, q, 0);
+        fi_status s = launch_timed_fft(c, n, q, 2);
         if (s != FI_OK) return s;
     } else if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
-        HIPCK(c, launch_fft_sub(c, rd_of(n), q, c->stream, 0, nullptr, nullptr, n));
+        HIPCK(c, launch_fft_sub(c, rd_of(n), q, c->stream, 2, nullptr, nullptr, n));
     } else {
-        HIPCK(c, launch_fft(c, rd_of(n), q, c->stream, 0));
+        HIPCK(c, launch_fft(c, rd_of(n), q, c->stream, 2));
     }
-    // stamped after the whole gray block (an FFT kernel's own stamp is its
-    // block 0's end, which for the widest blocks is far from the kernel's end)
-    hipLaunchKernelGGL(k_publish, dim3(1), dim3(64), 0, c->stream, c->dev, (long long)n);
-    HIPCK(c, hipGetLastError());
     return FI_OK;
 }
 

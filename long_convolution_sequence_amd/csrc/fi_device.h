@@ -113,13 +113,28 @@ __device__ __forceinline__ size_t filt_row(const Dev &p, int l, int c) {
 // fixed when a position's launches are recorded, so graphs can replay them).
 __device__ __forceinline__ long long position_of(const Dev &p, int rd) { return p.st->pos[rd] + 1; }
 
-// End of the last kernel of position n: block 0 publishes n (into the other
+// End of the last kernel of position n: one block publishes n (into the other
 // parity slot, which no kernel of this position reads) and stamps the device
 // clock.  The next kernel on the stream sees the new value through the kernel
-// boundary.  The stamp is block 0's end, within a block's run time of the
-// kernel's end.
+// boundary.  advance 1: the stamp is block 0's end (for a kernel whose blocks
+// all run at once, within a block's run time of the kernel's end); advance 2:
+// the last block's end, for kernels of many rounds of blocks.
 __device__ __forceinline__ void finish_position(const Dev &p, long long n, int advance) {
     if (!advance) return;
+    if (advance == 2) {
+        // the last workgroup in dispatch order stamps and publishes n once its
+        // own threads are done: blocks are dispatched in order, so it ends
+        // within one block's run time of the kernel's end
+        if (blockIdx.x == gridDim.x - 1 && blockIdx.y == gridDim.y - 1) {
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                p.stamps[n] = (long long)wall_clock64();
+                p.st->pos[(n - 1) & 1] = n - 1;
+                p.st->pos[n & 1] = n;
+            }
+        }
+        return;
+    }
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         p.stamps[n] = (long long)wall_clock64();
         p.st->pos[n & 1] = n;

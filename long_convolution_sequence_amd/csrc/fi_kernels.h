@@ -556,16 +556,6 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     }
 }
 
-// End of an FFT position reached from a chunk: n is published and stamped
-// once every gray-block kernel of n has finished (one thread).
-__global__ void __launch_bounds__(64) k_publish(Dev p, long long n) {
-    if (threadIdx.x == 0) {
-        p.stamps[n] = (long long)wall_clock64();
-        p.st->pos[(n - 1) & 1] = n - 1;
-        p.st->pos[n & 1] = n;
-    }
-}
-
 // Tap table of the chunk kernels' helper lanes: per (l, c), 8 runs of 32
 // floats, run s holding taps s, s+8, .., s+248 (zero past L).
 __global__ void __launch_bounds__(256) k_taps(Dev p, float *htap) {
