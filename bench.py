@@ -46,9 +46,10 @@ def fft_alg_bytes(w, U):
 
 
 def kernel_source_hash():
-    """Hash of the FFT gray-block kernel sources (the kernels the traffic summary covers)."""
+    """Hash of the FFT gray-block kernel sources (the kernels the traffic summary covers,
+    with the device helpers they include)."""
     h = hashlib.sha256()
-    for f in ("fi_fft_kernels.h", "fi_fft.h"):
+    for f in ("fi_fft_kernels.h", "fi_fft.h", "fi_device.h"):
         with open(os.path.join(ROOT, "long_convolution_sequence_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
