@@ -226,13 +226,14 @@ __device__ __forceinline__ void lds_group(float2 *X, int lt, const float2 *__res
     }
 }
 
-// Forward stage groups 1 .. NPASS-1, each preceded by a block barrier.
-template <int LOGN, int PASS>
+// Forward stage groups PASS .. END-1 (by default through NPASS-1), each
+// preceded by a block barrier.
+template <int LOGN, int PASS, int END = FftShape<LOGN>::NPASS>
 __device__ __forceinline__ void forward_groups(float2 *X, int lt, const float2 *__restrict__ tw, int logNT) {
-    if constexpr (PASS < FftShape<LOGN>::NPASS) {
+    if constexpr (PASS < END) {
         __syncthreads();
         lds_group<LOGN, PASS, true>(X, lt, tw, logNT);
-        forward_groups<LOGN, PASS + 1>(X, lt, tw, logNT);
+        forward_groups<LOGN, PASS + 1, END>(X, lt, tw, logNT);
     }
 }
 

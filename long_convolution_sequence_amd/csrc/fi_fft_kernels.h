@@ -24,10 +24,13 @@ namespace fi {
 // thread holds in v[HALF0 + m] the outputs at float2 index lt + (m << QLOG0)
 // of the exact upper half (targets n+1 .. n+N of the block after n).  Every
 // thread of the workgroup calls it (it synchronises); inactive teams compute
-// on zeros.  X: the team's LDS.
-template <int LOGN>
+// on zeros.  X: the team's LDS.  before_last() runs just before the last
+// inverse stage group (a caller issues its loads of the targets there, so
+// that the group's arithmetic covers their latency).
+template <int LOGN, typename BeforeLast>
 __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool active, const float2 *xsrc,
-                                          const float4 *sp, float2 (&v)[1 << FftShape<LOGN>::R0]) {
+                                          const float4 *sp, float2 (&v)[1 << FftShape<LOGN>::R0],
+                                          BeforeLast &&before_last) {
     using S = FftShape<LOGN>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
 #pragma unroll
@@ -38,9 +41,13 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
-    forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
-    // this thread's spectrum pairs, loaded only now: held across the forward
-    // transform they would cost the registers of a fourth wave per SIMD
+    // this thread's spectrum pairs, loaded late: held across the whole forward
+    // transform they would cost the registers of a fourth wave per SIMD.  When
+    // the last stage group is short (fewer than four stages), they are issued
+    // before it, so that it covers part of their latency.
+    constexpr int NP = S::NPASS;
+    constexpr bool EARLY = NP >= 2 && LOGN - 4 * (NP - 1) < 4;
+    forward_groups<LOGN, 1, EARLY ? NP - 1 : NP>(X, lt, p.twid, p.logNT);
     constexpr int PAIRS = (N / 2 + TT - 1) / TT;
     float4 gs[PAIRS];
 #pragma unroll
@@ -48,6 +55,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
         const int e = lt + m * TT;
         gs[m] = (active && e < N / 2) ? sp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if constexpr (EARLY) forward_groups<LOGN, NP - 1, NP>(X, lt, p.twid, p.logNT);
     __syncthreads();
 
     // bins of the real transform times the filter spectrum, re-packed for the inverse
@@ -76,6 +84,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     }
     __syncthreads();
     inverse_groups<LOGN, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    before_last();
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
     dit_group<R0>(v, lt, LOGN, p.twid, p.logNT);
@@ -104,11 +113,14 @@ k_fft_tile(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
     float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1);
     const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
     float2 v[1 << R0];
-    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v);
-    if (active) {  // the accumulators, like the spectrum, are read late
-        float2 acc[HALF0];
+    // the pending sums, like the spectrum, are read late: during the last
+    // inverse stage group
+    float2 acc[HALF0];
+    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v, [&]() {
 #pragma unroll
-        for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
+        for (int m = 0; m < HALF0; ++m) acc[m] = active ? adst[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
+    });
+    if (active) {
 #pragma unroll
         for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
     }
@@ -141,7 +153,7 @@ k_pre_fft(Dev p, const float4 *__restrict__ spec, int l, long long P, float *pre
     const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + n - N);
     const float4 *sp = spec + ((size_t)l * p.D + c) * (N / 2);
     float2 v[1 << R0];
-    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v);
+    fft_block<LOGN>(p, X, lt, active, xsrc, sp, v, []() {});
     if (active) {
 #pragma unroll
         for (int m = 0; m < HALF0; ++m) {

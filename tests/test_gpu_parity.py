@@ -262,3 +262,21 @@ def test_schedule_and_stamps():
         assert ctx.position == 0
         ctx.generate(3, want_y=False)
         assert ctx.position == 3
+
+
+def test_stamps_with_chunks():
+    """Positions run in chunks of 64 (first FFT class 6): every position is stamped in order,
+    including a chunk's last position, which is stamped by its FFT gray block's last workgroup,
+    also when a run stops right there."""
+    M, B, D, L = 2, 1, 16, 1024
+    say(f"case stamps with chunks M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 21, decay=64.0)
+    with fi.Context(_cuda(h), B, tau_split=6) as ctx:
+        assert ctx.schedule(64) == (6, fi.PATH_FFT)
+        ctx.generate(64, want_y=False)
+        st = ctx.stamps(1, 64)
+        assert (st > 0).all() and (np.diff(st) >= 0).all()
+        ctx.generate(L - 64, want_y=False)
+        st = ctx.stamps(1, L)
+        assert (st > 0).all() and (np.diff(st) >= 0).all()
+        assert ctx.position == L
