@@ -145,8 +145,7 @@ __device__ __forceinline__ void apply_powers(float2 (&v)[1 << R], float2 w) {
 // half of v is known to be zero.  TWIDDLE false: r is known to be 0 (the
 // group spans a whole block), so the outer twiddles are all 1.
 template <int R, bool PRUNED = false, bool TWIDDLE = true>
-__device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
-                                          const float2 *__restrict__ tw, int logNT) {
+__device__ __forceinline__ void dif_group_w(float2 (&v)[1 << R], float2 w) {
     static_for<0, R>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         constexpr int half = (1 << R) >> (t + 1);
@@ -164,15 +163,19 @@ __device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
             }
         });
     });
-    if constexpr (TWIDDLE) apply_powers<R, false>(v, twiddle(tw, logNT, slog, r));
+    if constexpr (TWIDDLE) apply_powers<R, false>(v, w);
+}
+template <int R, bool PRUNED = false, bool TWIDDLE = true>
+__device__ __forceinline__ void dif_group(float2 (&v)[1 << R], int r, int slog,
+                                          const float2 *__restrict__ tw, int logNT) {
+    dif_group_w<R, PRUNED, TWIDDLE>(v, TWIDDLE ? twiddle(tw, logNT, slog, r) : make_float2(1.f, 0.f));
 }
 
 // Inverse of dif_group up to the factor 2^R: conjugate outer twiddles, then
 // the stages in reverse order with conjugate constant roots.
 template <int R, bool TWIDDLE = true>
-__device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
-                                          const float2 *__restrict__ tw, int logNT) {
-    if constexpr (TWIDDLE) apply_powers<R, true>(v, twiddle(tw, logNT, slog, r));
+__device__ __forceinline__ void dit_group_w(float2 (&v)[1 << R], float2 w) {
+    if constexpr (TWIDDLE) apply_powers<R, true>(v, w);
     static_for<0, R>([&](auto tc) {
         constexpr int t = R - 1 - decltype(tc)::value;
         constexpr int half = (1 << R) >> (t + 1);
@@ -187,6 +190,11 @@ __device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
             }
         });
     });
+}
+template <int R, bool TWIDDLE = true>
+__device__ __forceinline__ void dit_group(float2 (&v)[1 << R], int r, int slog,
+                                          const float2 *__restrict__ tw, int logNT) {
+    dit_group_w<R, TWIDDLE>(v, TWIDDLE ? twiddle(tw, logNT, slog, r) : make_float2(1.f, 0.f));
 }
 
 // Compile-time description of a transform of 2^LOGN complex points.
@@ -203,14 +211,31 @@ struct FftShape {
     static constexpr int LDS = PER_BLOCK * lds_len(N);       // float2 per block
 };
 
-// Stage group PASS (>= 1) through LDS, all threads of one transform team.
+// The outer twiddle root W_S^r of thread lt's group in stage group PASS
+// (PASS >= 1: the LDS groups; PASS = 0: the outer group, S = 2^LOGN, r = lt).
+// Every twiddled LDS group has four stages, so a thread owns exactly one
+// group of it: the root can be read before the barrier that precedes the
+// group, and its latency hides behind the barrier.
+template <int LOGN, int PASS>
+__device__ __forceinline__ float2 group_root(int lt, const float2 *__restrict__ tw, int logNT) {
+    constexpr int SLOG = LOGN - 4 * PASS;
+    constexpr int R = SLOG < 4 ? SLOG : 4;
+    constexpr int QLOG = SLOG - R;
+    if constexpr (PASS == 0) return twiddle(tw, logNT, LOGN, lt);
+    else if constexpr (QLOG > 0) return twiddle(tw, logNT, SLOG, lt & ((1 << QLOG) - 1));
+    else return make_float2(1.f, 0.f);
+}
+
+// Stage group PASS (>= 1) through LDS, all threads of one transform team; w is
+// group_root<LOGN, PASS>.
 template <int LOGN, int PASS, bool FWD>
-__device__ __forceinline__ void lds_group(float2 *X, int lt, const float2 *__restrict__ tw, int logNT) {
+__device__ __forceinline__ void lds_group(float2 *X, int lt, float2 w) {
     constexpr int SLOG = LOGN - 4 * PASS;
     constexpr int R = SLOG < 4 ? SLOG : 4;
     constexpr int QLOG = SLOG - R;
     constexpr int G = 1 << (LOGN - R);
     constexpr int TT = FftShape<LOGN>::TT;
+    static_assert(QLOG == 0 || G == TT, "a twiddled group is the only one of its thread");
     for (int g = lt; g < G; g += TT) {
         const int r = g & ((1 << QLOG) - 1);
         const int base = ((g >> QLOG) << SLOG) + r;
@@ -218,32 +243,53 @@ __device__ __forceinline__ void lds_group(float2 *X, int lt, const float2 *__res
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) v[m] = X[lpad(base + (m << QLOG))];
         if constexpr (FWD)
-            dif_group<R, false, (QLOG > 0)>(v, r, SLOG, tw, logNT);
+            dif_group_w<R, false, (QLOG > 0)>(v, w);
         else
-            dit_group<R, (QLOG > 0)>(v, r, SLOG, tw, logNT);
+            dit_group_w<R, (QLOG > 0)>(v, w);
 #pragma unroll
         for (int m = 0; m < (1 << R); ++m) X[lpad(base + (m << QLOG))] = v[m];
     }
 }
 
 // Forward stage groups PASS .. END-1 (by default through NPASS-1), each
-// preceded by a block barrier.
-template <int LOGN, int PASS, int END = FftShape<LOGN>::NPASS>
+// preceded by a block barrier.  PRE: each group's root is read before its
+// barrier (off where the registers it holds across the barrier would spill).
+template <int LOGN, int PASS, int END = FftShape<LOGN>::NPASS, bool PRE = true>
 __device__ __forceinline__ void forward_groups(float2 *X, int lt, const float2 *__restrict__ tw, int logNT) {
     if constexpr (PASS < END) {
-        __syncthreads();
-        lds_group<LOGN, PASS, true>(X, lt, tw, logNT);
-        forward_groups<LOGN, PASS + 1, END>(X, lt, tw, logNT);
+        if constexpr (PRE) {
+            const float2 w = group_root<LOGN, PASS>(lt, tw, logNT);
+            __syncthreads();
+            lds_group<LOGN, PASS, true>(X, lt, w);
+        } else {
+            __syncthreads();
+            lds_group<LOGN, PASS, true>(X, lt, group_root<LOGN, PASS>(lt, tw, logNT));
+        }
+        forward_groups<LOGN, PASS + 1, END, PRE>(X, lt, tw, logNT);
     }
 }
 
-// Inverse stage groups PASS, PASS-1, ..., 1, each followed by a block barrier.
-template <int LOGN, int PASS>
-__device__ __forceinline__ void inverse_groups(float2 *X, int lt, const float2 *__restrict__ tw, int logNT) {
+// Inverse stage groups PASS, PASS-1, ..., 1, each followed by a block barrier;
+// w = group_root<LOGN, PASS> (PRE: read by the caller before its barrier, and
+// each next root read here before the barrier; otherwise w is not used and
+// every root is read after the barrier).  Returns group_root<LOGN, 0>, the
+// root of the outer group that follows.
+template <int LOGN, int PASS, bool PRE = true>
+__device__ __forceinline__ float2 inverse_groups(float2 *X, int lt, const float2 *__restrict__ tw, int logNT,
+                                                 float2 w) {
     if constexpr (PASS >= 1) {
-        lds_group<LOGN, PASS, false>(X, lt, tw, logNT);
-        __syncthreads();
-        inverse_groups<LOGN, PASS - 1>(X, lt, tw, logNT);
+        if constexpr (PRE) {
+            lds_group<LOGN, PASS, false>(X, lt, w);
+            const float2 wn = group_root<LOGN, PASS - 1>(lt, tw, logNT);
+            __syncthreads();
+            return inverse_groups<LOGN, PASS - 1, PRE>(X, lt, tw, logNT, wn);
+        } else {
+            lds_group<LOGN, PASS, false>(X, lt, group_root<LOGN, PASS>(lt, tw, logNT));
+            __syncthreads();
+            return inverse_groups<LOGN, PASS - 1, PRE>(X, lt, tw, logNT, w);
+        }
+    } else {
+        return PRE ? w : group_root<LOGN, 0>(lt, tw, logNT);
     }
 }
 

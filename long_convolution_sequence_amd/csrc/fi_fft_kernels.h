@@ -82,12 +82,13 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
             X[p2] = D2;
         }
     }
+    const float2 wi = group_root<LOGN, S::NPASS - 1>(lt, p.twid, p.logNT);
     __syncthreads();
-    inverse_groups<LOGN, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    const float2 w0 = inverse_groups<LOGN, S::NPASS - 1>(X, lt, p.twid, p.logNT, wi);
     before_last();
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_group<R0>(v, lt, LOGN, p.twid, p.logNT);
+    dit_group_w<R0>(v, w0);
 }
 
 // Four waves per SIMD is what the LDS allows at every size from 2^8 on; the
@@ -240,21 +241,22 @@ __device__ __forceinline__ void half_forward(const Dev &p, float2 *X, int lt, bo
     dif_group<R0>(v, lt, LOGM, p.twid, p.logNT);
 #pragma unroll
     for (int m = 0; m < 16; ++m) X[lpad(lt + (m << QLOG0))] = v[m];
-    forward_groups<LOGM, 1>(X, lt, p.twid, p.logNT);
+    forward_groups<LOGM, 1, S::NPASS, false>(X, lt, p.twid, p.logNT);
 }
 
 // Inverse transform of one half from X (items already re-packed; the caller
 // has synchronised) and its accumulation into dst[0..M): the odd half
-// subtracts W_{2M}^{-m} v, the even half adds v.
+// subtracts W_{2M}^{-m} v, the even half adds v.  The roots are read after
+// the barriers here: held across them, they spill in these kernels.
 template <int LOGM, bool ODD>
 __device__ __forceinline__ void half_inverse_acc(const Dev &p, float2 *X, int lt, bool active, float2 *dst) {
     using S = FftShape<LOGM>;
     constexpr int R0 = S::R0, QLOG0 = S::QLOG0;
-    inverse_groups<LOGM, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    const float2 w0 = inverse_groups<LOGM, S::NPASS - 1, false>(X, lt, p.twid, p.logNT, make_float2(1.f, 0.f));
     float2 v[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_group<R0>(v, lt, LOGM, p.twid, p.logNT);
+    dit_group_w<R0>(v, w0);
     if (!active) return;
     const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGM + 1, lt) : make_float2(1.f, 0.f);
     // in four runs of four, so that the accumulators never all occupy registers
@@ -567,12 +569,13 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
         mac(st + 1, a1, g1);
         if ((st + 1) % K == K - 1) flush(((st + 1) / K) * CH);
     }
+    const float2 wi = group_root<LOGV, S::NPASS - 1>(lt, p.twid, p.logNT);
     __syncthreads();
-    inverse_groups<LOGV, S::NPASS - 1>(X, lt, p.twid, p.logNT);
+    const float2 w0 = inverse_groups<LOGV, S::NPASS - 1>(X, lt, p.twid, p.logNT, wi);
     float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-    dit_group<R0>(v, lt, LOGV, p.twid, p.logNT);
+    dit_group_w<R0>(v, w0);
     float2 acc[HALF0];
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];

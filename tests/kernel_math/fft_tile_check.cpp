@@ -12,8 +12,8 @@ template <int LOGN> struct Emu {
   using S = FftShape<LOGN>;
   static constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
   template <int PASS, bool FWD> static void groups(std::vector<float2>& X, const float2* tw, int logNT) {
-    if constexpr (FWD) { if constexpr (PASS < S::NPASS) { for (int lt = 0; lt < TT; ++lt) lds_group<LOGN, PASS, true>(X.data(), lt, tw, logNT); groups<PASS + 1, true>(X, tw, logNT); } }
-    else { if constexpr (PASS >= 1) { for (int lt = 0; lt < TT; ++lt) lds_group<LOGN, PASS, false>(X.data(), lt, tw, logNT); groups<PASS - 1, false>(X, tw, logNT); } }
+    if constexpr (FWD) { if constexpr (PASS < S::NPASS) { for (int lt = 0; lt < TT; ++lt) lds_group<LOGN, PASS, true>(X.data(), lt, group_root<LOGN, PASS>(lt, tw, logNT)); groups<PASS + 1, true>(X, tw, logNT); } }
+    else { if constexpr (PASS >= 1) { for (int lt = 0; lt < TT; ++lt) lds_group<LOGN, PASS, false>(X.data(), lt, group_root<LOGN, PASS>(lt, tw, logNT)); groups<PASS - 1, false>(X, tw, logNT); } }
   }
   // forward transform of 2N reals src (pruned: upper half zero) -> X (bit reversed, LDS layout)
   static void forward(const float* src, bool pruned, std::vector<float2>& X, const float2* tw, int logNT) {
@@ -52,7 +52,7 @@ template <int LOGN> struct Emu {
     for (int lt = 0; lt < TT; ++lt) {
       float2 v[1 << R0];
       for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
-      dit_group<R0>(v, lt, LOGN, tw, logNT);
+      dit_group_w<R0>(v, group_root<LOGN, 0>(lt, tw, logNT));
       for (int m = 0; m < HALF0; ++m) a2[lt + (m << QLOG0)] = cadd(a2[lt + (m << QLOG0)], v[m + HALF0]);
     }
   }
