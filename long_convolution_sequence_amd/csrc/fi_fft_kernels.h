@@ -58,11 +58,16 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     if constexpr (EARLY) forward_groups<LOGN, NP - 1, NP>(X, lt, p.twid, p.logNT);
     __syncthreads();
 
-    // bins of the real transform times the filter spectrum, re-packed for the inverse
+    // bins of the real transform times the filter spectrum, re-packed for the
+    // inverse; the items' pair twiddles are all read first, so that their
+    // latency is paid once (item 0 reads an unused entry)
+    static_assert((N / 2) % TT == 0, "items per thread");
+    float2 wp[PAIRS];
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) wp[m] = p.ptw[N / 2 + lt + m * TT];
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
         const int e = lt + m * TT;
-        if (e >= N / 2) break;
         const float4 g = gs[m];
         if (e == 0) {
             const float2 C0 = X[0];
@@ -74,7 +79,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
         } else {
             const PairSlot ps = pair_slot(LOGN, e);
             const int p1 = lpad(ps.pj), p2 = lpad(ps.pm);
-            const float2 W = p.ptw[N / 2 + e];
+            const float2 W = wp[m];
             float2 A1, A2, D1, D2;
             real_bins(X[p1], X[p2], W, A1, A2);
             pack_inverse(cmul(A1, make_float2(g.x, g.y)), cmul(A2, make_float2(g.z, g.w)), W, D1, D2);
@@ -461,7 +466,15 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
     forward_groups<LOGV, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     float4 *dst = scratch + ((size_t)tile * K + i) * (N / 2);
-    for (int e = lt; e < N / 2; e += TT) {
+    // the items' pair twiddles first (item 0 reads an unused entry)
+    constexpr int PAIRS = N / 2 / TT;
+    static_assert((N / 2) % TT == 0, "items per thread");
+    float2 wp[PAIRS];
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) wp[m] = p.ptw[N / 2 + lt + m * TT];
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) {
+        const int e = lt + m * TT;
         if (e == 0) {
             const float2 C0 = X[0];
             const float2 Ch = X[lpad(1)];
@@ -469,7 +482,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
         } else {
             const PairSlot ps = pair_slot(LOGV, e);
             float2 A1, A2;
-            real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], p.ptw[N / 2 + e], A1, A2);
+            real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], wp[m], A1, A2);
             dst[e] = make_float4(A1.x, A1.y, A2.x, A2.y);
         }
     }
