@@ -88,19 +88,25 @@ __device__ __forceinline__ float apply_map(int kind, float y) { return kind == 0
 // least relative error (Lawson's iteratively reweighted least squares, in
 // double on Chebyshev nodes; coefficients rounded to float): under 0.9 ulp.
 // Both are evaluated and one selected, so lanes on either side never diverge.
-__device__ __forceinline__ float tanh_chain(float y) {
-    const float a = fabsf(y);
-    const float e = __builtin_amdgcn_exp2f(a * 2.88539008f);      // e^{2a} = 2^{2a log2(e)}
-    const float big = fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+__device__ __forceinline__ float tanh_odd_poly(float a) {   // |y| + |y|^3 P(|y|^2), a = |y|
     const float s = a * a;
     float q = fmaf(s, 0.0015847263857722282f, -0.007409499958157539f);
     q = fmaf(s, q, 0.021302949637174606f);
     q = fmaf(s, q, -0.05385231971740723f);
     q = fmaf(s, q, 0.13332220911979675f);
     q = fmaf(s, q, -0.33333298563957214f);
-    const float small = fmaf(a * s, q, a);
+    return fmaf(a * s, q, a);
+}
+__device__ __forceinline__ float tanh_chain(float y) {
+    const float a = fabsf(y);
+    const float e = __builtin_amdgcn_exp2f(a * 2.88539008f);      // e^{2a} = 2^{2a log2(e)}
+    const float big = fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+    const float small = tanh_odd_poly(a);
     return copysignf(a < 0.8f ? small : big, y);
 }
+// The polynomial half alone: equal to tanh_chain(y) for |y| < 0.8 (bit for
+// bit), meaningless above.
+__device__ __forceinline__ float tanh_small(float y) { return copysignf(tanh_odd_poly(fabsf(y)), y); }
 
 __device__ __forceinline__ size_t act_row(const Dev &p, int l, int b, int c) {
     return ((size_t)((size_t)l * p.B + b) * p.D + c) * (size_t)p.L;

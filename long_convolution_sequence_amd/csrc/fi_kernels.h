@@ -337,23 +337,47 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
             float a[MT];
 #pragma unroll
             for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
+            const float x0 = x;
+            unsigned long long far = 0;                // lanes with some |y| >= 0.8 (polynomial pass)
+            // the position's layers; FULL = false: tanh by its polynomial half
+            // alone, with a vote on whether every |y| stayed below 0.8
+            auto layers = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                x = x0;
 #pragma unroll
-            for (int k = 0; k < MT; ++k) {
-                y = fmaf(h0[k], x, a[k]);
-                xq[k] = x;
-                if constexpr (REC) {
-                    if (on) {
-                        const size_t r = ((size_t)(t - 1) * MT + k) * BD + chain;
-                        p.recx[r] = x;
-                        p.recy[r] = y;
+                for (int k = 0; k < MT; ++k) {
+                    y = fmaf(h0[k], x, a[k]);
+                    xq[k] = x;
+                    if constexpr (REC) {
+                        if (on) {
+                            const size_t r = ((size_t)(t - 1) * MT + k) * BD + chain;
+                            p.recx[r] = x;
+                            p.recy[r] = y;
+                        }
+                    }
+                    float th;
+                    if constexpr (FULL) {
+                        th = tanh_chain(y);
+                    } else {
+                        th = tanh_small(y);
+                        far |= __builtin_amdgcn_ballot_w64(!(fabsf(y) < 0.8f));
+                    }
+                    if constexpr (TANH_ALL) {
+                        x = th;
+                    } else {
+                        x = (k + 1 < MT ? map_id : fb_id) ? y : th;   // both maps evaluated, one selected
                     }
                 }
-                const float th = tanh_chain(y);
-                if constexpr (TANH_ALL) {
-                    x = th;
-                } else {
-                    x = (k + 1 < MT ? map_id : fb_id) ? y : th;   // both maps evaluated, one selected
-                }
+            };
+            if constexpr (TANH_ALL) {
+                // Both maps tanh: the polynomial pass first, which keeps the
+                // exponential's two transcendental steps off the chain; if any
+                // lane of the wave left its range, the position is run again
+                // with the full tanh (same values where both apply).
+                layers(std::false_type{});
+                if (far) layers(std::true_type{});
+            } else {
+                layers(std::true_type{});
             }
             if (on) {
 #pragma unroll
