@@ -303,6 +303,8 @@ constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
 constexpr int kChunkSlot = 120;
 // zero row after the slots: a helper tap that lies before the chunk reads it
 constexpr int kChunkZeroRows = 1;
+// positions a chain stays on the full tanh after its polynomial pass failed
+constexpr int kChainFullRun = 128;
 // chunk kernel variants: records every layer's input and output; both maps tanh
 constexpr int kChunkRec = 1, kChunkTanh = 2;
 
@@ -328,6 +330,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
     }
     float xf = on ? p.xin[(size_t)((cb + 1) & 1) * BD + chain] : 0.f;   // feedback input
     const bool map_id = !TANH_ALL && p.map != 0, fb_id = !TANH_ALL && p.fb != 0;
+    int full_left = 0;                         // wave-uniform: positions left on the full tanh
     for (int i = 0; i < G; ++i) {
         const long long t = cb + 1 + i;        // position
         float x = xs ? xs[i * CH + jr] : xf;   // teacher-forced inputs, staged in LDS
@@ -338,7 +341,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
 #pragma unroll
             for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
             const float x0 = x;
-            unsigned long long far = 0;                // lanes with some |y| >= 0.8 (polynomial pass)
+            unsigned long long far = 0;                // lanes with some |y| >= 0.8
             // the position's layers; FULL = false: tanh by its polynomial half
             // alone, with a vote on whether every |y| stayed below 0.8
             auto layers = [&](auto full) {
@@ -355,13 +358,8 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                             p.recy[r] = y;
                         }
                     }
-                    float th;
-                    if constexpr (FULL) {
-                        th = tanh_chain(y);
-                    } else {
-                        th = tanh_small(y);
-                        far |= __builtin_amdgcn_ballot_w64(!(fabsf(y) < 0.8f));
-                    }
+                    const float th = FULL ? tanh_chain(y) : tanh_small(y);
+                    if constexpr (!FULL) far |= __builtin_amdgcn_ballot_w64(!(fabsf(y) < 0.8f));
                     if constexpr (TANH_ALL) {
                         x = th;
                     } else {
@@ -370,12 +368,22 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                 }
             };
             if constexpr (TANH_ALL) {
-                // Both maps tanh: the polynomial pass first, which keeps the
-                // exponential's two transcendental steps off the chain; if any
-                // lane of the wave left its range, the position is run again
-                // with the full tanh (same values where both apply).
-                layers(std::false_type{});
-                if (far) layers(std::true_type{});
+                // Both maps tanh.  The polynomial pass runs first, which keeps
+                // the exponential's two transcendental steps off the chain; if
+                // some lane of the wave left its range, the position runs again
+                // with the full tanh (same values where both apply), and so do
+                // the next kChainFullRun positions before the polynomial pass
+                // is tried again (activations that stay large then cost one
+                // extra pass per kChainFullRun positions).
+                if (full_left == 0) {
+                    far = 0;
+                    layers(std::false_type{});
+                    if (far) full_left = kChainFullRun + 1;
+                }
+                if (full_left > 0) {
+                    layers(std::true_type{});
+                    --full_left;
+                }
             } else {
                 layers(std::true_type{});
             }
