@@ -286,8 +286,8 @@ __global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advan
 //
 // LDS: heads h01[R] (h[0], h[1]); slots xp[G][kChunkSlot], slot s at row
 // G-1-s (reversed, so that the taps of a helper lie at increasing addresses:
-// immediate offsets, read in pairs); a zero row G; teacher-forced inputs
-// xs[G][CH].  Rows rho = j * M + l for chain c0 + j, layer l.
+// immediate offsets, read in pairs); zero rows G .. G+63; teacher-forced
+// inputs xs[G][CH].  Rows rho = j * M + l for chain c0 + j, layer l.
 //
 // Global memory inside the position loop: the chain's last-layer output, the
 // helpers' history stores (one 128-byte line per row every 32 positions, for
@@ -301,8 +301,8 @@ constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
 // floats per slot: >= the rows, and 8 slots apart = 15 x 256 bytes (one
 // read2st64 reaches two taps); the eight lanes of a row then hit distinct banks
 constexpr int kChunkSlot = 120;
-// zero row after the slots: a helper tap that lies before the chunk reads it
-constexpr int kChunkZeroRows = 1;
+// zero rows after the slots: the helper taps that lie before the chunk read them
+constexpr int kChunkZeroRows = 64;
 // positions a chain stays on the full tanh after its polynomial pass failed
 constexpr int kChainFullRun = 128;
 // chunk kernel variants: records every layer's input and output; both maps tanh
@@ -426,18 +426,23 @@ __device__ __forceinline__ float sum8(float v) {
 }
 
 // A helper lane's partial sum over its taps m < 8 (NF + 1) (tap m: slot row
-// row0 + 8m, register hreg[m]): groups below NF read their rows as they are,
-// group NF clamps its rows to G, the zero row (taps that lie before the chunk).
+// row0 + 8m, register hreg[m]).  Taps of group NF that lie before the
+// chunk's first slot read the zero rows after the slots (rows G .. G+63:
+// with NF = (i+2)/64, row0 + 8m never passes G+63), so every tap is a plain
+// read at a fixed offset.
 template <int NF>
-__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho, int G) {
+__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho) {
     constexpr int S = 8, SP = kChunkSlot;
     constexpr int NT = NF < 4 ? 8 * (NF + 1) : 32;
     float v[NT];
     const float *base = xp + (size_t)row0 * SP + hrho;
+    // taps 16..31 from a second base 16 taps on: read in pairs, two taps
+    // apart by 15 x 256 bytes, the offsets from one base stop at 64 KB.  The
+    // empty asm keeps the compiler from folding the two bases back into one.
+    int off1 = row0 * SP + hrho + 16 * S * SP;
+    asm volatile("" : "+v"(off1));
 #pragma unroll
-    for (int m = 0; m < 8 * NF && m < NT; ++m) v[m] = base[(size_t)m * S * SP];
-#pragma unroll
-    for (int m = 8 * NF; m < NT; ++m) v[m] = xp[(size_t)min(row0 + S * m, G) * SP + hrho];
+    for (int m = 0; m < NT; ++m) v[m] = m < 16 ? base[(size_t)m * S * SP] : xp[off1 + (m - 16) * S * SP];
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NT; ++m) acc[m & 3] = fmaf(hreg[m], v[m], acc[m & 3]);
@@ -452,7 +457,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
     const int M = p.M, BD = p.B * p.D, R = CH * M;
     float2 *h01 = (float2 *)sm;                            // [R]
     float *xp = sm + 2 * R;                                // [G][SP], slot s at row G-1-s
-    float *xz = xp + (size_t)G * SP;                       // [kChunkZeroRows][SP] zeros: row G
+    float *xz = xp + (size_t)G * SP;                       // [kChunkZeroRows][SP] zeros: rows G..
     float *xs = xz + kChunkZeroRows * SP;                  // [G][CH] teacher-forced inputs
     const int c0 = blockIdx.x * CH;
     const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
@@ -543,7 +548,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
         // its tap-1 term: fft + sum_{k>=2} h[k] x_{i+1-k}.  Tap m of a lane
         // (k = seg + 8m) reads slot i+1-k at row row0 + 8m.  Taps come in four
         // groups of eight m; the first nf = (i+2)/64 groups exist in every
-        // lane, the next one in some (its other lanes read the zero row past
+        // lane, the next one in some (its other lanes read the zero rows past
         // the chunk's first slot), the rest in none.  nf is uniform and picks
         // a branch-free body, so all of a position's reads are in flight.
         for (int i = 0; i < G; ++i) {
@@ -558,11 +563,11 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
                 const int row0 = G - 2 - i + seg;
                 float acc;
                 switch ((i + 2) >> 6) {
-                    case 0: acc = helper_sum<0>(xp, hreg, row0, hrho, G); break;
-                    case 1: acc = helper_sum<1>(xp, hreg, row0, hrho, G); break;
-                    case 2: acc = helper_sum<2>(xp, hreg, row0, hrho, G); break;
-                    case 3: acc = helper_sum<3>(xp, hreg, row0, hrho, G); break;
-                    default: acc = helper_sum<4>(xp, hreg, row0, hrho, G); break;
+                    case 0: acc = helper_sum<0>(xp, hreg, row0, hrho); break;
+                    case 1: acc = helper_sum<1>(xp, hreg, row0, hrho); break;
+                    case 2: acc = helper_sum<2>(xp, hreg, row0, hrho); break;
+                    case 3: acc = helper_sum<3>(xp, hreg, row0, hrho); break;
+                    default: acc = helper_sum<4>(xp, hreg, row0, hrho); break;
                 }
                 acc = sum8(acc);
                 if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
