@@ -247,6 +247,26 @@ def test_edge_lengths_and_ragged_chain_counts(L):
                 ctx.step(_cuda(x[0]))
 
 
+@pytest.mark.parametrize("scale", [0.02, 1.0])
+def test_chunk_kernel_with_and_without_records_agree(scale):
+    """The chunk kernel the bench runs (no records) against the one the oracle replays check (records
+    on): the same arithmetic, so the outputs agree bit for bit.  scale 0.02 keeps every |y| below 0.8
+    (the chains' polynomial pass holds); scale 1.0 leaves that range (the full-tanh reruns)."""
+    M, B, D, L = 3, 2, 37, 2048
+    say(f"case chunk kernel records on/off scale={scale} M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 31, decay=200.0) * scale
+    x1 = np.random.default_rng(32).standard_normal((B, D)).astype(np.float32)
+    outs = []
+    for rec in (False, True):
+        with fi.Context(_cuda(h), B, record=rec) as ctx:
+            ctx.set_input(_cuda(x1))
+            outs.append(ctx.generate(L).cpu().numpy())
+    big = float(np.abs(outs[0]).max())
+    say(f"  max |y| {big:.3g}")
+    assert (big < 0.8) == (scale < 0.5)
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_schedule_and_stamps():
     M, B, D, L = 1, 1, 4, 64
     say(f"case schedule/stamps L={L}")
