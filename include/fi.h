@@ -305,6 +305,66 @@ fi_status fi_time_block(fi_ctx *ctx, int q, int path, int reps, double *us);
  * (fi_reset) before any further stepping (FI_ESTATE otherwise). */
 fi_status fi_lazy_time(fi_ctx *ctx, int64_t n, int reps, double *us);
 
+/* ------------------------------------------------------------------------
+ * Data-dependent filters.  Flash Inference, summary page, "Datenabhaengige
+ * Filter-Erweiterung (Appendix B)": with a filter that depends on the data, a
+ * modified tiling (Algorithm 5) keeps the method exact at twice the work; the
+ * rebuttal page adds that each block then takes two same-size transforms
+ * instead of one.  The pages give nothing more.  Reading used here: both
+ * sequences arrive online, per batch row b and channel c the input x_t and the
+ * filter tap h_t at position t (0-based, t = 0 .. L-1), and
+ *
+ *     y_t[b,c] = sum_{i+j=t} x_i[b,c] * h_j[b,c]
+ *
+ * (one layer; taps per (b, c), since a data-dependent filter differs per
+ * sequence).  Tiling, p a power of two: red cell y_t = pend_t + x_t h_0 +
+ * x_0 h_t; at t = 2p-1 the square x[p, 2p) * h[p, 2p); at t = (m+1)p-1,
+ * m >= 2, the two band products x[t+1-p, t] * h[p, 2p) and h[t+1-p, t] *
+ * x[p, 2p).  Each adds into the pending sums of positions t+1 .. t+2p-1.
+ * Products of p >= 2^fft_min_log2 run as 2p-point FFTs against the cached
+ * spectrum of the fixed block, smaller ones directly.
+ *
+ * One context per stream; calls are stream-ordered on the bound stream and
+ * not thread-safe.  All pointers are caller-owned device memory, fp32,
+ * [B][D] per position (row r = b*D + c), densely packed.
+ * ------------------------------------------------------------------------ */
+typedef struct fi_dd fi_dd; /* opaque, owned by the library */
+
+/* Device bytes the workspace of a data-dependent context needs: three
+ * [B*D][L] fp32 arrays (inputs, taps, pending sums) plus the fixed-block
+ * spectra (16 L bytes per row) and twiddles.  0 if the shape is unsupported:
+ * B, D >= 1, B*D <= 2^24, L a power of two up to 32768 (the widest product,
+ * L/2 points, must fit one workgroup's transform); fft_min_log2 in [2, 15], or
+ * -1 for the default 5. */
+size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log2);
+
+/* Create a context at position 0 over the caller's workspace (device, at
+ * least fi_dd_workspace_bytes, 256-byte aligned; the context keeps using it
+ * until fi_dd_destroy).  Synchronises the stream.  FI_EINVAL for a null
+ * pointer or an unsupported shape, FI_EDEVICE if a HIP call fails. */
+fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
+                     hipStream_t stream);
+
+/* One position: x_t and h_t ([B][D], device) arrive, y_t ([B][D], device) is
+ * written.  FI_ERANGE after L positions, FI_EINVAL for null pointers,
+ * FI_ESTATE after a device failure. */
+fi_status fi_dd_step(fi_dd *ctx, const float *x_t, const float *h_t, float *y_t);
+
+/* `steps` positions in a row: x, h, y are [steps][B][D] (device). */
+fi_status fi_dd_run(fi_dd *ctx, const float *x, const float *h, int64_t steps, float *y);
+
+/* Back to position 0 (inputs, taps and pending sums cleared). */
+fi_status fi_dd_reset(fi_dd *ctx);
+
+/* Positions produced so far (-1 for a null context). */
+int64_t fi_dd_position(const fi_dd *ctx);
+
+/* Message of the last failed call. */
+const char *fi_dd_last_error(const fi_dd *ctx);
+
+/* Synchronise the stream and free the context (not the workspace). */
+fi_status fi_dd_destroy(fi_dd *ctx);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@
 #include "fi_block.h"
 #include "fi_kernels.h"
 #include "fi_fft_kernels.h"
+#include "fi_dd_kernels.h"
 
 using namespace fi;
 
@@ -72,6 +73,32 @@ int sub_k(int q, int vlog) { return 1 << (q - vlog); }
 // float4 entries of class q's spectra per (l, c) row
 size_t spec_row_f4(int q, int vlog) {
     return is_sub(q, vlog) ? (size_t)(2 * sub_k(q, vlog) - 1) * ((size_t(1) << vlog) / 2) : (size_t(1) << q) / 2;
+}
+
+// Twiddle tables, fp64 on the host (2 NT float2, NT = 2^logNT): W_NT^k, then
+// for every transform size N = 2^logn the pair twiddle W_{2N}^j of each
+// real-spectrum item, then the odd-half pair twiddles W_{4N}^k.
+std::vector<float2> twiddle_tables(int logNT) {
+    const size_t nt = size_t(1) << logNT;
+    std::vector<float2> tw(2 * nt, make_float2(1.f, 0.f));
+    const double pi = 3.14159265358979323846;
+    for (size_t k = 0; k < nt; ++k) {
+        const double a = -2.0 * pi * (double)k / (double)nt;
+        tw[k] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+    for (int logn = 2; logn < logNT; ++logn) {
+        const int N = 1 << logn;
+        for (int e = 1; e < N / 2; ++e) {
+            const double a = -pi * (double)pair_slot(logn, e).j / (double)N;
+            tw[nt + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+        // odd halves of 2N-point transforms: W_{4N}^k
+        for (int e = 0; e < N / 2; ++e) {
+            const double a = -pi * (double)odd_slot(logn, e).j / (double)(2 * N);
+            tw[nt + nt / 2 + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+    }
+    return tw;
 }
 
 bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &lay) {
@@ -979,28 +1006,8 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
                        o.filters_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
                        c->stream) != hipSuccess)
         return bail(fail(c, FI_EDEVICE, "filter copy failed"));
-    // twiddle tables, fp64 on the host: W_NT^k, then for every transform size
-    // N = 2^logn the pair twiddle W_{2N}^j of each real-spectrum item
     {
-        const size_t nt = size_t(1) << lay.logNT;
-        std::vector<float2> tw(2 * nt, make_float2(1.f, 0.f));
-        const double pi = 3.14159265358979323846;
-        for (size_t k = 0; k < nt; ++k) {
-            const double a = -2.0 * pi * (double)k / (double)nt;
-            tw[k] = make_float2((float)std::cos(a), (float)std::sin(a));
-        }
-        for (int logn = 2; logn < lay.logNT; ++logn) {
-            const int N = 1 << logn;
-            for (int e = 1; e < N / 2; ++e) {
-                const double a = -pi * (double)pair_slot(logn, e).j / (double)N;
-                tw[nt + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
-            }
-            // odd halves of 2N-point transforms: W_{4N}^k
-            for (int e = 0; e < N / 2; ++e) {
-                const double a = -pi * (double)odd_slot(logn, e).j / (double)(2 * N);
-                tw[nt + nt / 2 + N / 2 + e] = make_float2((float)std::cos(a), (float)std::sin(a));
-            }
-        }
+        const std::vector<float2> tw = twiddle_tables(lay.logNT);
         if (hipMemcpyAsync((void *)d.twid, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice,
                            c->stream) != hipSuccess ||
             hipStreamSynchronize(c->stream) != hipSuccess)
@@ -1569,6 +1576,210 @@ fi_status fi_lazy_generate(fi_ctx *c, int64_t steps, float *y) {
                                 hipMemcpyDeviceToDevice, c->stream));
     }
     return FI_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Data-dependent filters: the taps arrive with the data (fi_dd_*).
+// ---------------------------------------------------------------------------
+struct fi_dd {
+    int B = 0, D = 0, R = 0, kmin = 0, kmax = -1;
+    int64_t L = 0, pos = 0;
+    hipStream_t stream = nullptr;
+    char *ws = nullptr;
+    fi::Dev dev{};
+    fi::DDev q{};
+    float4 *spx[kMaxP] = {}, *sph[kMaxP] = {};
+    bool poisoned = false;
+    std::string err;
+};
+
+namespace {
+
+constexpr int kDDMaxLog = 15;      // L <= 2^15: the widest product (L/2) is one workgroup's transform
+constexpr int kDDFftMinDefault = 5;
+
+struct DDLayout {
+    size_t xh = 0, hh = 0, acc = 0, twid = 0, total = 0;
+    size_t spx[kMaxP] = {0}, sph[kMaxP] = {0};
+    int kmin = 0, kmax = -1, logNT = 2;
+};
+
+bool dd_layout(int B, int D, int64_t L, int fft_min, DDLayout &ly) {
+    if (B < 1 || D < 1 || L < 1 || L > (int64_t(1) << kDDMaxLog) || (L & (L - 1)) != 0 ||
+        (int64_t)B * D > (int64_t(1) << 24))
+        return false;
+    if (fft_min < 2 || fft_min > kDDMaxLog) return false;
+    const size_t R = (size_t)B * D;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    ly.xh = take(R * L * sizeof(float));
+    ly.hh = take(R * L * sizeof(float));
+    ly.acc = take(R * L * sizeof(float));
+    ly.kmin = fft_min;
+    ly.kmax = -1;
+    for (int k = fft_min; (int64_t(2) << k) <= L; ++k) ly.kmax = k;   // products of p = 2^k: 2p <= L
+    for (int k = ly.kmin; k <= ly.kmax; ++k) {
+        ly.spx[k] = take(R * (size_t(1) << (k - 1)) * sizeof(float4));
+        ly.sph[k] = take(R * (size_t(1) << (k - 1)) * sizeof(float4));
+    }
+    ly.logNT = std::max(2, ly.kmax + 1);
+    ly.twid = take((size_t(2) << ly.logNT) * sizeof(float2));
+    ly.total = off;
+    return true;
+}
+
+fi_status dd_fail(fi_dd *c, fi_status s, const std::string &msg) {
+    c->err = msg;
+    if (s == FI_EDEVICE) c->poisoned = true;
+    return s;
+}
+
+#define DDCK(ctx, call)                                                                      \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return dd_fail((ctx), FI_EDEVICE, std::string(#call) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+template <int K>
+void dd_launch_k(fi_dd *c, int64_t n) {
+    using S = fi::FftShape<K>;
+    const unsigned grid = (unsigned)((c->R + S::PER_BLOCK - 1) / S::PER_BLOCK);
+    if (n + 1 == (int64_t(2) << K))   // the fixed blocks x[p, 2p), h[p, 2p) are complete: their spectra
+        hipLaunchKernelGGL((fi::k_dd_band<K>), dim3(grid, 2), dim3(S::TPB), 0, c->stream, c->dev, c->q, c->spx[K],
+                           c->sph[K]);
+    hipLaunchKernelGGL((fi::k_dd_fft<K>), dim3(grid), dim3(S::TPB), 0, c->stream, c->dev, c->q, c->spx[K], c->sph[K],
+                       (long long)n);
+}
+
+void dd_launch(fi_dd *c, int k, int64_t n) {
+    switch (k) {
+        case 2: return dd_launch_k<2>(c, n);
+        case 3: return dd_launch_k<3>(c, n);
+        case 4: return dd_launch_k<4>(c, n);
+        case 5: return dd_launch_k<5>(c, n);
+        case 6: return dd_launch_k<6>(c, n);
+        case 7: return dd_launch_k<7>(c, n);
+        case 8: return dd_launch_k<8>(c, n);
+        case 9: return dd_launch_k<9>(c, n);
+        case 10: return dd_launch_k<10>(c, n);
+        case 11: return dd_launch_k<11>(c, n);
+        case 12: return dd_launch_k<12>(c, n);
+        case 13: return dd_launch_k<13>(c, n);
+        case 14: return dd_launch_k<14>(c, n);
+        default: return;
+    }
+}
+
+fi_status dd_step(fi_dd *c, const float *x, const float *h, float *y) {
+    const int64_t n = c->pos;
+    hipLaunchKernelGGL(fi::k_dd_step, dim3((unsigned)((c->R + 255) / 256)), dim3(256), 0, c->stream, c->q,
+                       (long long)n, x, h, y);
+    for (int k = c->kmin; k <= c->kmax && (int64_t(2) << k) <= n + 1 && (n + 1) % (int64_t(1) << k) == 0; ++k)
+        dd_launch(c, k, n);
+    DDCK(c, hipGetLastError());
+    ++c->pos;
+    return FI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log2) {
+    DDLayout ly;
+    return dd_layout(batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly) ? ly.total : 0;
+}
+
+fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
+                     hipStream_t stream) {
+    if (!out || !workspace) return FI_EINVAL;
+    *out = nullptr;
+    DDLayout ly;
+    if (!dd_layout(batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly)) return FI_EINVAL;
+    fi_dd *c = new fi_dd();
+    c->B = batch;
+    c->D = channels;
+    c->R = batch * channels;
+    c->L = L;
+    c->stream = stream;
+    c->ws = (char *)workspace;
+    c->kmin = ly.kmin;
+    c->kmax = ly.kmax;
+    c->q.xh = (float *)(c->ws + ly.xh);
+    c->q.hh = (float *)(c->ws + ly.hh);
+    c->q.acc = (float *)(c->ws + ly.acc);
+    c->q.L = L;
+    c->q.R = c->R;
+    c->q.pd = 1 << ly.kmin;
+    for (int k = ly.kmin; k <= ly.kmax; ++k) {
+        c->spx[k] = (float4 *)(c->ws + ly.spx[k]);
+        c->sph[k] = (float4 *)(c->ws + ly.sph[k]);
+    }
+    c->dev.twid = (const float2 *)(c->ws + ly.twid);
+    c->dev.ptw = c->dev.twid + (size_t(1) << ly.logNT);
+    c->dev.optw = c->dev.ptw + (size_t(1) << (ly.logNT - 1));
+    c->dev.logNT = ly.logNT;
+    const std::vector<float2> tw = twiddle_tables(ly.logNT);
+    fi_status s = FI_OK;
+    if (hipMemcpyAsync((void *)c->dev.twid, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice, stream) !=
+            hipSuccess ||
+        hipMemsetAsync(c->ws + ly.xh, 0, ly.twid - ly.xh, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        s = FI_EDEVICE;
+    if (s != FI_OK) {
+        delete c;
+        return s;
+    }
+    *out = c;
+    return FI_OK;
+}
+
+fi_status fi_dd_step(fi_dd *c, const float *x_t, const float *h_t, float *y_t) {
+    if (!c || !x_t || !h_t || !y_t) return FI_EINVAL;
+    if (c->poisoned) return FI_ESTATE;
+    if (c->pos >= c->L) return dd_fail(c, FI_ERANGE, "stepped past L");
+    return dd_step(c, x_t, h_t, y_t);
+}
+
+fi_status fi_dd_run(fi_dd *c, const float *x, const float *h, int64_t steps, float *y) {
+    if (!c || steps < 0 || (steps > 0 && (!x || !h || !y))) return FI_EINVAL;
+    if (c->poisoned) return FI_ESTATE;
+    if (c->pos + steps > c->L) return dd_fail(c, FI_ERANGE, "run past L");
+    const size_t R = (size_t)c->R;
+    for (int64_t i = 0; i < steps; ++i) {
+        const fi_status s = dd_step(c, x + i * R, h + i * R, y + i * R);
+        if (s != FI_OK) return s;
+    }
+    return FI_OK;
+}
+
+fi_status fi_dd_reset(fi_dd *c) {
+    if (!c) return FI_EINVAL;
+    if (c->poisoned) return FI_ESTATE;
+    const size_t bytes = (size_t)c->R * c->L * sizeof(float);
+    DDCK(c, hipMemsetAsync(c->q.xh, 0, bytes, c->stream));
+    DDCK(c, hipMemsetAsync(c->q.hh, 0, bytes, c->stream));
+    DDCK(c, hipMemsetAsync(c->q.acc, 0, bytes, c->stream));
+    c->pos = 0;
+    return FI_OK;
+}
+
+int64_t fi_dd_position(const fi_dd *c) { return c ? c->pos : -1; }
+
+const char *fi_dd_last_error(const fi_dd *c) { return c ? c->err.c_str() : "null context"; }
+
+fi_status fi_dd_destroy(fi_dd *c) {
+    if (!c) return FI_EINVAL;
+    const hipError_t e = hipStreamSynchronize(c->stream);
+    delete c;
+    return e == hipSuccess ? FI_OK : FI_EDEVICE;
 }
 
 }  // extern "C"

@@ -87,6 +87,14 @@ def load_library():
         "fi_set_block_weights": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
+        "fi_dd_workspace_bytes": (S, [I, I, I64, I]),
+        "fi_dd_init": (I, [ctypes.POINTER(P), I, I, I64, I, P, P]),
+        "fi_dd_step": (I, [P, P, P, P]),
+        "fi_dd_run": (I, [P, P, P, I64, P]),
+        "fi_dd_reset": (I, [P]),
+        "fi_dd_position": (I64, [P]),
+        "fi_dd_last_error": (ctypes.c_char_p, [P]),
+        "fi_dd_destroy": (I, [P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -317,6 +325,75 @@ class Context:
     def close(self):
         if getattr(self, "_h", None):
             self._lib.fi_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+
+class DDContext:
+    """Data-dependent filters: per position both the input x_t and the filter tap h_t arrive
+    ([B][D] each, one layer, taps per (b, c)) and y_t = sum_{i+j=t} x_i h_j is produced.
+    Wraps the fi_dd_* calls (see include/fi.h); no CPU path."""
+
+    def __init__(self, batch, channels, L, *, fft_min_log2=-1, device=None):
+        import torch
+        if not torch.cuda.is_available():
+            raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
+        lib = load_library()
+        self._torch = torch
+        self.device = torch.device(device or "cuda")
+        self.B, self.D, self.L = int(batch), int(channels), int(L)
+        nbytes = lib.fi_dd_workspace_bytes(self.B, self.D, self.L, int(fft_min_log2))
+        if nbytes == 0:
+            raise FiError(FI_EINVAL, f"unsupported shape B={batch} D={channels} L={L}")
+        self.workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        st = lib.fi_dd_init(ctypes.byref(h), self.B, self.D, self.L, int(fft_min_log2),
+                            ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_void_p(self.stream.cuda_stream))
+        if st != FI_OK:
+            raise FiError(st, "fi_dd_init failed")
+        self._h = h
+        self._lib = lib
+
+    def _check(self, st):
+        if st != FI_OK:
+            msg = self._lib.fi_dd_last_error(self._h)
+            raise FiError(st, msg.decode() if msg else "")
+
+    @property
+    def position(self) -> int:
+        return int(self._lib.fi_dd_position(self._h))
+
+    def step(self, x, h, y=None):
+        """One position: x, h [B][D] device tensors; returns y [B][D]."""
+        y = self._torch.empty((self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
+        self._check(self._lib.fi_dd_step(self._h, _dptr(x), _dptr(h), _dptr(y)))
+        return y
+
+    def run(self, x, h, y=None):
+        """len(x) positions: x, h [T][B][D] device tensors; returns y [T][B][D]."""
+        T = int(x.shape[0])
+        y = self._torch.empty((T, self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
+        self._check(self._lib.fi_dd_run(self._h, _dptr(x), _dptr(h), T, _dptr(y)))
+        return y
+
+    def reset(self):
+        self._check(self._lib.fi_dd_reset(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.fi_dd_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -1,0 +1,102 @@
+"""Data-dependent filters (fi_dd_*): parity with the definition y_t = sum_{i+j=t} x_i h_j.
+
+Flash Inference (arXiv 2410.12982), summary page, "Datenabhaengige Filter-Erweiterung
+(Appendix B)": the taps depend on the data, so they arrive online with the inputs; the oracle
+is the plain causal convolution of the realised sequences (oracle.conv_rows, fp64), and the
+tolerance is the teacher-forced bar 1e-4 * ||h||_1 * max|x| per row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_convolution_sequence_amd import fi
+from tests._parity import TF_TOL, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows_worst(x, h, y):
+    """x, h, y: [T][B][D]; worst error / tolerance over all rows against the oracle."""
+    T = x.shape[0]
+    xr = np.ascontiguousarray(x.reshape(T, -1).T)
+    hr = np.ascontiguousarray(h.reshape(T, -1).T)
+    ref = oracle.conv_rows(hr, xr)
+    got = y.reshape(T, -1).T
+    worst = 0.0
+    for r in range(xr.shape[0]):
+        tol = TF_TOL * np.abs(hr[r].astype(np.float64)).sum() * np.abs(xr[r]).max()
+        worst = max(worst, np.abs(got[r] - ref[r]).max() / tol)
+    return worst
+
+
+def _seq(T, B, D, seed, decay):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, B, D)).astype(np.float32)
+    h = (rng.standard_normal((T, B, D)) * np.exp(-np.arange(T) / decay)[:, None, None]).astype(np.float32)
+    return x, h
+
+
+@pytest.mark.parametrize("fft_min", [2, 3, 5, 15])
+def test_dd_matches_definition(fft_min):
+    B, D, L = 2, 5, 1024
+    say(f"case data-dependent B={B} D={D} L={L} fft_min_log2={fft_min}")
+    x, h = _seq(L, B, D, 41, 300.0)
+    with fi.DDContext(B, D, L, fft_min_log2=fft_min) as ctx:
+        y = ctx.run(torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()).cpu().numpy()
+        assert ctx.position == L
+        with pytest.raises(fi.FiError):
+            ctx.step(torch.from_numpy(x[0]).cuda(), torch.from_numpy(h[0]).cuda())
+    worst = _rows_worst(x, h, y)
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+
+
+def test_dd_steps_equal_run_and_reset_repeats():
+    B, D, L = 1, 7, 256
+    say(f"case data-dependent steps/run/reset B={B} D={D} L={L}")
+    x, h = _seq(L, B, D, 42, 100.0)
+    xd, hd = torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()
+    with fi.DDContext(B, D, L, fft_min_log2=3) as ctx:
+        ys = torch.stack([ctx.step(xd[t], hd[t]) for t in range(L)]).cpu().numpy()
+        ctx.reset()
+        assert ctx.position == 0
+        yr = ctx.run(xd, hd).cpu().numpy()
+    assert np.array_equal(ys, yr)
+
+
+def test_dd_taps_made_from_the_outputs():
+    """Both sequences depend on the outputs so far (x_{t+1} = tanh(y_t) + noise,
+    h_{t+1} = 0.3 tanh(y_t) e^{-t/150}), so each arrives only after the previous position: the
+    realised sequences, recorded, are checked against the definition."""
+    B, D, L = 2, 3, 512
+    say(f"case data-dependent taps from outputs B={B} D={D} L={L}")
+    rng = np.random.default_rng(43)
+    noise = torch.from_numpy(rng.standard_normal((L, B, D)).astype(np.float32) * 0.1).cuda()
+    xs = torch.empty((L, B, D), device="cuda")
+    hs = torch.empty((L, B, D), device="cuda")
+    ys = torch.empty((L, B, D), device="cuda")
+    xs[0] = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).cuda()
+    hs[0] = 1.0
+    with fi.DDContext(B, D, L, fft_min_log2=4) as ctx:
+        for t in range(L):
+            ctx.step(xs[t], hs[t], ys[t])
+            if t + 1 < L:
+                xs[t + 1] = torch.tanh(ys[t]) + noise[t]
+                hs[t + 1] = 0.3 * torch.tanh(ys[t]) * float(np.exp(-t / 150.0))
+    worst = _rows_worst(xs.cpu().numpy(), hs.cpu().numpy(), ys.cpu().numpy())
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+
+
+def test_dd_widest_products_sampled_rows():
+    """L = 2^15, the widest products (p = 2^14) one workgroup's transform; 6 of 256 rows checked."""
+    B, D, L = 1, 256, 32768
+    say(f"case data-dependent full width B={B} D={D} L={L}")
+    x, h = _seq(L, B, D, 44, 4096.0)
+    with fi.DDContext(B, D, L) as ctx:
+        y = ctx.run(torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()).cpu().numpy()
+    rows = [0, 17, 100, 128, 201, 255]
+    worst = _rows_worst(x[:, :, rows], h[:, :, rows], y[:, :, rows])
+    say(f"  worst error/tolerance over {len(rows)} rows {worst:.3e}")
+    assert worst <= 1.0

@@ -251,6 +251,46 @@ def test_schedule_counts_match_proposition_1(P):
     assert area == L * (L - 1) // 2
 
 
+@pytest.mark.parametrize("L", [1, 2, 16, 100, 512])
+def test_data_dependent_tiling_covers_every_pair_once_in_time(L):
+    """Two-sided tiling for filters that arrive with the data: every pair (i, j) with i + j < L
+    exactly once, each formed at a step n with both inputs known (max(i, j) <= n) and, for a
+    block, its target still ahead (i + j > n); red cells at their own target."""
+    cover = np.zeros((L, L), np.int32)
+    for n in range(L):
+        for i, j in schedule.dd_red_pairs(n):
+            assert max(i, j) == n == i + j
+            cover[i, j] += 1
+        for kind, p, xl, hl in schedule.dd_blocks(n):
+            assert xl + p - 1 <= n and hl + p - 1 <= n and xl + hl > n
+            assert xl + hl + 2 * p - 2 >= xl + hl
+            hi_i, hi_j = min(xl + p, L), min(hl + p, L)
+            cover[xl:hi_i, hl:hi_j] += 1
+    want = np.fliplr(np.triu(np.ones((L, L), np.int32)))      # i + j <= L - 1
+    want_mask = np.add.outer(np.arange(L), np.arange(L)) < L
+    assert np.array_equal(cover[want_mask], np.ones(int(want_mask.sum()), np.int32))
+    assert want.sum() == want_mask.sum()
+
+
+def test_data_dependent_tiling_runs_two_products_per_band_block():
+    """The pages' account of the modification: a step forms two same-size products where the
+    fixed-filter tiling forms one (the squares at 2p - 1 excepted); the products' total area is
+    the number of pairs, L(L+1)/2 minus the red cells, over all steps up to L = 2^10 - 1."""
+    L = 1024
+    area = 0
+    for n in range(L):
+        blocks = list(schedule.dd_blocks(n))
+        sizes = {}
+        for kind, p, xl, hl in blocks:
+            sizes.setdefault(p, []).append(kind)
+            area += p * p
+        for p, kinds in sizes.items():
+            assert sorted(kinds) in (["square"], ["h", "x"])
+            assert (kinds == ["square"]) == (n + 1 == 2 * p)
+    # pairs (i, j), i, j >= 1, with max(i, j) < L: blocks never stop short of L
+    assert area == (L - 1) * (L - 1)
+
+
 def test_schedule_fractions_match_pages():
     facts = json.load(open(os.path.join(GOLDEN, "schedule_facts.json")))
     P = 17
