@@ -229,6 +229,7 @@ def main():
     ap.add_argument("--no-lazy", action="store_true")
     ap.add_argument("--no-defer-leg", action="store_true", help="skip the generation with deferred split blocks")
     ap.add_argument("--no-prefill-leg", action="store_true", help="skip the prefill timing")
+    ap.add_argument("--no-dd-leg", action="store_true", help="skip the data-dependent-filter timing")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
     ap.add_argument("--traffic-run", action="store_true",
                     help="launch each FFT class once and a calibration copy (run under rocprofv3 --pmc)")
@@ -438,6 +439,52 @@ def main():
                            "two warm runs, HIP events on the stream")
         log(f"bench: prefill P={P}: eager {prefill['eager_ms']} ms, steps {prefill['steps_ms']} ms")
 
+    dd = None
+    if not args.no_dd_leg:
+        # data-dependent filters (taps arriving with the data), one layer of the workload's
+        # channels over L_dd positions, against the fixed-filter path with one launch per
+        # position at the same shape (both one position at a time, no chunks)
+        Ld = min(16384, w.L)
+        rng = np.random.default_rng(9)
+        xd = torch.from_numpy(rng.standard_normal((Ld, w.B, w.D)).astype(np.float32)).cuda()
+        hd = torch.from_numpy((rng.standard_normal((Ld, w.B, w.D)) *
+                               np.exp(-np.arange(Ld) / 2048.0)[:, None, None]).astype(np.float32)).cuda()
+        yd = torch.empty_like(xd)
+        ddc = fi.DDContext(w.B, w.D, Ld)
+        ms = []
+        for _ in range(2):
+            ddc.reset()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ddc.run(xd, hd, yd)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ddc.close()
+        del ddc
+        hf = torch.from_numpy(np.ascontiguousarray(h[:1, :, :Ld])).cuda()
+        fx = fi.Context(hf, w.B, chunk_direct=False)
+        fx.set_input(xd[0])
+        fx.generate(Ld, want_y=False)      # warm
+        fx.reset()
+        fx.set_input(xd[0])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fx.generate(Ld, want_y=False)
+        b.record()
+        torch.cuda.synchronize()
+        fixed_ms = a.elapsed_time(b)
+        fx.close()
+        del fx
+        dd = {"L": Ld, "B": w.B, "D": w.D, "ms": round(ms[-1], 3),
+              "tokens_per_s": round(Ld / (ms[-1] * 1e-3), 1),
+              "fixed_filter_per_position_tokens_per_s": round(Ld / (fixed_ms * 1e-3), 1),
+              "note": ("fi_dd_run over L positions of one layer (x and taps h seeded, given per position), "
+                       "warm, HIP events; beside it the fixed-filter path at the same shape with one launch "
+                       "per position (chunks off), one warm generation")}
+        log(f"bench: data-dependent filters L={Ld}: {dd['tokens_per_s']:,.0f} tokens/s; fixed filters per "
+            f"position {dd['fixed_filter_per_position_tokens_per_s']:,.0f}")
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, h)
 
     out = {
@@ -465,6 +512,7 @@ def main():
         "lazy_gpu": lazy,
         "ablations": ablations,
         "prefill": prefill,
+        "data_dependent": dd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

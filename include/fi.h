@@ -335,7 +335,8 @@ typedef struct fi_dd fi_dd; /* opaque, owned by the library */
  * spectra (16 L bytes per row) and twiddles.  0 if the shape is unsupported:
  * B, D >= 1, B*D <= 2^24, L a power of two up to 32768 (the widest product,
  * L/2 points, must fit one workgroup's transform); fft_min_log2 in [2, 15], or
- * -1 for the default 5. */
+ * -1 for the default 2 (products from p = 4 on as FFTs: the direct products
+ * run one thread per row and only pay off for p <= 2). */
 size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log2);
 
 /* Create a context at position 0 over the caller's workspace (device, at

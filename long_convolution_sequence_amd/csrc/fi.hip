@@ -1598,7 +1598,7 @@ struct fi_dd {
 namespace {
 
 constexpr int kDDMaxLog = 15;      // L <= 2^15: the widest product (L/2) is one workgroup's transform
-constexpr int kDDFftMinDefault = 5;
+constexpr int kDDFftMinDefault = 2;
 
 struct DDLayout {
     size_t xh = 0, hh = 0, acc = 0, twid = 0, total = 0;
