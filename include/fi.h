@@ -363,7 +363,8 @@ int64_t fi_dd_position(const fi_dd *ctx);
 /* Message of the last failed call. */
 const char *fi_dd_last_error(const fi_dd *ctx);
 
-/* Synchronise the stream and free the context (not the workspace). */
+/* Synchronise the stream and free the context (not the workspace); FI_OK
+ * for a null context, FI_EDEVICE if the synchronisation fails. */
 fi_status fi_dd_destroy(fi_dd *ctx);
 
 #ifdef __cplusplus

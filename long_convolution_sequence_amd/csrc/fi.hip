@@ -1776,7 +1776,7 @@ int64_t fi_dd_position(const fi_dd *c) { return c ? c->pos : -1; }
 const char *fi_dd_last_error(const fi_dd *c) { return c ? c->err.c_str() : "null context"; }
 
 fi_status fi_dd_destroy(fi_dd *c) {
-    if (!c) return FI_EINVAL;
+    if (!c) return FI_OK;
     const hipError_t e = hipStreamSynchronize(c->stream);
     delete c;
     return e == hipSuccess ? FI_OK : FI_EDEVICE;

@@ -93,3 +93,52 @@ def test_null_context_calls_are_rejected(lib):
     assert lib.fi_destroy(None) == fi.FI_OK
     assert lib.fi_debug_schedule(None, 1, None, None) == fi.FI_EINVAL
     assert lib.fi_set_defer_wide(None, 1) == fi.FI_EINVAL
+
+
+def _dd_expected_bytes(B, D, L, kmin):
+    """Workspace of a data-dependent context as the header states it: three
+    [B*D][L] fp32 arrays, the two fixed-block spectra (8p bytes per row each) of
+    every FFT product size p = 2^k with k >= kmin and 2p <= L, and the twiddles
+    of the widest transform; every part 256-byte aligned."""
+    al = lambda v: (v + 255) // 256 * 256
+    R = B * D
+    total = 3 * al(R * L * 4)
+    k, kmax = kmin, -1
+    while (2 << k) <= L:
+        total += 2 * al(R * 8 * (1 << k))
+        kmax = k
+        k += 1
+    total += al((2 << max(2, kmax + 1)) * 8)
+    return total
+
+
+@pytest.mark.parametrize("B,D,L,kmin", [(1, 1, 1, 2), (1, 4, 2, 2), (2, 5, 1024, 3), (1, 864, 16384, 2),
+                                        (3, 7, 32768, 15), (1, 256, 32768, 5)])
+def test_dd_workspace_bytes(lib, B, D, L, kmin):
+    assert lib.fi_dd_workspace_bytes(B, D, L, kmin) == _dd_expected_bytes(B, D, L, kmin)
+
+
+def test_dd_workspace_default_threshold_is_two(lib):
+    assert lib.fi_dd_workspace_bytes(2, 3, 4096, -1) == lib.fi_dd_workspace_bytes(2, 3, 4096, 2)
+
+
+@pytest.mark.parametrize("B,D,L,kmin", [(0, 4, 64, 2), (1, 0, 64, 2), (1, 4, 0, 2), (1, 4, 48, 2),
+                                        (1, 4, 65536, 2), (1, 4, 64, 1), (1, 4, 64, 16),
+                                        (1 << 12, 1 << 12 | 1, 64, 2)])
+def test_dd_workspace_bytes_rejects_bad_shapes(lib, B, D, L, kmin):
+    assert lib.fi_dd_workspace_bytes(B, D, L, kmin) == 0
+
+
+def test_dd_calls_reject_bad_arguments_without_a_device(lib):
+    h = ctypes.c_void_p()
+    ws = ctypes.c_void_p(0x10000)
+    assert lib.fi_dd_init(None, 1, 4, 64, -1, ws, None) == fi.FI_EINVAL
+    assert lib.fi_dd_init(ctypes.byref(h), 1, 4, 64, -1, None, None) == fi.FI_EINVAL
+    assert lib.fi_dd_init(ctypes.byref(h), 1, 4, 48, -1, ws, None) == fi.FI_EINVAL
+    assert not h.value
+    assert lib.fi_dd_step(None, None, None, None) == fi.FI_EINVAL
+    assert lib.fi_dd_run(None, None, None, 1, None) == fi.FI_EINVAL
+    assert lib.fi_dd_reset(None) == fi.FI_EINVAL
+    assert lib.fi_dd_position(None) == -1
+    assert lib.fi_dd_last_error(None) == b"null context"
+    assert lib.fi_dd_destroy(None) == fi.FI_OK

@@ -100,3 +100,29 @@ def test_dd_widest_products_sampled_rows():
     worst = _rows_worst(x[:, :, rows], h[:, :, rows], y[:, :, rows])
     say(f"  worst error/tolerance over {len(rows)} rows {worst:.3e}")
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8, 16])
+def test_dd_tiny_lengths(L):
+    """The degenerate lengths: red cells only (L <= 2), one square (L = 4), the
+    first band products (L = 8, 16)."""
+    B, D = 1, 3
+    say(f"case data-dependent tiny B={B} D={D} L={L}")
+    x, h = _seq(L, B, D, 45 + L, 4.0)
+    with fi.DDContext(B, D, L) as ctx:
+        y = ctx.run(torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()).cpu().numpy()
+        assert ctx.position == L
+    assert _rows_worst(x, h, y) <= 1.0
+
+
+def test_dd_many_rows_ragged():
+    """B*D = 1011 rows: several blocks of the per-row kernels and a partly
+    filled last one."""
+    B, D, L = 3, 337, 2048
+    say(f"case data-dependent rows B={B} D={D} L={L}")
+    x, h = _seq(L, B, D, 46, 500.0)
+    with fi.DDContext(B, D, L) as ctx:
+        y = ctx.run(torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()).cpu().numpy()
+    worst = _rows_worst(x, h, y)
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
