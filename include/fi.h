@@ -335,8 +335,9 @@ typedef struct fi_dd fi_dd; /* opaque, owned by the library */
  * spectra (16 L bytes per row) and twiddles.  0 if the shape is unsupported:
  * B, D >= 1, B*D <= 2^24, L a power of two up to 32768 (the widest product,
  * L/2 points, must fit one workgroup's transform); fft_min_log2 in [2, 15], or
- * -1 for the default 2 (products from p = 4 on as FFTs: the direct products
- * run one thread per row and only pay off for p <= 2). */
+ * -1 for the default 7.  Products of p < 2^fft_min_log2 run directly: up to
+ * p = 64 inside the position's first launch (one thread per target), wider
+ * ones one thread per row; the rest as FFTs. */
 size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log2);
 
 /* Create a context at position 0 over the caller's workspace (device, at

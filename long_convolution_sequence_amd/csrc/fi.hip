@@ -1598,7 +1598,7 @@ struct fi_dd {
 namespace {
 
 constexpr int kDDMaxLog = 15;      // L <= 2^15: the widest product (L/2) is one workgroup's transform
-constexpr int kDDFftMinDefault = 2;
+constexpr int kDDFftMinDefault = 7;    // products of p <= 64 run in the per-position launch
 
 struct DDLayout {
     size_t xh = 0, hh = 0, acc = 0, twid = 0, total = 0;
@@ -1677,10 +1677,32 @@ void dd_launch(fi_dd *c, int k, int64_t n) {
     }
 }
 
+template <int PM>
+void dd_near_launch(fi_dd *c, int64_t n, const float *x, const float *h, float *y, bool prod) {
+    constexpr int RPW = 128 / PM;   // rows per 256-thread workgroup
+    hipLaunchKernelGGL(fi::k_dd_near<PM>, dim3((unsigned)((c->R + RPW - 1) / RPW)), dim3(256), 0, c->stream, c->q,
+                       (long long)n, x, h, y, prod);
+}
+
 fi_status dd_step(fi_dd *c, const float *x, const float *h, float *y) {
     const int64_t n = c->pos;
-    hipLaunchKernelGGL(fi::k_dd_step, dim3((unsigned)((c->R + 255) / 256)), dim3(256), 0, c->stream, c->q,
-                       (long long)n, x, h, y);
+    // largest direct product of this position up to the one-launch limit (0: none)
+    int64_t pm = 0;
+    for (int64_t p = 1; p <= fi::kDDNearMax && p < c->q.pd && 2 * p <= n + 1 && (n + 1) % p == 0; p *= 2) pm = p;
+    switch (pm) {
+        case 0: dd_near_launch<1>(c, n, x, h, y, false); break;
+        case 1: dd_near_launch<1>(c, n, x, h, y, true); break;
+        case 2: dd_near_launch<2>(c, n, x, h, y, true); break;
+        case 4: dd_near_launch<4>(c, n, x, h, y, true); break;
+        case 8: dd_near_launch<8>(c, n, x, h, y, true); break;
+        case 16: dd_near_launch<16>(c, n, x, h, y, true); break;
+        case 32: dd_near_launch<32>(c, n, x, h, y, true); break;
+        default: dd_near_launch<fi::kDDNearMax>(c, n, x, h, y, true); break;
+    }
+    const int64_t pw = 2 * fi::kDDNearMax;
+    if (c->q.pd > pw && 2 * pw <= n + 1 && (n + 1) % pw == 0)
+        hipLaunchKernelGGL(fi::k_dd_wide, dim3((unsigned)((c->R + 255) / 256)), dim3(256), 0, c->stream, c->q,
+                           (long long)n);
     for (int k = c->kmin; k <= c->kmax && (int64_t(2) << k) <= n + 1 && (n + 1) % (int64_t(1) << k) == 0; ++k)
         dd_launch(c, k, n);
     DDCK(c, hipGetLastError());

@@ -33,18 +33,78 @@ struct DDev {
     int pd;         // products of blocks p < pd run directly
 };
 
-// Red cells of position n and its direct products (p < pd), one thread per row.
-__global__ void __launch_bounds__(256) k_dd_step(DDev q, long long n, const float *__restrict__ x,
-                                                 const float *__restrict__ h, float *__restrict__ y) {
+// Direct products run in one launch per position up to this block size; wider
+// direct products (only when the FFT threshold is set above it) take the
+// serial per-row loop below.
+constexpr int kDDNearMax = 64;
+
+// Red cells of position n and every direct product of that position with
+// p <= PM.  The products of a position are those of p = 1, 2, 4, .., pm (each
+// condition on p -- below the FFT threshold, 2p <= n + 1, p | n + 1 -- holds
+// for all smaller powers of two once it holds for pm), so the host passes the
+// largest one as PM (prod false: no products, red cells only).  2 PM threads
+// per row, thread j owns target n + 1 + j (j < 2 PM - 1) and sums its terms of
+// every size at once; thread 0 also forms the red cell.  Per row, LDS holds
+// x and h over [0, 2 PM) (the fixed blocks [p, 2p)) and over (n - PM, n] (the
+// newest blocks), with position n taken from the arriving x_n, h_n.
+template <int PM>
+__global__ void __launch_bounds__(256) k_dd_near(DDev q, long long n, const float *__restrict__ x,
+                                                 const float *__restrict__ h, float *__restrict__ y, bool prod) {
+    constexpr int TR = 2 * PM, RPW = 256 / TR;
+    __shared__ float fx[RPW][TR], fh[RPW][TR], nx[RPW][PM], nh[RPW][PM];
+    const int lr = threadIdx.x / TR, j = threadIdx.x % TR;
+    const int r = blockIdx.x * RPW + lr;
+    const bool live = r < q.R;
+    const size_t base = (size_t)(live ? r : 0) * q.L;
+    const float *xr = q.xh + base, *hr = q.hh + base;
+    float xn = 0.f, hn = 0.f;
+    if (live) {
+        xn = x[r];
+        hn = h[r];
+    }
+    if (prod && live) {
+        // every index read here is <= n, since 2 PM <= n + 1
+        fx[lr][j] = j == n ? xn : xr[j];
+        fh[lr][j] = j == n ? hn : hr[j];
+        if (j < PM) {
+            const long long i = n + 1 - PM + j;
+            nx[lr][j] = i == n ? xn : xr[i];
+            nh[lr][j] = i == n ? hn : hr[i];
+        }
+    }
+    if (live && j == 0) {
+        float *ar = q.acc + base;
+        q.xh[base + n] = xn;
+        q.hh[base + n] = hn;
+        y[r] = n == 0 ? xn * hn : fmaf(xr[0], hn, fmaf(xn, hr[0], ar[n]));
+    }
+    if (!prod) return;
+    __syncthreads();
+    if (!live || j >= TR - 1 || n + 1 + j >= q.L) return;
+    float s = 0.f;
+#pragma unroll
+    for (int p = 1; p <= PM; p *= 2) {
+        if (j >= 2 * p - 1) continue;
+        const bool square = n + 1 == 2 * p;
+        const int a0 = j < p ? 0 : j - p + 1, a1 = j < p ? j : p - 1;
+        // newest block [n + 1 - p, n] sits at nx[PM - p ..]
+        for (int a = a0; a <= a1; ++a) {
+            s = fmaf(nx[lr][PM - p + a], fh[lr][p + j - a], s);
+            if (!square) s = fmaf(nh[lr][PM - p + a], fx[lr][p + j - a], s);
+        }
+    }
+    q.acc[base + n + 1 + j] += s;
+}
+
+// Direct products of kDDNearMax < p < pd at position n, one thread per row,
+// after k_dd_near (which stored x_n, h_n).  Both products of a band block go
+// to the same targets.
+__global__ void __launch_bounds__(256) k_dd_wide(DDev q, long long n) {
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= q.R) return;
-    float *xr = q.xh + (size_t)r * q.L, *hr = q.hh + (size_t)r * q.L, *ar = q.acc + (size_t)r * q.L;
-    const float xn = x[r], hn = h[r];
-    xr[n] = xn;
-    hr[n] = hn;
-    y[r] = n == 0 ? xn * hn : fmaf(xr[0], hn, fmaf(xn, hr[0], ar[n]));
-    // direct blocks: both products of a band block go to the same targets
-    for (long long p = 1; p < q.pd && 2 * p <= n + 1 && (n + 1) % p == 0; p *= 2) {
+    const float *xr = q.xh + (size_t)r * q.L, *hr = q.hh + (size_t)r * q.L;
+    float *ar = q.acc + (size_t)r * q.L;
+    for (long long p = 2 * kDDNearMax; p < q.pd && 2 * p <= n + 1 && (n + 1) % p == 0; p *= 2) {
         const bool square = n + 1 == 2 * p;
         const long long lo = n + 1 - p;           // newest block [lo, n]
         for (long long j = 0; j < 2 * p - 1 && n + 1 + j < q.L; ++j) {

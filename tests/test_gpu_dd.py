@@ -37,7 +37,7 @@ def _seq(T, B, D, seed, decay):
     return x, h
 
 
-@pytest.mark.parametrize("fft_min", [2, 3, 5, 15])
+@pytest.mark.parametrize("fft_min", [2, 3, 5, 7, 8, 15])
 def test_dd_matches_definition(fft_min):
     B, D, L = 2, 5, 1024
     say(f"case data-dependent B={B} D={D} L={L} fft_min_log2={fft_min}")
