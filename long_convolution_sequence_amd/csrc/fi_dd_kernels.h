@@ -81,18 +81,25 @@ __global__ void __launch_bounds__(256) k_dd_near(DDev q, long long n, const floa
     if (!prod) return;
     __syncthreads();
     if (!live || j >= TR - 1 || n + 1 + j >= q.L) return;
-    float s = 0.f;
+    // term (a, b): newest-block element a times fixed-block element b, a + b = j.
+    // b runs over the whole block (compile-time trip counts, so the LDS reads
+    // pipeline); a = j - b outside [0, p) leaves the sums as they are.
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int p = 1; p <= PM; p *= 2) {
         if (j >= 2 * p - 1) continue;
         const bool square = n + 1 == 2 * p;
-        const int a0 = j < p ? 0 : j - p + 1, a1 = j < p ? j : p - 1;
-        // newest block [n + 1 - p, n] sits at nx[PM - p ..]
-        for (int a = a0; a <= a1; ++a) {
-            s = fmaf(nx[lr][PM - p + a], fh[lr][p + j - a], s);
-            if (!square) s = fmaf(nh[lr][PM - p + a], fx[lr][p + j - a], s);
+#pragma unroll
+        for (int b = 0; b < p; ++b) {
+            const int a = j - b;
+            const bool ok = (unsigned)a < (unsigned)p;
+            const int ai = PM - p + (ok ? a : 0);
+            const float s1 = fmaf(nx[lr][ai], fh[lr][p + b], s), t1 = fmaf(nh[lr][ai], fx[lr][p + b], t);
+            s = ok ? s1 : s;
+            t = ok && !square ? t1 : t;
         }
     }
+    s += t;
     q.acc[base + n + 1 + j] += s;
 }
 
