@@ -477,8 +477,8 @@ def main():
         fx.close()
         del fx
         dd = {"L": Ld, "B": w.B, "D": w.D, "ms": round(ms[-1], 3),
-              "tokens_per_s": round(Ld / (ms[-1] * 1e-3), 1),
-              "fixed_filter_per_position_tokens_per_s": round(Ld / (fixed_ms * 1e-3), 1),
+              "tokens_per_s": round(Ld * w.B / (ms[-1] * 1e-3), 1),
+              "fixed_filter_per_position_tokens_per_s": round(Ld * w.B / (fixed_ms * 1e-3), 1),
               "note": ("fi_dd_run over L positions of one layer (x and taps h seeded, given per position), "
                        "warm, HIP events; beside it the fixed-filter path at the same shape with one launch "
                        "per position (chunks off), one warm generation")}
