@@ -335,8 +335,8 @@ typedef struct fi_dd fi_dd; /* opaque, owned by the library */
  * spectra (16 L bytes per row) and twiddles.  0 if the shape is unsupported:
  * B, D >= 1, B*D <= 2^24, L a power of two up to 32768 (the widest product,
  * L/2 points, must fit one workgroup's transform); fft_min_log2 in [2, 15], or
- * -1 for the default 7.  Products of p < 2^fft_min_log2 run directly: up to
- * p = 64 inside the position's first launch (one thread per target), wider
+ * -1 for the default 8.  Products of p < 2^fft_min_log2 run directly: up to
+ * p = 128 inside the position's first launch (one thread per target), wider
  * ones one thread per row; the rest as FFTs. */
 size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log2);
 

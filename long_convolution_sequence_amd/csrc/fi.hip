@@ -1598,7 +1598,7 @@ struct fi_dd {
 namespace {
 
 constexpr int kDDMaxLog = 15;      // L <= 2^15: the widest product (L/2) is one workgroup's transform
-constexpr int kDDFftMinDefault = 7;    // products of p <= 64 run in the per-position launch
+constexpr int kDDFftMinDefault = 8;    // products of p <= 128 run in the per-position launch
 
 struct DDLayout {
     size_t xh = 0, hh = 0, acc = 0, twid = 0, total = 0;
@@ -1697,6 +1697,7 @@ fi_status dd_step(fi_dd *c, const float *x, const float *h, float *y) {
         case 8: dd_near_launch<8>(c, n, x, h, y, true); break;
         case 16: dd_near_launch<16>(c, n, x, h, y, true); break;
         case 32: dd_near_launch<32>(c, n, x, h, y, true); break;
+        case 64: dd_near_launch<64>(c, n, x, h, y, true); break;
         default: dd_near_launch<fi::kDDNearMax>(c, n, x, h, y, true); break;
     }
     const int64_t pw = 2 * fi::kDDNearMax;

@@ -36,7 +36,7 @@ struct DDev {
 // Direct products run in one launch per position up to this block size; wider
 // direct products (only when the FFT threshold is set above it) take the
 // serial per-row loop below.
-constexpr int kDDNearMax = 64;
+constexpr int kDDNearMax = 128;
 
 // Red cells of position n and every direct product of that position with
 // p <= PM.  The products of a position are those of p = 1, 2, 4, .., pm (each

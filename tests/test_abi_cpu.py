@@ -118,8 +118,8 @@ def test_dd_workspace_bytes(lib, B, D, L, kmin):
     assert lib.fi_dd_workspace_bytes(B, D, L, kmin) == _dd_expected_bytes(B, D, L, kmin)
 
 
-def test_dd_workspace_default_threshold_is_seven(lib):
-    assert lib.fi_dd_workspace_bytes(2, 3, 4096, -1) == lib.fi_dd_workspace_bytes(2, 3, 4096, 7)
+def test_dd_workspace_default_threshold_is_eight(lib):
+    assert lib.fi_dd_workspace_bytes(2, 3, 4096, -1) == lib.fi_dd_workspace_bytes(2, 3, 4096, 8)
 
 
 @pytest.mark.parametrize("B,D,L,kmin", [(0, 4, 64, 2), (1, 0, 64, 2), (1, 4, 0, 2), (1, 4, 48, 2),
