@@ -110,14 +110,20 @@ def test_paths_agree_and_runs_are_deterministic(chunk):
     say(f"case path agreement chunk={chunk} M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 5, decay=300.0) * 0.05
     x1 = np.random.default_rng(6).standard_normal((B, D)).astype(np.float32)
-    outs = {}
+    outs, paths = {}, {}
     for name, tau in TAUS.items():
         for graphs in (True, False):
             with fi.Context(_cuda(h), B, tau_mode=tau, use_graphs=graphs, chunk_direct=chunk) as ctx:
+                paths[(name, graphs)] = [q[1] for q in ctx.tau_table()]
                 ctx.set_input(_cuda(x1))
                 outs[(name, graphs)] = ctx.generate(L).cpu().numpy()
     for name in TAUS:
-        assert np.array_equal(outs[(name, True)], outs[(name, False)]), name
+        # "auto" times its split in each context; only the same choice fixes the order of the additions
+        if paths[(name, True)] == paths[(name, False)]:
+            assert np.array_equal(outs[(name, True)], outs[(name, False)]), name
+        else:
+            rel = np.abs(outs[(name, True)] - outs[(name, False)]).max() / np.abs(outs[(name, False)]).max()
+            assert name == "auto" and rel <= 1e-3, name
     ref = outs[("direct", True)]
     for name in ("fft", "auto"):
         rel = np.abs(outs[(name, True)] - ref).max() / np.abs(ref).max()
@@ -251,14 +257,16 @@ def test_edge_lengths_and_ragged_chain_counts(L):
 def test_chunk_kernel_with_and_without_records_agree(scale):
     """The chunk kernel the bench runs (no records) against the one the oracle replays check (records
     on): the same arithmetic, so the outputs agree bit for bit.  scale 0.02 keeps every |y| below 0.8
-    (the chains' polynomial pass holds); scale 1.0 leaves that range (the full-tanh reruns)."""
+    (the chains' polynomial pass holds); scale 1.0 leaves that range (the full-tanh reruns).  The
+    split is pinned: a calibrated one is timed per context and can differ between the two, and with
+    it the chunk length and the order of the additions."""
     M, B, D, L = 3, 2, 37, 2048
     say(f"case chunk kernel records on/off scale={scale} M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 31, decay=200.0) * scale
     x1 = np.random.default_rng(32).standard_normal((B, D)).astype(np.float32)
     outs = []
     for rec in (False, True):
-        with fi.Context(_cuda(h), B, record=rec) as ctx:
+        with fi.Context(_cuda(h), B, record=rec, tau_split=8) as ctx:
             ctx.set_input(_cuda(x1))
             outs.append(ctx.generate(L).cpu().numpy())
     big = float(np.abs(outs[0]).max())
