@@ -183,14 +183,21 @@ fi_status fi_step(fi_ctx *ctx, const float *x_t, float *y_t);
  * output exists (position 0), device fp32 [B][D]. */
 fi_status fi_set_input(fi_ctx *ctx, const float *x0);
 
-/* Teacher-forced prompt: equivalent to P calls fi_step(x + (i-1)*B*D, y ...)
+/* Teacher-forced prompt (Flash Inference rebuttal page, reply on prefill: the
+ * prompt is given at once, so its contributions to all later outputs can be
+ * pushed eagerly; summary page, "Einschraenkungen": prefill dominates the
+ * cost for long prompts): equivalent to P calls fi_step(x + (i-1)*B*D, y ...)
  * for i = 1..P (the invariant the tests check).
  *   x: device fp32 [P][B][D]; y: device fp32 [P][B][D] or NULL.
  * The prompt's positions are processed in place (position advances by P). */
 fi_status fi_prefill(fi_ctx *ctx, const float *x, int64_t P, float *y);
 
-/* Free-running generation of `steps` positions with internal feedback, with
- * one hipGraph per block-size class plus block graphs (use_graphs = 1).
+/* Free-running generation of `steps` positions with internal feedback (summary
+ * page, "LCSM-Inferenz-Algorithmus", Algorithm 2: per position the layers' red
+ * cells in order, the next input from the last layer's output, then every
+ * layer's gray block; "Schicht-uebergreifende Parallelisierung", Algorithm 3:
+ * the gray blocks of all layers in one launch), with one hipGraph per
+ * block-size class plus block graphs (use_graphs = 1) or chunk launches.
  *   y: device fp32 [steps][B][D] receiving y^{M-1}_n for each position, or NULL.
  * FI_ERANGE if position + steps > L (nothing is run). */
 fi_status fi_generate(fi_ctx *ctx, int64_t steps, float *y);
@@ -342,10 +349,11 @@ size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log
 
 /* Create a context at position 0 over the caller's workspace (device, at
  * least fi_dd_workspace_bytes, 256-byte aligned; the context keeps using it
- * until fi_dd_destroy).  Synchronises the stream.  FI_EINVAL for a null
+ * until fi_dd_destroy).  stream: the hipStream_t every call of the context is
+ * ordered on (NULL = default stream).  Synchronises the stream.  FI_EINVAL for a null
  * pointer or an unsupported shape, FI_EDEVICE if a HIP call fails. */
 fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
-                     hipStream_t stream);
+                     void *stream);
 
 /* One position: x_t and h_t ([B][D], device) arrive, y_t ([B][D], device) is
  * written.  FI_ERANGE after L positions, FI_EINVAL for null pointers,

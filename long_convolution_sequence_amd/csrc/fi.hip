@@ -23,6 +23,7 @@
 #include "fi_kernels.h"
 #include "fi_fft_kernels.h"
 #include "fi_dd_kernels.h"
+#include "fi_tables.h"
 
 using namespace fi;
 
@@ -39,6 +40,13 @@ constexpr int kHeadTaps = 256;    // taps h[0..255] serve direct blocks up to U 
 constexpr int kChunkEv = -1;      // event-pair class of a timed chunk kernel
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Launch shape of the transform kernels of 2^logn points (FftShape on the host).
+int fft_tpb(int logn) {
+    const int tt = logn >= 4 ? (1 << logn) / 16 : 1;
+    return tt >= 256 ? tt : 256;
+}
+int fft_per_block(int logn) { return fft_tpb(logn) / (logn >= 4 ? (1 << logn) / 16 : 1); }
 
 int ilog2_exact(int64_t L) {
     if (L < 1 || (L & (L - 1)) != 0) return -1;
@@ -322,16 +330,10 @@ int choose_chunk_ch(int M, int BD, int logg, int cus) {
 
 // k_chunk<MT, MODE>: MT = M up to kChunkRegLayers (layers in registers), else
 // 0; MODE = kChunkRec (records kept) | kChunkTanh (tanh map and feedback)
-using ChunkKernel = void (*)(Dev, long long, int, int, const float *);
-template <int... I>
-constexpr std::array<ChunkKernel, 4 * sizeof...(I)> chunk_table(std::integer_sequence<int, I...>) {
-    return {{&k_chunk<I / 4, I % 4>...}};
-}
-constexpr auto kChunkKernels = chunk_table(std::make_integer_sequence<int, 4 * (kChunkRegLayers + 1)>{});
-ChunkKernel chunk_kernel(const fi_ctx *c) {
+ChunkK chunk_kernel(const fi_ctx *c) {
     const int mode = (c->opt.record ? kChunkRec : 0) |
                      (c->opt.map == FI_MAP_TANH && c->opt.feedback == FI_FEEDBACK_TANH ? kChunkTanh : 0);
-    return kChunkKernels[4 * (c->M <= kChunkRegLayers ? c->M : 0) + mode];
+    return chunk_k(c->M <= kChunkRegLayers ? c->M : 0, mode);
 }
 
 // ev0/ev1 (optional) are stamped by the dispatch at the kernel's start and end
@@ -364,22 +366,20 @@ void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hi
         hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
-template <int LOGN>
-hipError_t launch_fft_n(fi_ctx *c, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
-    using S = FftShape<LOGN>;
-    const long long tiles = (long long)c->M * c->B * c->D;
-    const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    launch_k(k_fft_tile<LOGN>, dim3((unsigned)grid), dim3(S::TPB), s, ev0, ev1, c->dev, rd,
-             (const float4 *)c->spec[LOGN], advance);
+hipError_t launch_fft_n(fi_ctx *c, int logn, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
+    const FftTileK k = fft_tile_k(logn);
+    if (!k) return hipErrorInvalidValue;
+    const long long tiles = (long long)c->M * c->B * c->D, pb = fft_per_block(logn);
+    launch_k(k, dim3((unsigned)((tiles + pb - 1) / pb)), dim3(fft_tpb(logn)), s, ev0, ev1, c->dev, rd,
+             (const float4 *)c->spec[logn], advance);
     return hipGetLastError();
 }
 
-template <int LOGN>
-hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long goff, long long stride) {
-    using S = FftShape<LOGN>;
-    const long long rows = (long long)c->M * c->D;
-    const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_spectrum<LOGN>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst, goff,
+hipError_t launch_spectrum_n(fi_ctx *c, int logn, hipStream_t s, float4 *dst, long long goff, long long stride) {
+    const SpectrumK k = spectrum_k(logn);
+    if (!k) return hipErrorInvalidValue;
+    const long long rows = (long long)c->M * c->D, pb = fft_per_block(logn);
+    hipLaunchKernelGGL(k, dim3((unsigned)((rows + pb - 1) / pb)), dim3(fft_tpb(logn)), 0, s, c->dev, dst, goff,
                        stride);
     return hipGetLastError();
 }
@@ -388,54 +388,44 @@ hipError_t launch_spectrum_n(fi_ctx *c, hipStream_t s, float4 *dst, long long go
 // position n known): the forward kernel and output sub-block 0 on s, output
 // sub-blocks 1..K-1 on the side stream after the forward kernel, timed by
 // dv0/dv1 when given.
-template <int LOGV>
-hipError_t launch_fft_sub_v(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
-                            int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
+hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
+                          int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
+    const int LOGV = c->opt.fft_max_log2;
+    const SubFwdK kf = sub_fwd_k(LOGV);
+    const SubInvK ki = sub_inv_k(LOGV);
+    if (!kf || !ki) return hipErrorInvalidValue;
     const int K = sub_k(q, LOGV);
     const long long rows = (long long)c->M * c->B * c->D;
-    const dim3 blk(FftShape<LOGV>::TPB);
-    launch_k(k_fft_sub_fwd<LOGV>, dim3((unsigned)(rows * K)), blk, s, ev0, nullptr, c->dev, rd, c->scratch, K);
+    const dim3 blk(fft_tpb(LOGV));
+    launch_k(kf, dim3((unsigned)(rows * K)), blk, s, ev0, nullptr, c->dev, rd, c->scratch, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float4 *A = c->scratch, *G = c->spec[q];
     if (!defer) {
-        launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)(rows * K)), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, K,
-                 0LL, advance);
+        launch_k(ki, dim3((unsigned)(rows * K)), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, K, 0LL, advance);
         return hipGetLastError();
     }
-    launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)rows), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, 1, 0LL,
-             advance);
+    launch_k(ki, dim3((unsigned)rows), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, 1, 0LL, advance);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the deferred sub-blocks start once sub-block 0 is done, so they never
     // compete with the position's critical path
     if ((e = hipEventRecord(c->ev_split, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(c->side, c->ev_split, 0)) != hipSuccess) return e;
-    launch_k(k_fft_sub_inv<LOGV>, dim3((unsigned)(rows * (K - 1))), blk, c->side, dv0, dv1, c->dev, rd, A, G, K, 1,
-             K - 1, (long long)defer, 0);
+    launch_k(ki, dim3((unsigned)(rows * (K - 1))), blk, c->side, dv0, dv1, c->dev, rd, A, G, K, 1, K - 1,
+             (long long)defer, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipEventRecord(c->ev_side, c->side)) != hipSuccess) return e;
     c->side_until = defer + (int64_t(1) << LOGV);
     return hipSuccess;
 }
 
-template <int LOGM>
-hipError_t launch_fft2_m(fi_ctx *c, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
-    using S = FftShape<LOGM>;
-    const long long tiles = (long long)c->M * c->B * c->D;
-    const long long grid = (tiles + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    launch_k(k_fft_tile2<LOGM>, dim3((unsigned)grid), dim3(S::TPB), s, ev0, ev1, c->dev, rd,
-             (const float4 *)c->spec[LOGM + 1], advance);
+hipError_t launch_fft2_m(fi_ctx *c, int logm, int rd, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1) {
+    const FftTileK k = fft_tile2_k(logm);
+    if (!k) return hipErrorInvalidValue;
+    const long long tiles = (long long)c->M * c->B * c->D, pb = fft_per_block(logm);
+    launch_k(k, dim3((unsigned)((tiles + pb - 1) / pb)), dim3(fft_tpb(logm)), s, ev0, ev1, c->dev, rd,
+             (const float4 *)c->spec[logm + 1], advance);
     return hipGetLastError();
-}
-
-hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
-                          int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
-    switch (c->opt.fft_max_log2) {
-        case 12: return launch_fft_sub_v<12>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
-        case 13: return launch_fft_sub_v<13>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
-        case 14: return launch_fft_sub_v<14>(c, rd, q, s, advance, ev0, ev1, defer, dv0, dv1);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 // FFT gray blocks of class q; ev0/ev1 (optional) are stamped at the start of
@@ -443,38 +433,16 @@ hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, 
 hipError_t launch_fft(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0 = nullptr,
                       hipEvent_t ev1 = nullptr) {
     if (is_sub(q, c->opt.fft_max_log2)) return launch_fft_sub(c, rd, q, s, advance, ev0, ev1);
-    if (is_pair(q, c->opt.fft_max_log2)) {
-        switch (c->opt.fft_max_log2) {
-            case 12: return launch_fft2_m<12>(c, rd, s, advance, ev0, ev1);
-            case 13: return launch_fft2_m<13>(c, rd, s, advance, ev0, ev1);
-            case 14: return launch_fft2_m<14>(c, rd, s, advance, ev0, ev1);
-            default: return hipErrorInvalidValue;
-        }
-    }
-    switch (q) {
-        case 2: return launch_fft_n<2>(c, rd, s, advance, ev0, ev1);
-        case 3: return launch_fft_n<3>(c, rd, s, advance, ev0, ev1);
-        case 4: return launch_fft_n<4>(c, rd, s, advance, ev0, ev1);
-        case 5: return launch_fft_n<5>(c, rd, s, advance, ev0, ev1);
-        case 6: return launch_fft_n<6>(c, rd, s, advance, ev0, ev1);
-        case 7: return launch_fft_n<7>(c, rd, s, advance, ev0, ev1);
-        case 8: return launch_fft_n<8>(c, rd, s, advance, ev0, ev1);
-        case 9: return launch_fft_n<9>(c, rd, s, advance, ev0, ev1);
-        case 10: return launch_fft_n<10>(c, rd, s, advance, ev0, ev1);
-        case 11: return launch_fft_n<11>(c, rd, s, advance, ev0, ev1);
-        case 12: return launch_fft_n<12>(c, rd, s, advance, ev0, ev1);
-        case 13: return launch_fft_n<13>(c, rd, s, advance, ev0, ev1);
-        case 14: return launch_fft_n<14>(c, rd, s, advance, ev0, ev1);
-        default: return hipErrorInvalidValue;
-    }
+    if (is_pair(q, c->opt.fft_max_log2)) return launch_fft2_m(c, c->opt.fft_max_log2, rd, s, advance, ev0, ev1);
+    return launch_fft_n(c, q, rd, s, advance, ev0, ev1);
 }
 
-template <int LOGM>
-hipError_t launch_spectrum2_m(fi_ctx *c, hipStream_t s, float4 *dst, long long goff, long long stride) {
-    using S = FftShape<LOGM>;
-    const long long rows = (long long)c->M * c->D;
-    const long long grid = (rows + S::PER_BLOCK - 1) / S::PER_BLOCK;
-    hipLaunchKernelGGL((k_spectrum2<LOGM>), dim3((unsigned)grid), dim3(S::TPB), 0, s, c->dev, dst, goff, stride);
+hipError_t launch_spectrum2_m(fi_ctx *c, int logm, hipStream_t s, float4 *dst, long long goff, long long stride) {
+    const SpectrumK k = spectrum2_k(logm);
+    if (!k) return hipErrorInvalidValue;
+    const long long rows = (long long)c->M * c->D, pb = fft_per_block(logm);
+    hipLaunchKernelGGL(k, dim3((unsigned)((rows + pb - 1) / pb)), dim3(fft_tpb(logm)), 0, s, c->dev, dst, goff,
+                       stride);
     return hipGetLastError();
 }
 
@@ -488,37 +456,13 @@ hipError_t launch_spectrum(fi_ctx *c, int q, hipStream_t s) {
         for (int d = 1; d <= 2 * sub_k(q, vlog) - 1; ++d) {
             float4 *dd = dst + (d - 1) * (V / 2);
             const long long goff = (d - 1) * V;
-            hipError_t e = vlog == 12   ? launch_spectrum_n<12>(c, s, dd, goff, stride)
-                           : vlog == 13 ? launch_spectrum_n<13>(c, s, dd, goff, stride)
-                                        : launch_spectrum_n<14>(c, s, dd, goff, stride);
+            hipError_t e = launch_spectrum_n(c, vlog, s, dd, goff, stride);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
-    if (is_pair(q, vlog)) {
-        switch (vlog) {
-            case 12: return launch_spectrum2_m<12>(c, s, dst, 0, stride);
-            case 13: return launch_spectrum2_m<13>(c, s, dst, 0, stride);
-            case 14: return launch_spectrum2_m<14>(c, s, dst, 0, stride);
-            default: return hipErrorInvalidValue;
-        }
-    }
-    switch (q) {
-        case 2: return launch_spectrum_n<2>(c, s, dst, 0, stride);
-        case 3: return launch_spectrum_n<3>(c, s, dst, 0, stride);
-        case 4: return launch_spectrum_n<4>(c, s, dst, 0, stride);
-        case 5: return launch_spectrum_n<5>(c, s, dst, 0, stride);
-        case 6: return launch_spectrum_n<6>(c, s, dst, 0, stride);
-        case 7: return launch_spectrum_n<7>(c, s, dst, 0, stride);
-        case 8: return launch_spectrum_n<8>(c, s, dst, 0, stride);
-        case 9: return launch_spectrum_n<9>(c, s, dst, 0, stride);
-        case 10: return launch_spectrum_n<10>(c, s, dst, 0, stride);
-        case 11: return launch_spectrum_n<11>(c, s, dst, 0, stride);
-        case 12: return launch_spectrum_n<12>(c, s, dst, 0, stride);
-        case 13: return launch_spectrum_n<13>(c, s, dst, 0, stride);
-        case 14: return launch_spectrum_n<14>(c, s, dst, 0, stride);
-        default: return hipErrorInvalidValue;
-    }
+    if (is_pair(q, vlog)) return launch_spectrum2_m(c, vlog, s, dst, 0, stride);
+    return launch_spectrum_n(c, q, s, dst, 0, stride);
 }
 
 // All kernels of one position of class q (q == P: the last position, red cells only).
@@ -1157,35 +1101,15 @@ bool eager_prefill_ok(const fi_ctx *c, int64_t P) {
            P < (int64_t(1) << (c->opt.fft_max_log2 + 1)) && P <= c->pre_stride;
 }
 
-template <int LOGN>
-hipError_t launch_pre_fft_n(fi_ctx *c, int l, int64_t P) {
-    using S = FftShape<LOGN>;
-    const long long BD = (long long)c->B * c->D;
-    const unsigned nb = (unsigned)(((P >> LOGN) + 1) >> 1);   // odd multiples of 2^LOGN up to P
-    if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pre_fft<LOGN>, dim3((unsigned)((BD + S::PER_BLOCK - 1) / S::PER_BLOCK), nb), dim3(S::TPB),
-                       0, c->stream, c->dev, (const float4 *)c->spec[LOGN], l, (long long)P, c->pre,
-                       c->pre_stride);
-    return hipGetLastError();
-}
-
 hipError_t launch_pre_fft(fi_ctx *c, int q, int l, int64_t P) {
-    switch (q) {
-        case 2: return launch_pre_fft_n<2>(c, l, P);
-        case 3: return launch_pre_fft_n<3>(c, l, P);
-        case 4: return launch_pre_fft_n<4>(c, l, P);
-        case 5: return launch_pre_fft_n<5>(c, l, P);
-        case 6: return launch_pre_fft_n<6>(c, l, P);
-        case 7: return launch_pre_fft_n<7>(c, l, P);
-        case 8: return launch_pre_fft_n<8>(c, l, P);
-        case 9: return launch_pre_fft_n<9>(c, l, P);
-        case 10: return launch_pre_fft_n<10>(c, l, P);
-        case 11: return launch_pre_fft_n<11>(c, l, P);
-        case 12: return launch_pre_fft_n<12>(c, l, P);
-        case 13: return launch_pre_fft_n<13>(c, l, P);
-        case 14: return launch_pre_fft_n<14>(c, l, P);
-        default: return hipErrorInvalidValue;
-    }
+    const PreFftK k = pre_fft_k(q);
+    if (!k) return hipErrorInvalidValue;
+    const long long BD = (long long)c->B * c->D, pb = fft_per_block(q);
+    const unsigned nb = (unsigned)(((P >> q) + 1) >> 1);   // odd multiples of 2^q up to P
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(k, dim3((unsigned)((BD + pb - 1) / pb), nb), dim3(fft_tpb(q)), 0, c->stream, c->dev,
+                       (const float4 *)c->spec[q], l, (long long)P, c->pre, c->pre_stride);
+    return hipGetLastError();
 }
 
 // The prompt x[P][B][D] at position 0, layer by layer with all positions at
@@ -1647,40 +1571,21 @@ fi_status dd_fail(fi_dd *c, fi_status s, const std::string &msg) {
             return dd_fail((ctx), FI_EDEVICE, std::string(#call) + ": " + hipGetErrorString(e_)); \
     } while (0)
 
-template <int K>
-void dd_launch_k(fi_dd *c, int64_t n) {
-    using S = fi::FftShape<K>;
-    const unsigned grid = (unsigned)((c->R + S::PER_BLOCK - 1) / S::PER_BLOCK);
-    if (n + 1 == (int64_t(2) << K))   // the fixed blocks x[p, 2p), h[p, 2p) are complete: their spectra
-        hipLaunchKernelGGL((fi::k_dd_band<K>), dim3(grid, 2), dim3(S::TPB), 0, c->stream, c->dev, c->q, c->spx[K],
-                           c->sph[K]);
-    hipLaunchKernelGGL((fi::k_dd_fft<K>), dim3(grid), dim3(S::TPB), 0, c->stream, c->dev, c->q, c->spx[K], c->sph[K],
-                       (long long)n);
-}
-
 void dd_launch(fi_dd *c, int k, int64_t n) {
-    switch (k) {
-        case 2: return dd_launch_k<2>(c, n);
-        case 3: return dd_launch_k<3>(c, n);
-        case 4: return dd_launch_k<4>(c, n);
-        case 5: return dd_launch_k<5>(c, n);
-        case 6: return dd_launch_k<6>(c, n);
-        case 7: return dd_launch_k<7>(c, n);
-        case 8: return dd_launch_k<8>(c, n);
-        case 9: return dd_launch_k<9>(c, n);
-        case 10: return dd_launch_k<10>(c, n);
-        case 11: return dd_launch_k<11>(c, n);
-        case 12: return dd_launch_k<12>(c, n);
-        case 13: return dd_launch_k<13>(c, n);
-        case 14: return dd_launch_k<14>(c, n);
-        default: return;
-    }
+    const fi::DDBandK kb = fi::dd_band_k(k);
+    const fi::DDFftK kf = fi::dd_fft_k(k);
+    if (!kb || !kf) return;
+    const long long pb = fft_per_block(k);
+    const unsigned grid = (unsigned)((c->R + pb - 1) / pb);
+    if (n + 1 == (int64_t(2) << k))   // the fixed blocks x[p, 2p), h[p, 2p) are complete: their spectra
+        hipLaunchKernelGGL(kb, dim3(grid, 2), dim3(fft_tpb(k)), 0, c->stream, c->dev, c->q, c->spx[k], c->sph[k]);
+    hipLaunchKernelGGL(kf, dim3(grid), dim3(fft_tpb(k)), 0, c->stream, c->dev, c->q, (const float4 *)c->spx[k],
+                       (const float4 *)c->sph[k], (long long)n);
 }
 
-template <int PM>
-void dd_near_launch(fi_dd *c, int64_t n, const float *x, const float *h, float *y, bool prod) {
-    constexpr int RPW = 128 / PM;   // rows per 256-thread workgroup
-    hipLaunchKernelGGL(fi::k_dd_near<PM>, dim3((unsigned)((c->R + RPW - 1) / RPW)), dim3(256), 0, c->stream, c->q,
+void dd_near_launch(fi_dd *c, int pm, int64_t n, const float *x, const float *h, float *y, bool prod) {
+    const int rpw = 128 / pm;   // rows per 256-thread workgroup
+    hipLaunchKernelGGL(fi::dd_near_k(pm), dim3((unsigned)((c->R + rpw - 1) / rpw)), dim3(256), 0, c->stream, c->q,
                        (long long)n, x, h, y, prod);
 }
 
@@ -1689,17 +1594,7 @@ fi_status dd_step(fi_dd *c, const float *x, const float *h, float *y) {
     // largest direct product of this position up to the one-launch limit (0: none)
     int64_t pm = 0;
     for (int64_t p = 1; p <= fi::kDDNearMax && p < c->q.pd && 2 * p <= n + 1 && (n + 1) % p == 0; p *= 2) pm = p;
-    switch (pm) {
-        case 0: dd_near_launch<1>(c, n, x, h, y, false); break;
-        case 1: dd_near_launch<1>(c, n, x, h, y, true); break;
-        case 2: dd_near_launch<2>(c, n, x, h, y, true); break;
-        case 4: dd_near_launch<4>(c, n, x, h, y, true); break;
-        case 8: dd_near_launch<8>(c, n, x, h, y, true); break;
-        case 16: dd_near_launch<16>(c, n, x, h, y, true); break;
-        case 32: dd_near_launch<32>(c, n, x, h, y, true); break;
-        case 64: dd_near_launch<64>(c, n, x, h, y, true); break;
-        default: dd_near_launch<fi::kDDNearMax>(c, n, x, h, y, true); break;
-    }
+    dd_near_launch(c, pm ? (int)pm : 1, n, x, h, y, pm != 0);
     const int64_t pw = 2 * fi::kDDNearMax;
     if (c->q.pd > pw && 2 * pw <= n + 1 && (n + 1) % pw == 0)
         hipLaunchKernelGGL(fi::k_dd_wide, dim3((unsigned)((c->R + 255) / 256)), dim3(256), 0, c->stream, c->q,
@@ -1721,7 +1616,8 @@ size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log
 }
 
 fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
-                     hipStream_t stream) {
+                     void *stream_) {
+    hipStream_t stream = (hipStream_t)stream_;
     if (!out || !workspace) return FI_EINVAL;
     *out = nullptr;
     DDLayout ly;

@@ -1,0 +1,350 @@
+// The chunk kernel: all positions between two FFT positions as one launch
+// for maps that act channel by channel (see the comment on k_chunk).
+//
+// Flash Inference (arXiv 2410.12982), summary page, "Kachelung-Strategie
+// (Algorithmus 1)": the gray blocks of edge below G inside a chunk cover every
+// pair s < t of the chunk exactly once; "LCSM-Inferenz-Algorithmus"
+// (Algorithm 2): the red cells of a position run layer after layer.
+#pragma once
+#include <type_traits>
+
+#include "fi_device.h"
+
+namespace fi {
+
+constexpr int kChunkThreads = 1024;  // chunk workgroups: wave 0 + up to 15 helper waves
+
+// ---------------------------------------------------------------------------
+// All positions of one chunk (cb, cb + G] (cb a multiple of G, the edge of
+// the first FFT class, G <= 256) for maps that act channel by channel.  Then
+// every (b, c) chain is independent through all layers, and so is every gray
+// block below G: their sources and targets lie in the same chunk (a block
+// after n has U = lowbit(n) < G, so n + U never passes the next multiple of
+// G).  One workgroup owns CH chains and all M layers and runs the chunk's G
+// positions back to back, with a barrier between positions and no launch.
+//
+// The gray blocks of edge U < G inside a chunk cover every pair s < t of the
+// chunk exactly once, so their sum into target t is the causal dot product
+// over the chunk.  It is formed here target by target:
+//   pend(t) = fft(t) + sum_{k=2..} h[k] x_{t-k}  (helpers, during position t-1)
+//           + h[1] x_{t-1}                       (chain lane, at position t)
+// so only the last term waits for the position before.  One LDS slot per
+// (position, row) holds the FFT pending sum (loaded from the row-major
+// history), then the finished sum, then the input x_t (the pages' activation
+// reuse); at the end the slots are the inputs the next FFT block reads.
+//
+// Waves (16): wave 0 runs the red cells, one chain per lane; the other waves
+// of its SIMD (4, 8, 12: waves go to the four SIMDs in turn) stay off the
+// arithmetic, and wave 4 stamps each position once its barrier has passed;
+// the twelve remaining waves are helpers, eight lanes per row.
+//
+// LDS: heads h01[R] (h[0], h[1]); slots xp[G][kChunkSlot], slot s at row
+// G-1-s (reversed, so that the taps of a helper lie at increasing addresses:
+// immediate offsets, read in pairs); zero rows G .. G+63; teacher-forced
+// inputs xs[G][CH].  Rows rho = j * M + l for chain c0 + j, layer l.
+//
+// Global memory inside the position loop: the chain's last-layer output, the
+// helpers' history stores (one 128-byte line per row every 32 positions, for
+// the FFT block at the chunk's end) and wave 4's stamps.
+// ---------------------------------------------------------------------------
+constexpr int kChunkTaps = 32;       // taps per helper lane: h[seg + 8m], m < 32 (G <= 256)
+constexpr int kChunkTapRow = 8 * kChunkTaps;   // tap-table floats per (l, c): taps 0..255
+constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's layers in registers
+constexpr int kChunkHelperWaves = 12;
+constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
+// floats per slot: >= the rows, and 8 slots apart = 15 x 256 bytes (one
+// read2st64 reaches two taps); the eight lanes of a row then hit distinct banks
+constexpr int kChunkSlot = 120;
+// zero rows after the slots: the helper taps that lie before the chunk read them
+constexpr int kChunkZeroRows = 64;
+// positions a chain stays on the full tanh after its polynomial pass failed
+constexpr int kChainFullRun = 128;
+// chunk kernel variants: records every layer's input and output; both maps tanh
+constexpr int kChunkRec = 1, kChunkTanh = 2;
+
+// Red cells of the chunk's positions for one chain per lane of wave 0, all
+// layers; one barrier per position, as in the other waves.  MT = M layers:
+// heads and the previous position's inputs in registers, the pending sums of
+// the position read from LDS in one batch, then straight-line code with no
+// branch between layers.  Lanes without a chain run the same code on chain
+// 0's data and store nothing.  MT = 0: any depth, one layer at a time from LDS.
+template <int MT, bool REC, bool TANH_ALL>
+__device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
+                                          int chain, bool on, const float *xs, int CH) {
+    const int BD = p.B * p.D, M = p.M;
+    const int jr = on ? j : 0;                 // the chain whose LDS data this lane reads
+    constexpr int NR = MT > 0 ? MT : 1;
+    float h0[NR], h1[NR], xq[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const float2 v = MT > 0 ? hz[jr * M + k] : make_float2(0.f, 0.f);
+        h0[k] = v.x;
+        h1[k] = v.y;
+        xq[k] = 0.f;                           // slot -1: its tap-1 term is in the FFT sums
+    }
+    float xf = on ? p.xin[(size_t)((cb + 1) & 1) * BD + chain] : 0.f;   // feedback input
+    const bool map_id = !TANH_ALL && p.map != 0, fb_id = !TANH_ALL && p.fb != 0;
+    int full_left = 0;                         // wave-uniform: positions left on the full tanh
+    for (int i = 0; i < G; ++i) {
+        const long long t = cb + 1 + i;        // position
+        float x = xs ? xs[i * CH + jr] : xf;   // teacher-forced inputs, staged in LDS
+        float *cur = xp + (size_t)(G - 1 - i) * kChunkSlot + jr * M;   // this chain's layers at slot i
+        float y = 0.f;
+        if constexpr (MT > 0) {
+            float a[MT];
+#pragma unroll
+            for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
+            const float x0 = x;
+            unsigned long long far = 0;                // lanes with some |y| >= 0.8
+            // the position's layers; FULL = false: tanh by its polynomial half
+            // alone, with a vote on whether every |y| stayed below 0.8
+            auto layers = [&](auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                x = x0;
+#pragma unroll
+                for (int k = 0; k < MT; ++k) {
+                    y = fmaf(h0[k], x, a[k]);
+                    xq[k] = x;
+                    if constexpr (REC) {
+                        if (on) {
+                            const size_t r = ((size_t)(t - 1) * MT + k) * BD + chain;
+                            p.recx[r] = x;
+                            p.recy[r] = y;
+                        }
+                    }
+                    const float th = FULL ? tanh_chain(y) : tanh_small(y);
+                    if constexpr (!FULL) far |= __builtin_amdgcn_ballot_w64(!(fabsf(y) < 0.8f));
+                    if constexpr (TANH_ALL) {
+                        x = th;
+                    } else {
+                        x = (k + 1 < MT ? map_id : fb_id) ? y : th;   // both maps evaluated, one selected
+                    }
+                }
+            };
+            if constexpr (TANH_ALL) {
+                // Both maps tanh.  The polynomial pass runs first, which keeps
+                // the exponential's two transcendental steps off the chain; if
+                // some lane of the wave left its range, the position runs again
+                // with the full tanh (same values where both apply), and so do
+                // the next kChainFullRun positions before the polynomial pass
+                // is tried again (activations that stay large then cost one
+                // extra pass per kChainFullRun positions).
+                if (full_left == 0) {
+                    far = 0;
+                    layers(std::false_type{});
+                    if (far) full_left = kChainFullRun + 1;
+                }
+                if (full_left > 0) {
+                    layers(std::true_type{});
+                    --full_left;
+                }
+            } else {
+                layers(std::true_type{});
+            }
+            if (on) {
+#pragma unroll
+                for (int k = 0; k < MT; ++k) cur[k] = xq[k];
+            }
+        } else {
+            for (int l = 0; l < M; ++l) {
+                const float2 h = hz[jr * M + l];
+                const float pend = i > 0 ? fmaf(h.y, cur[l + kChunkSlot], cur[l]) : cur[l];
+                y = fmaf(h.x, x, pend);
+                if (on) cur[l] = x;
+                if (REC && on) {
+                    const size_t r = ((size_t)(t - 1) * M + l) * BD + chain;
+                    p.recx[r] = x;
+                    p.recy[r] = y;
+                }
+                x = apply_map(l + 1 < M ? p.map : p.fb, y);
+            }
+        }
+        if (on) p.ylast[(size_t)(t - 1) * BD + chain] = y;
+        xf = x;
+        __syncthreads();
+    }
+    if (on) p.xin[(size_t)((cb + G + 1) & 1) * BD + chain] = xf;
+}
+
+// Sum over each aligned group of eight lanes, in every lane of the group:
+// swaps within quads (lane ^ 1, lane ^ 2), then the mirror within the group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);   // row_half_mirror
+    return v;
+}
+
+// A helper lane's partial sum over its taps m < 8 (NF + 1) (tap m: slot row
+// row0 + 8m, register hreg[m]).  Taps of group NF that lie before the
+// chunk's first slot read the zero rows after the slots (rows G .. G+63:
+// with NF = (i+2)/64, row0 + 8m never passes G+63), so every tap is a plain
+// read at a fixed offset.
+template <int NF>
+__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho) {
+    constexpr int S = 8, SP = kChunkSlot;
+    constexpr int NT = NF < 4 ? 8 * (NF + 1) : 32;
+    float v[NT];
+    const float *base = xp + (size_t)row0 * SP + hrho;
+    // taps 16..31 from a second base 16 taps on: read in pairs, two taps
+    // apart by 15 x 256 bytes, the offsets from one base stop at 64 KB.  The
+    // empty asm keeps the compiler from folding the two bases back into one.
+    int off1 = row0 * SP + hrho + 16 * S * SP;
+    asm volatile("" : "+v"(off1));
+#pragma unroll
+    for (int m = 0; m < NT; ++m) v[m] = m < 16 ? base[(size_t)m * S * SP] : xp[off1 + (m - 16) * S * SP];
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m & 3] = fmaf(hreg[m], v[m], acc[m & 3]);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <int MT, int MODE>
+__global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, int G, int CH, const float *xseq) {
+    constexpr int S = 8;                       // helper lanes per row
+    constexpr int SP = kChunkSlot;
+    extern __shared__ float sm[];
+    const int M = p.M, BD = p.B * p.D, R = CH * M;
+    float2 *h01 = (float2 *)sm;                            // [R]
+    float *xp = sm + 2 * R;                                // [G][SP], slot s at row G-1-s
+    float *xz = xp + (size_t)G * SP;                       // [kChunkZeroRows][SP] zeros: rows G..
+    float *xs = xz + kChunkZeroRows * SP;                  // [G][CH] teacher-forced inputs
+    const int c0 = blockIdx.x * CH;
+    const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
+    const int logG = 31 - __clz(G);
+    auto grow = [&](int rho) {                             // history row of local row rho
+        return ((size_t)(rho % M) * BD + c0 + rho / M) * (size_t)p.L;
+    };
+    auto frow = [&](int rho) {                             // filter row
+        return ((size_t)(rho % M) * p.D + (c0 + rho / M) % p.D) * (size_t)p.L;
+    };
+    auto trow = [&](int rho) {                             // tap-table row
+        return (size_t)(rho % M) * p.D + (c0 + rho / M) % p.D;
+    };
+    auto live = [&](int rho) { return c0 + rho / M < BD; };
+
+    // helper lanes: row hrho, taps h[seg + 8m] (zero for k < 2: the chain
+    // adds tap 1, tap 0 is the red cell's own term); loads issued first
+    const int hw = (wave & 3) ? wave - 1 - wave / 4 : -1;
+    const int hid = hw * kLanes + lane;
+    const int hrho = hid / S, seg = hid & (S - 1);
+    const bool helper = hw >= 0 && hrho < R && live(hrho);
+    float hreg[kChunkTaps];
+    {
+        // the lane's 32 taps lie together in the tap table: eight 16-byte loads
+        const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
+                                            seg * kChunkTaps);
+#pragma unroll
+        for (int q = 0; q < kChunkTaps / 4; ++q) {
+            const float4 v = tp[q];
+            hreg[4 * q] = v.x;
+            hreg[4 * q + 1] = v.y;
+            hreg[4 * q + 2] = v.z;
+            hreg[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int m = 0; m < kChunkTaps; ++m) {
+            const int k = seg + S * m;
+            if (!(helper && k >= 2 && k < G)) hreg[m] = 0.f;
+        }
+    }
+
+    // pending sums of the chunk's positions (rows of the history, G slots
+    // each: coalesced reads), the heads, the teacher-forced inputs
+    if (G >= 4) {
+        const int g4 = logG - 2;                           // float4 per row: G / 4
+        for (int e = threadIdx.x; e < (R * G) >> 2; e += blockDim.x) {
+            const int rho = e >> g4, s0 = (e & ((G >> 2) - 1)) * 4;
+            const float4 v = live(rho) ? *(const float4 *)(p.buf + grow(rho) + cb + s0)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+            float *d = xp + (size_t)(G - 1 - s0) * SP + rho;
+            d[0] = v.x;
+            d[-SP] = v.y;
+            d[-2 * SP] = v.z;
+            d[-3 * SP] = v.w;
+        }
+    } else {
+        for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
+            const int rho = e >> logG;
+            xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho] = live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
+        }
+    }
+    for (int e = threadIdx.x; e < kChunkZeroRows * SP; e += blockDim.x) xz[e] = 0.f;
+    for (int rho = threadIdx.x; rho < R; rho += blockDim.x)
+        h01[rho] = live(rho) ? make_float2(p.filt[frow(rho)], p.L > 1 ? p.filt[frow(rho) + 1] : 0.f)
+                             : make_float2(0.f, 0.f);
+    if (xseq)
+        for (int e = threadIdx.x; e < G * CH; e += blockDim.x) {
+            const int i = e / CH, j = e % CH;
+            xs[e] = c0 + j < BD ? xseq[(size_t)i * BD + c0 + j] : 0.f;
+        }
+    __syncthreads();
+
+    float *hist = p.buf + (helper ? grow(hrho) + cb : 0);   // a helper row's positions of the chunk
+    if (wave == 0) {
+        // ---- red cells; the helpers do not share this wave's SIMD
+        __builtin_amdgcn_s_setprio(3);
+        chain_run<MT, (MODE & kChunkRec) != 0, (MODE & kChunkTanh) != 0>(
+            p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH);
+    } else if (hw < 0) {
+        // ---- waves 4, 8, 12: barriers only; wave 4 stamps each position's end
+        for (int i = 0; i < G; ++i) {
+            __syncthreads();
+            if (wave == 4 && lane == 0)
+                atomicMax((unsigned long long *)&p.stamps[cb + 1 + i], (unsigned long long)wall_clock64());
+        }
+    } else {
+        // ---- helpers: during position i, the pending sum of slot i+1 but for
+        // its tap-1 term: fft + sum_{k>=2} h[k] x_{i+1-k}.  Tap m of a lane
+        // (k = seg + 8m) reads slot i+1-k at row row0 + 8m.  Taps come in four
+        // groups of eight m; the first nf = (i+2)/64 groups exist in every
+        // lane, the next one in some (its other lanes read the zero rows past
+        // the chunk's first slot), the rest in none.  nf is uniform and picks
+        // a branch-free body, so all of a position's reads are in flight.
+        for (int i = 0; i < G; ++i) {
+            // every 32 positions, the inputs of the last 32 into the history,
+            // for the FFT block at the chunk's end: one whole 128-byte line per
+            // row, 16 bytes per lane (slots i-32+4seg .. +3, from row G-i+31-4seg down)
+            if (helper && i >= 32 && (i & 31) == 0) {
+                const float *src = xp + (size_t)(G - i + 31 - 4 * seg) * SP + hrho;
+                *(float4 *)(hist + i - 32 + 4 * seg) = make_float4(src[0], src[-SP], src[-2 * SP], src[-3 * SP]);
+            }
+            if (i + 1 < G) {
+                const int row0 = G - 2 - i + seg;
+                float acc;
+                switch ((i + 2) >> 6) {
+                    case 0: acc = helper_sum<0>(xp, hreg, row0, hrho); break;
+                    case 1: acc = helper_sum<1>(xp, hreg, row0, hrho); break;
+                    case 2: acc = helper_sum<2>(xp, hreg, row0, hrho); break;
+                    case 3: acc = helper_sum<3>(xp, hreg, row0, hrho); break;
+                    default: acc = helper_sum<4>(xp, hreg, row0, hrho); break;
+                }
+                acc = sum8(acc);
+                if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
+            }
+            __syncthreads();                   // the chain has written slot i
+        }
+    }
+
+    // the remaining inputs into the history: the last 32 slots as above, or
+    // all of a chunk shorter than 32
+    if (helper) {
+        if (G >= 32) {
+            const float *src = xp + (size_t)(31 - 4 * seg) * SP + hrho;   // slot G-32+4seg at row 31-4seg
+            *(float4 *)(hist + G - 32 + 4 * seg) = make_float4(src[0], src[-SP], src[-2 * SP], src[-3 * SP]);
+        } else {
+            for (int sl = seg; sl < G; sl += S) hist[sl] = xp[(size_t)(G - 1 - sl) * SP + hrho];
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const long long n = cb + G;           // published: the FFT block of n reads slot (n-1)&1
+        p.st->pos[(n - 1) & 1] = n - 1;
+        p.st->pos[n & 1] = n;
+    }
+}
+
+}  // namespace fi

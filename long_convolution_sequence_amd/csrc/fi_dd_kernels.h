@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) k_dd_near(DDev q, long long n, const floa
 // Direct products of kDDNearMax < p < pd at position n, one thread per row,
 // after k_dd_near (which stored x_n, h_n).  Both products of a band block go
 // to the same targets.
-__global__ void __launch_bounds__(256) k_dd_wide(DDev q, long long n) {
+static __global__ void __launch_bounds__(256) k_dd_wide(DDev q, long long n) {
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= q.R) return;
     const float *xr = q.xh + (size_t)r * q.L, *hr = q.hh + (size_t)r * q.L;

@@ -30,6 +30,8 @@
 
 namespace fi {
 
+constexpr int kLanes = 64;  // lanes of a wave: one chain per lane, so every access is coalesced
+
 // Positions produced so far, in two slots by parity: the kernels of position
 // n read slot (n-1)&1 (holding n-1) and the last kernel of position n writes n
 // into slot n&1, so no kernel ever reads the slot it may be overwriting.

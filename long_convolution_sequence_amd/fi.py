@@ -114,11 +114,27 @@ def workspace_bytes(M, B, D, L, opt: Options | None = None) -> int:
     return int(load_library().fi_workspace_bytes(M, B, D, L, ctypes.byref(opt) if opt else None))
 
 
-def _dptr(t):
-    """Device pointer of a CUDA tensor (or None)."""
+def _dptr(t, shape=None, device=None, name="tensor", dtypes=None):
+    """Device pointer of a tensor (None passes through), after checking that it
+    is a contiguous tensor on ``device`` with the dtype and exact shape the C
+    call will read or write.  A mismatch raises FiError(FI_EINVAL) instead of
+    letting a kernel run past the buffer."""
     if t is None:
         return None
-    assert t.is_cuda and t.is_contiguous(), "expected a contiguous device tensor"
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise FiError(FI_EINVAL, f"{name}: expected a torch tensor, got {type(t).__name__}")
+    ok = dtypes or (torch.float32,)
+    if t.dtype not in ok:
+        raise FiError(FI_EINVAL, f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in ok)}")
+    if not t.is_cuda:
+        raise FiError(FI_EINVAL, f"{name}: not a device tensor")
+    if device is not None and t.device != device:
+        raise FiError(FI_EINVAL, f"{name}: on {t.device}, the context is on {device}")
+    if not t.is_contiguous():
+        raise FiError(FI_EINVAL, f"{name}: not contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise FiError(FI_EINVAL, f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -146,6 +162,8 @@ class Context:
         opt.defer_wide = int(defer_wide)
         opt.chunk_direct = int(chunk_direct)
         opt.eager_prefill = int(eager_prefill)
+        if getattr(filters, "ndim", 0) != 3:
+            raise FiError(FI_EINVAL, "filters: expected an fp32 [M][D][L] array or tensor")
         if isinstance(filters, np.ndarray):
             f = np.ascontiguousarray(filters, dtype=np.float32)
             fptr = f.ctypes.data_as(ctypes.c_void_p)
@@ -184,13 +202,23 @@ class Context:
         return self._torch.empty(tuple(lead) + (self.B, self.D), dtype=self._torch.float32,
                                  device=self.device)
 
+    def _p(self, t, lead=(), name="tensor"):
+        """Checked device pointer of an fp32 [*lead][B][D] tensor (or None)."""
+        dev = self.device if self.device.index is not None else None
+        p = _dptr(t, tuple(lead) + (self.B, self.D), dev, name)
+        if t is not None and dev is None and t.device.index != self._torch.cuda.current_device():
+            raise FiError(FI_EINVAL, f"{name}: on {t.device}, the context is on the current device")
+        return p
+
     # -- API ----------------------------------------------------------------
     @property
     def position(self) -> int:
         return int(self._lib.fi_position(self._h))
 
     def set_input(self, x0):
-        self._check(self._lib.fi_set_input(self._h, _dptr(x0)))
+        if x0 is None:
+            raise FiError(FI_EINVAL, "x0: required")
+        self._check(self._lib.fi_set_input(self._h, self._p(x0, name="x0")))
 
     def set_defer_wide(self, on):
         """Defer the later sub-blocks of split gray blocks to a second stream (or not)."""
@@ -199,47 +227,54 @@ class Context:
     def step(self, x=None, y=None):
         """One position; x: [B][D] device tensor or None (feedback). Returns y [B][D]."""
         y = self._bd() if y is None else y
-        self._check(self._lib.fi_step(self._h, _dptr(x), _dptr(y)))
+        self._check(self._lib.fi_step(self._h, self._p(x, name="x"), self._p(y, name="y")))
         return y
 
     def prefill(self, x, y=None, want_y=True):
+        if x is None or getattr(x, "ndim", 0) != 3:
+            raise FiError(FI_EINVAL, "x: expected a [P][B][D] device tensor")
         P = int(x.shape[0])
         if want_y and y is None:
             y = self._bd((P,))
-        self._check(self._lib.fi_prefill(self._h, _dptr(x), P, _dptr(y)))
+        self._check(self._lib.fi_prefill(self._h, self._p(x, (P,), "x"), P, self._p(y, (P,), "y")))
         return y
 
     def generate(self, steps, y=None, want_y=True):
+        steps = int(steps)
         if want_y and y is None:
             y = self._bd((steps,))
-        self._check(self._lib.fi_generate(self._h, int(steps), _dptr(y)))
+        self._check(self._lib.fi_generate(self._h, steps, self._p(y, (steps,), "y")))
         return y
 
     def lazy_step(self, x=None, y=None):
         y = self._bd() if y is None else y
-        self._check(self._lib.fi_lazy_step(self._h, _dptr(x), _dptr(y)))
+        self._check(self._lib.fi_lazy_step(self._h, self._p(x, name="x"), self._p(y, name="y")))
         return y
 
     def lazy_generate(self, steps, y=None, want_y=True):
+        steps = int(steps)
         if want_y and y is None:
             y = self._bd((steps,))
-        self._check(self._lib.fi_lazy_generate(self._h, int(steps), _dptr(y)))
+        self._check(self._lib.fi_lazy_generate(self._h, steps, self._p(y, (steps,), "y")))
         return y
 
     def baseline_step(self, kind, x=None, y=None):
         y = self._bd() if y is None else y
-        self._check(self._lib.fi_baseline_step(self._h, int(kind), _dptr(x), _dptr(y)))
+        self._check(self._lib.fi_baseline_step(self._h, int(kind), self._p(x, name="x"), self._p(y, name="y")))
         return y
 
     def baseline_generate(self, kind, steps, y=None, want_y=True):
+        steps = int(steps)
         if want_y and y is None:
             y = self._bd((steps,))
-        self._check(self._lib.fi_baseline_generate(self._h, int(kind), int(steps), _dptr(y)))
+        self._check(self._lib.fi_baseline_generate(self._h, int(kind), steps, self._p(y, (steps,), "y")))
         return y
 
     def layer_red(self, layer, q, y=None):
         y = self._bd() if y is None else y
-        self._check(self._lib.fi_layer_red(self._h, int(layer), _dptr(q), _dptr(y)))
+        if q is None:
+            raise FiError(FI_EINVAL, "q: required")
+        self._check(self._lib.fi_layer_red(self._h, int(layer), self._p(q, name="q"), self._p(y, name="y")))
         return y
 
     def tiles(self):
@@ -250,11 +285,19 @@ class Context:
         device tensors): W [M][D][3D], W1 [M][D][4D], W2 [M][4D][D] (row-major x*W)."""
         if isinstance(W, np.ndarray):
             arrs = [np.ascontiguousarray(a, dtype=np.uint16) for a in (W, W1, W2)]
+            M, D = self.M, self.D
+            for a, shp, nm in zip(arrs, ((M, D, 3 * D), (M, D, 4 * D), (M, 4 * D, D)), ("W", "W1", "W2")):
+                if a.shape != shp:
+                    raise FiError(FI_EINVAL, f"{nm}: shape {a.shape}, expected {shp}")
             ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
             on_dev = 0
         else:
+            import torch
+            M, D = self.M, self.D
+            shapes = ((M, D, 3 * D), (M, D, 4 * D), (M, 4 * D, D))
             arrs = [a.contiguous() for a in (W, W1, W2)]
-            ptrs = [ctypes.c_void_p(a.data_ptr()) for a in arrs]
+            ptrs = [_dptr(a, shp, None, nm, (torch.int16, torch.uint16, torch.bfloat16))
+                    for a, shp, nm in zip(arrs, shapes, ("W", "W1", "W2"))]
             on_dev = 1
         self._check(self._lib.fi_set_block_weights(self._h, *ptrs, on_dev))
 
@@ -264,7 +307,8 @@ class Context:
         count = self.position - first + 1 if count is None else count
         dst = self._torch.empty((max(count, 1), self.B, self.D), dtype=self._torch.float32,
                                 device=self.device)[:count]
-        self._check(self._lib.fi_history(self._h, int(layer), int(what), int(first), int(count), _dptr(dst)))
+        self._check(self._lib.fi_history(self._h, int(layer), int(what), int(first), int(count),
+                                         ctypes.c_void_p(dst.data_ptr())))
         return dst
 
     def stamps(self, first, count):
@@ -371,6 +415,13 @@ class DDContext:
             msg = self._lib.fi_dd_last_error(self._h)
             raise FiError(st, msg.decode() if msg else "")
 
+    def _p(self, t, shape, name):
+        dev = self.device if self.device.index is not None else None
+        p = _dptr(t, shape, dev, name)
+        if t is not None and dev is None and t.device.index != self._torch.cuda.current_device():
+            raise FiError(FI_EINVAL, f"{name}: on {t.device}, the context is on the current device")
+        return p
+
     @property
     def position(self) -> int:
         return int(self._lib.fi_dd_position(self._h))
@@ -378,14 +429,22 @@ class DDContext:
     def step(self, x, h, y=None):
         """One position: x, h [B][D] device tensors; returns y [B][D]."""
         y = self._torch.empty((self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
-        self._check(self._lib.fi_dd_step(self._h, _dptr(x), _dptr(h), _dptr(y)))
+        shp = (self.B, self.D)
+        if x is None or h is None:
+            raise FiError(FI_EINVAL, "x and h are required")
+        self._check(self._lib.fi_dd_step(self._h, self._p(x, shp, "x"), self._p(h, shp, "h"),
+                                         self._p(y, shp, "y")))
         return y
 
     def run(self, x, h, y=None):
         """len(x) positions: x, h [T][B][D] device tensors; returns y [T][B][D]."""
+        if x is None or h is None or getattr(x, "ndim", 0) != 3:
+            raise FiError(FI_EINVAL, "x and h: expected [T][B][D] device tensors")
         T = int(x.shape[0])
         y = self._torch.empty((T, self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
-        self._check(self._lib.fi_dd_run(self._h, _dptr(x), _dptr(h), T, _dptr(y)))
+        shp = (T, self.B, self.D)
+        self._check(self._lib.fi_dd_run(self._h, self._p(x, shp, "x"), self._p(h, shp, "h"), T,
+                                        self._p(y, shp, "y")))
         return y
 
     def reset(self):

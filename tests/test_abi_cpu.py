@@ -142,3 +142,70 @@ def test_dd_calls_reject_bad_arguments_without_a_device(lib):
     assert lib.fi_dd_position(None) == -1
     assert lib.fi_dd_last_error(None) == b"null context"
     assert lib.fi_dd_destroy(None) == fi.FI_OK
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "fi.h"
+
+int main(void) {
+    fi_options o;
+    fi_ctx *c = 0;
+    fi_dd *d = 0;
+    size_t bytes, dd_bytes;
+    fi_status s1, s2;
+    fi_default_options(&o);
+    bytes = fi_workspace_bytes(1, 1, 4, 1024, &o);
+    dd_bytes = fi_dd_workspace_bytes(1, 4, 64, -1);
+    s1 = fi_init(&c, 1, 1, 1, 12, 0, &o, 0, 0);          /* L not a power of two */
+    s2 = fi_dd_init(&d, 1, 4, 48, -1, 0, 0);              /* null workspace */
+    printf("%s|%zu|%zu|%d|%d|%d|%d|%d\n", fi_version(), bytes, dd_bytes, (int)s1, (int)s2,
+           c == 0, d == 0, o.fft_max_log2);
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(lib, tmp_path):
+    """A C11 caller includes fi.h with no HIP header, builds warning-free, links
+    against libfi.so and calls the device-free entry points through it."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(fi.LIB_PATH)
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           str(src), "-L", libdir, "-l:libfi.so", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    ver, nbytes, ddbytes, s1, s2, cnull, dnull, vlog = out.stdout.strip().split("|")
+    assert ver.startswith("fi ")
+    assert int(nbytes) == fi.workspace_bytes(1, 1, 4, 1024, fi.default_options())
+    assert int(ddbytes) == lib.fi_dd_workspace_bytes(1, 4, 64, -1)
+    assert (int(s1), int(s2), int(cnull), int(dnull), int(vlog)) == (fi.FI_EINVAL, fi.FI_EINVAL, 1, 1, 14)
+
+
+def test_binding_rejects_wrong_tensors_before_the_call():
+    """The binding's checks run on the host: a wrong type, dtype or device is an
+    FI_EINVAL error, never a pointer handed to a kernel."""
+    import numpy as np
+    import torch
+    with pytest.raises(fi.FiError) as e:
+        fi._dptr(np.zeros((2, 3), np.float32), (2, 3))
+    assert e.value.status == fi.FI_EINVAL
+    with pytest.raises(fi.FiError) as e:
+        fi._dptr(torch.zeros((2, 3), dtype=torch.float64), (2, 3))
+    assert e.value.status == fi.FI_EINVAL and "dtype" in str(e.value)
+    with pytest.raises(fi.FiError) as e:
+        fi._dptr(torch.zeros((2, 3), dtype=torch.float16), (2, 3))
+    assert e.value.status == fi.FI_EINVAL
+    with pytest.raises(fi.FiError) as e:
+        fi._dptr(torch.zeros((2, 3), dtype=torch.float32), (2, 3))      # host memory
+    assert e.value.status == fi.FI_EINVAL and "device" in str(e.value)
+    assert fi._dptr(None, (2, 3)) is None

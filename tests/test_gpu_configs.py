@@ -28,12 +28,17 @@ def _horizon(h, chans, x_first, steps):
     return (int(over[0]) if over.size else steps), y64, scale
 
 
-def _free_running(ctx_y_last, h, w, chains, steps):
-    """GPU last-layer outputs [steps][B][D] vs the fp64 oracle for sampled chains."""
+def _free_running(ctx_y_last, h, w, chains, steps, min_horizon):
+    """GPU last-layer outputs [steps][B][D] vs the fp64 oracle for sampled chains,
+    over the first half of the fp32/fp64 divergence horizon.  The horizon itself
+    must reach min_horizon: a collapse would otherwise shrink the check to a
+    handful of positions."""
     bs = np.array([k // w.D for k in chains])
     cs = np.array([k % w.D for k in chains])
     x1 = workloads.x_first(w)[bs, cs]
     horizon, y64, scale = _horizon(h, cs, x1, steps)
+    say(f"  fp32/fp64 divergence horizon {horizon} (required >= {min_horizon})")
+    assert horizon >= min_horizon
     gpu = ctx_y_last[:steps, bs, cs].T                          # [nch][steps]
     rel = np.abs(gpu - y64[:, -1, :]).max(axis=0) / scale[-1]
     upto = max(1, horizon // 2)
@@ -78,12 +83,12 @@ def test_small_stack_d256_feedback():
     worst = max(replay_ratio(h[0, c], xs[:, :, c].T, ys[:, :, c].T) for c in rng.choice(w.D, 24, replace=False))
     say(f"  replay worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
-    horizon, rel = _free_running(y, h, w, list(rng.choice(w.D, 8, replace=False)), w.L)
+    horizon, rel = _free_running(y, h, w, list(rng.choice(w.D, 8, replace=False)), w.L, min_horizon=1024)
     say(f"  free-running: fp32/fp64 horizon {horizon}, GPU rel error before half of it {rel:.2e}")
     assert rel <= 1e-3
 
 
-def _stack_feedback_case(idx, replay_layers, prefix, points=None):
+def _stack_feedback_case(idx, replay_layers, prefix, min_horizon, points=None):
     w = workloads.WORKLOADS[idx]
     say(f"case {w.name} feedback (record)")
     t0 = time.time()
@@ -118,16 +123,11 @@ def _stack_feedback_case(idx, replay_layers, prefix, points=None):
         say(f"  replay worst error/tolerance {worst:.3e}")
         assert worst <= 1.0
     chains = list(rng.choice(w.B * w.D, 4, replace=False))
-    horizon, rel = _free_running(y, h, w, chains, prefix)
+    horizon, rel = _free_running(y, h, w, chains, prefix, min_horizon)
     say(f"  free-running over {prefix} positions: fp32/fp64 horizon {horizon}, GPU rel error {rel:.2e}")
     assert rel <= 1e-3
 
 
 def test_stack_18x4x768_feedback():
     """18 layers, B=4, D=768, L=2^15, h ~ N(0,1) exp(-8k/L), tanh map and feedback."""
-    _stack_feedback_case(3, replay_layers=(0, 9, 17), prefix=2048)
-
-
-def test_stack_18x1x864_L131072_feedback():
-    """18 layers, B=1, D=864, L=2^17, h ~ N(0,1) exp(-k/16384)/sqrt(L) (contracting)."""
-    _stack_feedback_case(4, replay_layers=(0, 17), prefix=8192, points=400)
+    _stack_feedback_case(3, replay_layers=(0, 9, 17), prefix=2048, min_horizon=256)

@@ -2,7 +2,8 @@
 twice that width (two halves in one workgroup) and the wider classes (split
 into K sub-blocks with offset-tap spectra), against the CPU oracle at sampled
 positions of full-length rows; and the deferred later sub-blocks of split
-blocks (defer_wide), which must change no bit of any output."""
+blocks (defer_wide): the deferred run replays against the oracle and equals
+the undeferred run bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -70,13 +71,31 @@ def test_deferred_split_sub_blocks_change_nothing(graphs):
     h = (rng.standard_normal((M, D, L)) * np.exp(-np.arange(L) / 4096.0) / np.sqrt(L)).astype(np.float32)
     x1 = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).cuda()
     outs = []
+    worst = 0.0
     for defer in (False, True):
         with fi.Context(torch.from_numpy(h).cuda(), B, tau_split=6, fft_max_log2=12, use_graphs=graphs,
-                        defer_wide=defer) as ctx:
+                        defer_wide=defer, record=defer) as ctx:
             ctx.set_input(x1)
             a = ctx.generate(16384 + 100)          # stops 100 positions into the first deferral
             b = torch.stack([ctx.step() for _ in range(200)])
             c = ctx.generate(L - 16384 - 300)
             outs.append(torch.cat([a, b, c]).cpu().numpy())
+            if defer:
+                # the deferred run itself against the oracle: every layer, every (b, c), replayed
+                # from its recorded inputs at the ends of every dyadic range (where the split
+                # classes' output sub-blocks start and end) and at random positions
+                ts = _positions(L, rng, 200)
+                ts = np.unique(np.concatenate([ts, np.arange(16384, L, 4096) - 1, np.arange(16384, L, 4096)]))
+                for l in range(M):
+                    xs = ctx.history(l, 0).cpu().numpy()
+                    ys = ctx.history(l, 1).cpu().numpy()
+                    for bb in range(B):
+                        for cc in range(D):
+                            xrow = np.ascontiguousarray(xs[:, bb, cc])
+                            ref = oracle.conv_points(h[l, cc], xrow, ts)
+                            tol = TF_TOL * np.abs(h[l, cc].astype(np.float64)).sum() * np.abs(xrow).max()
+                            worst = max(worst, float(np.abs(ys[ts, bb, cc] - ref).max() / tol))
+    say(f"  deferred run vs oracle (replay at {len(ts)} positions): worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
     assert np.array_equal(outs[0], outs[1])
     assert np.abs(outs[0]).max() > 0
