@@ -232,6 +232,20 @@ fi_status fi_history(const fi_ctx *ctx, int layer, int what, int64_t first, int6
 fi_status fi_set_block_weights(fi_ctx *ctx, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
                                int on_device);
 
+/* fi_set_block_weights for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same upload and the same result, but the staging buffer the
+ * weights pass through on their way to the transposed layout is a fixed
+ * device array of the library (8 MiB per device, taken when the first call on
+ * a device looks up its address) instead of an allocation; no hipMalloc,
+ * hipFree or other allocating call is made.  Limit: 4*D*D 16-bit values must
+ * fit the array, i.e. D <= 1024 (FI_EINVAL with a message otherwise).  Every
+ * call on one device shares that device's array and leaves its contents there:
+ * calls that overlap on one device (other streams or threads) race.
+ * Synchronises the stream, like fi_set_block_weights. */
+fi_status fi_set_block_weights_static(fi_ctx *ctx, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
+                                      int on_device);
+
 /* Device wall-clock stamps (100 MHz counter ticks) written when each position
  * finished: dst (host int64 [count]) receives the stamps of positions
  * first..first+count-1.  Synchronises the stream. */

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1093,6 +1094,68 @@ fi_status fi_step(fi_ctx *c, const float *x_t, float *y_t) {
 
 namespace {
 
+// ---- block weights ---------------------------------------------------------
+
+// Elements of the staging buffer the weight upload goes through: the widest
+// part of one layer, W1 [D][4D] or W2 [4D][D].
+size_t block_stage_elems(int D) { return (size_t)4 * D * D; }
+
+// Copy one layer's part at a time into `stage` (device, block_stage_elems(D)
+// 16-bit values), then transpose it into the context's weight area; ends with
+// a synchronisation of the stream.
+fi_status load_block_weights(fi_ctx *c, const uint16_t *W, const uint16_t *W1, const uint16_t *W2, int on_device,
+                             unsigned short *stage) {
+    const int D = c->D, M = c->M;
+    struct Part { const uint16_t *src; unsigned short *dst; int rows, cols; };
+    const Part parts[3] = {{W, const_cast<unsigned short *>(c->dev.Wt), D, 3 * D},
+                           {W1, const_cast<unsigned short *>(c->dev.W1t), D, 4 * D},
+                           {W2, const_cast<unsigned short *>(c->dev.W2t), 4 * D, D}};
+    hipError_t e = hipSuccess;
+    for (int pi = 0; pi < 3 && e == hipSuccess; ++pi) {
+        const Part &pt = parts[pi];
+        const size_t per = (size_t)pt.rows * pt.cols;
+        for (int l = 0; l < M && e == hipSuccess; ++l) {
+            e = hipMemcpyAsync(stage, pt.src + l * per, per * sizeof(unsigned short),
+                               on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, c->stream);
+            if (e != hipSuccess) break;
+            hipLaunchKernelGGL(k_transpose16, dim3((pt.cols + 31) / 32, (pt.rows + 31) / 32), dim3(256), 0,
+                               c->stream, stage, pt.dst + l * per, pt.rows, pt.cols);
+            e = hipGetLastError();
+        }
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail(c, FI_EDEVICE, std::string("block weights: ") + hipGetErrorString(e));
+    c->weights_set = true;
+    return FI_OK;
+}
+
+// Staging for fi_set_block_weights_static: a fixed device array instead of an
+// allocation.  In host code `scratch` only names the symbol; its device
+// address, one per device, comes from hipGetSymbolAddress and is kept here.
+// Every call on a device shares that device's array: calls that overlap on one
+// device (different streams or threads) race.
+constexpr size_t kStaticStageBytes = size_t(8) << 20;
+constexpr size_t kStaticStageElems = kStaticStageBytes / sizeof(unsigned short);
+static __device__ __align__(256) unsigned short scratch[kStaticStageElems];
+constexpr int kMaxDevices = 64;
+std::mutex g_stage_mu;
+void *g_stage_ptr[kMaxDevices] = {nullptr};
+
+fi_status static_stage(fi_ctx *c, unsigned short **out) {
+    int dev = -1;
+    HIPCK(c, hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(c, FI_EDEVICE, "device index out of range for the static scratch");
+    std::lock_guard<std::mutex> lock(g_stage_mu);
+    if (!g_stage_ptr[dev]) {
+        void *ptr = nullptr;
+        HIPCK(c, hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return fail(c, FI_EDEVICE, "hipGetSymbolAddress returned no address for the static scratch");
+        g_stage_ptr[dev] = ptr;
+    }
+    *out = (unsigned short *)g_stage_ptr[dev];
+    return FI_OK;
+}
+
 // Whether fi_prefill may take the eager path (see fi_options.eager_prefill).
 bool eager_prefill_ok(const fi_ctx *c, int64_t P) {
     const int64_t G = c->dev.G;
@@ -1262,32 +1325,28 @@ fi_status fi_set_block_weights(fi_ctx *c, const uint16_t *W, const uint16_t *W1,
     if (s != FI_OK) return s;
     if (c->opt.map != FI_MAP_HYENA) return fail(c, FI_ESTATE, "block weights need FI_MAP_HYENA");
     if (!W || !W1 || !W2) return FI_EINVAL;
-    const int D = c->D, M = c->M;
-    const size_t DD = (size_t)D * D;
     unsigned short *tmp = nullptr;
-    HIPCK(c, hipMalloc((void **)&tmp, 4 * DD * sizeof(unsigned short)));
-    struct Part { const uint16_t *src; unsigned short *dst; int rows, cols; };
-    const Part parts[3] = {{W, const_cast<unsigned short *>(c->dev.Wt), D, 3 * D},
-                           {W1, const_cast<unsigned short *>(c->dev.W1t), D, 4 * D},
-                           {W2, const_cast<unsigned short *>(c->dev.W2t), 4 * D, D}};
-    hipError_t e = hipSuccess;
-    for (int pi = 0; pi < 3 && e == hipSuccess; ++pi) {
-        const Part &pt = parts[pi];
-        const size_t per = (size_t)pt.rows * pt.cols;
-        for (int l = 0; l < M && e == hipSuccess; ++l) {
-            e = hipMemcpyAsync(tmp, pt.src + l * per, per * sizeof(unsigned short),
-                               on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, c->stream);
-            if (e != hipSuccess) break;
-            hipLaunchKernelGGL(k_transpose16, dim3((pt.cols + 31) / 32, (pt.rows + 31) / 32), dim3(256), 0,
-                               c->stream, tmp, pt.dst + l * per, pt.rows, pt.cols);
-            e = hipGetLastError();
-        }
-    }
-    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    HIPCK(c, hipMalloc((void **)&tmp, block_stage_elems(c->D) * sizeof(unsigned short)));
+    s = load_block_weights(c, W, W1, W2, on_device, tmp);
     (void)hipFree(tmp);
-    if (e != hipSuccess) return fail(c, FI_EDEVICE, std::string("block weights: ") + hipGetErrorString(e));
-    c->weights_set = true;
-    return FI_OK;
+    return s;
+}
+
+fi_status fi_set_block_weights_static(fi_ctx *c, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
+                                      int on_device) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if (c->opt.map != FI_MAP_HYENA) return fail(c, FI_ESTATE, "block weights need FI_MAP_HYENA");
+    if (!W || !W1 || !W2) return FI_EINVAL;
+    if (block_stage_elems(c->D) > kStaticStageElems)
+        return fail(c, FI_EINVAL,
+                    "fi_set_block_weights_static: D = " + std::to_string(c->D) + " needs " +
+                        std::to_string(block_stage_elems(c->D) * sizeof(unsigned short)) +
+                        " bytes of staging, more than the " + std::to_string(kStaticStageBytes) +
+                        " of the static scratch (D <= 1024)");
+    unsigned short *stage = nullptr;
+    if ((s = static_stage(c, &stage)) != FI_OK) return s;
+    return load_block_weights(c, W, W1, W2, on_device, stage);
 }
 
 fi_status fi_stamps(fi_ctx *c, int64_t first, int64_t count, int64_t *dst) {

@@ -85,6 +85,7 @@ def load_library():
         "fi_baseline_generate": (I, [P, I, I64, P]),
         "fi_baseline_time": (I, [P, I, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_set_block_weights": (I, [P, P, P, P, I]),
+        "fi_set_block_weights_static": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_dd_workspace_bytes": (S, [I, I, I64, I]),
@@ -280,7 +281,12 @@ class Context:
     def tiles(self):
         self._check(self._lib.fi_tiles(self._h))
 
-    def set_block_weights(self, W, W1, W2):
+    def set_block_weights_static(self, W, W1, W2):
+        """set_block_weights staged through the library's fixed device array (fi_set_block_weights_static:
+        no device allocation; D <= 1024)."""
+        self.set_block_weights(W, W1, W2, _fn="fi_set_block_weights_static")
+
+    def set_block_weights(self, W, W1, W2, _fn="fi_set_block_weights"):
         """Hyena-style block weights as bf16 bit patterns (uint16 numpy arrays or int16/uint16
         device tensors): W [M][D][3D], W1 [M][D][4D], W2 [M][4D][D] (row-major x*W)."""
         if isinstance(W, np.ndarray):
@@ -299,7 +305,7 @@ class Context:
             ptrs = [_dptr(a, shp, None, nm, (torch.int16, torch.uint16, torch.bfloat16))
                     for a, shp, nm in zip(arrs, shapes, ("W", "W1", "W2"))]
             on_dev = 1
-        self._check(self._lib.fi_set_block_weights(self._h, *ptrs, on_dev))
+        self._check(getattr(self._lib, _fn)(self._h, *ptrs, on_dev))
 
     def history(self, layer, what, count=None, first=1):
         """[count][B][D] device tensor of positions first.. : what=0 layer (convolution) inputs,
