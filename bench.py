@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--no-prefill-leg", action="store_true", help="skip the prefill timing")
     ap.add_argument("--no-dd-leg", action="store_true", help="skip the data-dependent-filter timing")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
+    ap.add_argument("--tau-split", type=int, default=-1,
+                    help="first FFT block class (log2 U) instead of the calibrated choice; chunks are that long")
     ap.add_argument("--traffic-run", action="store_true",
                     help="launch each FFT class once and a calibration copy (run under rocprofv3 --pmc)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -257,7 +259,7 @@ def main():
     h = workloads.filters(w)
     hdev = torch.from_numpy(h).cuda()
     x1 = torch.from_numpy(workloads.x_first(w)).cuda()
-    ctx = fi.Context(hdev, w.B, time_blocks=True)
+    ctx = fi.Context(hdev, w.B, time_blocks=True, tau_split=args.tau_split)
     del hdev
     tau = ctx.tau_table()
     log("bench: block paths", [(q, "fft" if p == fi.PATH_FFT else "direct") for (q, p, _, _) in tau])
@@ -319,9 +321,19 @@ def main():
     chunk = None
     if chunk_n:
         avg_us = chunk_ms * 1e3 / chunk_n
+        # per-position latency inside chunks, by the position's place in its chunk
+        # (r = 2 .. G: a chunk's first position follows the FFT block before it)
+        r = (npos - 1) % G + 1
+        win = max(1, G // 8)
+        by_place = {}
+        for a in range(0, G, win):
+            sel = (r > max(a, 1)) & (r <= a + win)
+            if sel.any():
+                by_place[f"{max(a, 1) + 1}-{a + win}"] = round(float(np.median(lat[sel])), 3)
         chunk = {"kernel": "k_chunk (red cells and direct gray blocks of a chunk of positions)",
                  "launches": int(chunk_n), "positions_per_launch": G,
                  "avg_launch_us": round(avg_us, 2), "us_per_position": round(avg_us / G, 4),
+                 "median_us_by_place_in_chunk": by_place,
                  "share_of_step_time": round(chunk_ms * 1e-3 / total, 4),
                  "fft_share_of_step_time": round(tot_ms * 1e-3 / total, 4),
                  "bound": "latency: the serial red-cell chain (M layers of fma + tanh per position) "

@@ -179,28 +179,77 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
+// Lags of a chunk split between the two kinds of helper work: a lane's taps
+// m < kChunkPullTaps (lags k = seg + 8m below 8 kChunkPullTaps) are pulled,
+// target by target, one position ahead; taps m >= kChunkPullTaps (the longer
+// lags, only in chunks longer than 8 kChunkPullTaps) are pushed from each
+// source one position after it is known.
+constexpr int kChunkPullTaps = 24;
+static_assert(kChunkPullTaps % 8 == 0 && kChunkPullTaps <= kChunkTaps, "pulled taps come in groups of eight");
+
+// f(std::integral_constant<int, v>) for the v in [0, N] equal to the runtime
+// value (uniform over the wave: a scalar branch to a body with fixed offsets).
+template <int N, int V = 0, typename F>
+__device__ __forceinline__ void dispatch(int v, F &&f) {
+    if constexpr (V < N) {
+        if (v == V) {
+            f(std::integral_constant<int, V>{});
+            return;
+        }
+        dispatch<N, V + 1>(v, f);
+    } else {
+        f(std::integral_constant<int, N>{});
+    }
+}
+
 // A helper lane's partial sum over its taps m < 8 (NF + 1) (tap m: slot row
-// row0 + 8m, register hreg[m]).  Taps of group NF that lie before the
-// chunk's first slot read the zero rows after the slots (rows G .. G+63:
-// with NF = (i+2)/64, row0 + 8m never passes G+63), so every tap is a plain
-// read at a fixed offset.
+// row0 + 8m, register hreg[m]).  Taps of group NF that lie before the chunk's
+// first slot read the zero rows after the slots (rows G .. G+63: with
+// NF = min((i+2)/64, kChunkPullTaps/8 - 1), row0 + 8m never passes G+63), so
+// every tap is a plain read at a fixed offset.
 template <int NF>
 __device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho) {
     constexpr int S = 8, SP = kChunkSlot;
-    constexpr int NT = NF < 4 ? 8 * (NF + 1) : 32;
+    constexpr int NT = 8 * (NF + 1);
+    static_assert(NT <= kChunkPullTaps, "pulled taps");
     float v[NT];
     const float *base = xp + (size_t)row0 * SP + hrho;
-    // taps 16..31 from a second base 16 taps on: read in pairs, two taps
-    // apart by 15 x 256 bytes, the offsets from one base stop at 64 KB.  The
-    // empty asm keeps the compiler from folding the two bases back into one.
-    int off1 = row0 * SP + hrho + 16 * S * SP;
-    asm volatile("" : "+v"(off1));
 #pragma unroll
-    for (int m = 0; m < NT; ++m) v[m] = m < 16 ? base[(size_t)m * S * SP] : xp[off1 + (m - 16) * S * SP];
+    for (int m = 0; m < NT; ++m) v[m] = base[(size_t)m * S * SP];
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NT; ++m) acc[m & 3] = fmaf(hreg[m], v[m], acc[m & 3]);
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// A helper lane's push of the source x (slot i-1, known from position i on)
+// into the pending sums of its targets t = i-1 + seg + 8m for its pushed taps
+// m = kChunkPullTaps .. kChunkPullTaps+C-1, which lie inside the chunk in every
+// lane (target of tap m at row rowp - 8 (m - kChunkPullTaps)), and for tap
+// m = kChunkPullTaps+C where its row is still a slot (row >= 0: this lane's
+// target inside the chunk).  C is uniform over the wave, so the reads and
+// writes are plain accesses at fixed offsets.  Each target belongs to one
+// lane of its row (its lag fixes seg and m), so no two lanes update one sum.
+template <int C>
+__device__ __forceinline__ void helper_push(float *xp, const float *hreg, int rowp, int hrho, float x) {
+    constexpr int S = 8, SP = kChunkSlot, P = kChunkPullTaps;
+    if constexpr (C > 0) {
+        // from the lowest row up, so that every access is the base plus a
+        // non-negative immediate (rows 8 apart: pairs of 15 x 256 bytes)
+        float *b = xp + (size_t)(rowp - S * (C - 1)) * SP + hrho;
+        float v[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) v[c] = b[(size_t)(C - 1 - c) * S * SP];
+#pragma unroll
+        for (int c = 0; c < C; ++c) b[(size_t)(C - 1 - c) * S * SP] = fmaf(hreg[P + c], x, v[c]);
+    }
+    if constexpr (P + C < kChunkTaps) {
+        const int r = rowp - S * C;
+        if (r >= 0) {
+            float *d = xp + (size_t)r * SP + hrho;
+            *d = fmaf(hreg[P + C], x, *d);
+        }
+    }
 }
 
 template <int MT, int MODE>
@@ -298,13 +347,18 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
                 atomicMax((unsigned long long *)&p.stamps[cb + 1 + i], (unsigned long long)wall_clock64());
         }
     } else {
-        // ---- helpers: during position i, the pending sum of slot i+1 but for
-        // its tap-1 term: fft + sum_{k>=2} h[k] x_{i+1-k}.  Tap m of a lane
-        // (k = seg + 8m) reads slot i+1-k at row row0 + 8m.  Taps come in four
-        // groups of eight m; the first nf = (i+2)/64 groups exist in every
-        // lane, the next one in some (its other lanes read the zero rows past
-        // the chunk's first slot), the rest in none.  nf is uniform and picks
-        // a branch-free body, so all of a position's reads are in flight.
+        // ---- helpers, during position i.  Pull: the pending sum of slot i+1
+        // but for its tap-1 term, over lags 2 .. K-1 (K = 8 kChunkPullTaps):
+        // fft + sum h[k] x_{i+1-k} (the pushes below have added the lags from
+        // K on by then).  Tap m of a lane (k = seg + 8m) reads slot i+1-k at
+        // row row0 + 8m; taps come in groups of eight m, a new group from
+        // i = 62, 126, ... on (its other lanes then read the zero rows past
+        // the chunk's first slot).  Push (chunks longer than K): the source
+        // x_{i-1}, now final, times lags K .. 255 into the targets
+        // i-1+K .. 255.  Pulling every lag would leave position i with i taps
+        // per row, the last positions of a chunk with 255; split this way the
+        // pulled lags stop growing at K-1 and the pushed ones shrink as the
+        // chunk proceeds (a push costs a read and a write per tap).
         for (int i = 0; i < G; ++i) {
             // every 32 positions, the inputs of the last 32 into the history,
             // for the FFT block at the chunk's end: one whole 128-byte line per
@@ -315,16 +369,21 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, in
             }
             if (i + 1 < G) {
                 const int row0 = G - 2 - i + seg;
-                float acc;
-                switch ((i + 2) >> 6) {
-                    case 0: acc = helper_sum<0>(xp, hreg, row0, hrho); break;
-                    case 1: acc = helper_sum<1>(xp, hreg, row0, hrho); break;
-                    case 2: acc = helper_sum<2>(xp, hreg, row0, hrho); break;
-                    case 3: acc = helper_sum<3>(xp, hreg, row0, hrho); break;
-                    default: acc = helper_sum<4>(xp, hreg, row0, hrho); break;
-                }
+                float acc = 0.f;
+                dispatch<kChunkPullTaps / 8 - 1>(min((i + 2) >> 6, kChunkPullTaps / 8 - 1), [&](auto nf) {
+                    acc = helper_sum<decltype(nf)::value>(xp, hreg, row0, hrho);
+                });
                 acc = sum8(acc);
                 if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
+            }
+            if (G > 8 * kChunkPullTaps && i >= 1 && i <= G - 8 * kChunkPullTaps && helper) {
+                const float x = xp[(size_t)(G - i) * SP + hrho];             // slot i-1
+                const int rowp = G - i - seg - 8 * kChunkPullTaps;             // target of the first pushed tap
+                // pushed taps present in every lane of the wave: m <= (G-i-7)/8
+                const int c = min(kChunkTaps - kChunkPullTaps, max(0, ((G - i - 7) >> 3) - kChunkPullTaps + 1));
+                dispatch<kChunkTaps - kChunkPullTaps>(c, [&](auto cc) {
+                    helper_push<decltype(cc)::value>(xp, hreg, rowp, hrho, x);
+                });
             }
             __syncthreads();                   // the chain has written slot i
         }

@@ -86,29 +86,31 @@ __device__ __forceinline__ float apply_map(int kind, float y) { return kind == 0
 // tanh without branches, for the red-cell chains (the critical path of a
 // chunk of positions).  |y| >= 0.8: 1 - 2 / (e^{2|y|} + 1), with e^{2|y|}
 // from the hardware base-2 exponential and the reciprocal.  |y| < 0.8, where
-// that difference cancels: |y| + |y|^3 P(|y|^2), P of degree 5 fitted for
-// least relative error (Lawson's iteratively reweighted least squares, in
-// double on Chebyshev nodes; coefficients rounded to float): under 0.9 ulp.
-// Both are evaluated and one selected, so lanes on either side never diverge.
-__device__ __forceinline__ float tanh_odd_poly(float a) {   // |y| + |y|^3 P(|y|^2), a = |y|
-    const float s = a * a;
-    float q = fmaf(s, 0.0015847263857722282f, -0.007409499958157539f);
-    q = fmaf(s, q, 0.021302949637174606f);
-    q = fmaf(s, q, -0.05385231971740723f);
-    q = fmaf(s, q, 0.13332220911979675f);
-    q = fmaf(s, q, -0.33333298563957214f);
-    return fmaf(a * s, q, a);
+// that difference cancels: y + y^3 P(y^2), P of degree 5 fitted for least
+// relative error (Lawson's iteratively reweighted least squares, in double on
+// Chebyshev nodes; coefficients rounded to float).  P is evaluated in Estrin's
+// scheme and the result formed in y itself (odd, so no sign fix-up): from y to
+// the result is six dependent operations (y*y, its square, two fma levels of
+// P, the final fma), against nine in Horner's form, which matters because a
+// chain runs one tanh per layer back to back.  Error under 1 ulp.  Both halves
+// are evaluated and one selected, so lanes on either side never diverge.
+__device__ __forceinline__ float tanh_small(float y) {   // y + y^3 P(y^2); meaningful for |y| < 0.8
+    const float s = y * y;
+    const float s2 = s * s;
+    const float p01 = fmaf(s, 0.13332220911979675f, -0.33333298563957214f);
+    const float p23 = fmaf(s, 0.021302949637174606f, -0.05385231971740723f);
+    const float p45 = fmaf(s, 0.0015847263857722282f, -0.007409499958157539f);
+    const float q = fmaf(fmaf(p45, s2, p23), s2, p01);
+    return fmaf(y * s, q, y);
 }
+// The full tanh: equal to tanh_small(y) for |y| < 0.8 (bit for bit).
 __device__ __forceinline__ float tanh_chain(float y) {
     const float a = fabsf(y);
     const float e = __builtin_amdgcn_exp2f(a * 2.88539008f);      // e^{2a} = 2^{2a log2(e)}
-    const float big = fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
-    const float small = tanh_odd_poly(a);
-    return copysignf(a < 0.8f ? small : big, y);
+    const float big = copysignf(fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f), y);
+    const float small = tanh_small(y);
+    return a < 0.8f ? small : big;
 }
-// The polynomial half alone: equal to tanh_chain(y) for |y| < 0.8 (bit for
-// bit), meaningless above.
-__device__ __forceinline__ float tanh_small(float y) { return copysignf(tanh_odd_poly(fabsf(y)), y); }
 
 __device__ __forceinline__ size_t act_row(const Dev &p, int l, int b, int c) {
     return ((size_t)((size_t)l * p.B + b) * p.D + c) * (size_t)p.L;
