@@ -219,6 +219,80 @@ def traffic_summary(args):
     print(json.dumps(out, indent=1))
 
 
+def hyena_run(w, positions, warm=512):
+    """One free-running generation of the Hyena-style block workload (projection,
+    gate, mixer, GELU MLP, RMSNorm, tanh feedback), end to end, and the split of
+    its time between the mixer and the block: the block kernels of one position
+    are timed alone with HIP events (fi_time_hyena_block), the mixer's share is
+    the rest of the generation."""
+    import torch
+
+    from long_convolution_sequence_amd import fi, workloads
+
+    h = workloads.filters(w)
+    bits = workloads.hyena_weights(w)
+    x1 = torch.from_numpy(workloads.x_first(w)).cuda()
+    hc = fi.Context(torch.from_numpy(h).cuda(), w.B, map=fi.MAP_HYENA)
+    del h
+    hc.set_block_weights(bits["W"], bits["W1"], bits["W2"])
+    hc.set_input(x1)
+    hc.generate(min(positions, warm), want_y=False)            # warm-up (graphs, caches)
+    hc.reset()
+    hc.set_input(x1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hc.generate(positions, want_y=False)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = hc.stamps(1, positions).astype(np.float64)
+    lat = np.diff(st) / 100.0
+    block_us = hc.time_hyena_block(reps=20)
+    paths = [p for (_, p, _, _) in hc.tau_table()]
+    hc.close()
+    del hc
+    torch.cuda.empty_cache()
+    block_s = positions * block_us * 1e-6
+    return {
+        "workload": w.name, "positions": positions,
+        "e2e_s": round(dt, 4), "e2e_tokens_per_s": round(positions * w.B / dt, 1),
+        "block_us_per_position": round(block_us, 2),
+        "block_share": round(min(1.0, block_s / dt), 4),
+        "mixer_s": round(max(0.0, dt - block_s), 4),
+        "mixer_tokens_per_s": round(positions * w.B / max(dt - block_s, 1e-9), 1),
+        "latency_us": {"p50": round(float(np.percentile(lat, 50)), 2),
+                       "p99": round(float(np.percentile(lat, 99)), 2),
+                       "max": round(float(lat.max()), 1)},
+        "block_paths": ["fft" if p == fi.PATH_FFT else "direct" for p in paths],
+        "note": "free-running generation from position 0 (graphs per block-size class); block time = "
+                "positions x the event-timed block kernels of one position (projections with the red "
+                "cells, GELU MLP, RMSNorm, output), mixer time = the rest (gray blocks and launches)",
+    }
+
+
+def pareto(w, h, split, reps=8):
+    """Per block size, the device time of one launch of each gray-block path at the
+    real shape (the pages' runtime-per-tile-size comparison): the direct kernel
+    (one launch per position, red cells included) where it exists (U <= 128),
+    the FFT kernels where they exist (U >= 4)."""
+    import torch
+
+    from long_convolution_sequence_amd import fi
+
+    pc = fi.Context(torch.from_numpy(h).cuda(), w.B, tau_split=split, use_graphs=False)
+    rows = []
+    for q in range(w.P):
+        row = {"U": 1 << q}
+        if q <= 7:
+            row["direct_us"] = round(pc.time_block(q, fi.PATH_DIRECT, reps=reps), 2)
+        if q >= 2:
+            row["fft_us"] = round(pc.time_block(q, fi.PATH_FFT, reps=2 if q >= 14 else reps), 2)
+        rows.append(row)
+    pc.close()
+    del pc
+    torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +304,10 @@ def main():
     ap.add_argument("--no-defer-leg", action="store_true", help="skip the generation with deferred split blocks")
     ap.add_argument("--no-prefill-leg", action="store_true", help="skip the prefill timing")
     ap.add_argument("--no-dd-leg", action="store_true", help="skip the data-dependent-filter timing")
+    ap.add_argument("--no-pareto-leg", action="store_true", help="skip the per-size path timing")
+    ap.add_argument("--no-hyena-leg", action="store_true", help="skip the Hyena-style block workload leg")
+    ap.add_argument("--hyena-positions", type=int, default=4096,
+                    help="positions of the Hyena-style block leg (the whole L with --workload 5)")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
     ap.add_argument("--tau-split", type=int, default=-1,
                     help="first FFT block class (log2 U) instead of the calibrated choice; chunks are that long")
@@ -255,44 +333,47 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     L = args.positions or w.L
+    if w.block == "hyena":
+        # the Hyena-style block workload end to end (its own line)
+        hy = hyena_run(w, L)
+        log(f"bench: {w.name}: {hy['e2e_tokens_per_s']:,.0f} tokens/s end to end, block share {hy['block_share']}")
+        out = {"metric": "end-to-end tokens/sec + mixer/block time split (Hyena-style block, L=2^15)",
+               "value": hy["e2e_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": 1, "warmup": 1,
+               "ms_per_step": round(hy["e2e_s"] * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "f32 (bf16 weights)",
+               "data": "synthetic (seeded random filters, block weights and first input, recipe in DESIGN.md)",
+               "config": {"workload": w.name, "M": w.M, "B": w.B, "D": w.D, "L": L}, "hyena": hy}
+        print(json.dumps(out), flush=True)
+        return
     log(f"bench: {w.name}, generating inputs")
     h = workloads.filters(w)
     hdev = torch.from_numpy(h).cuda()
     x1 = torch.from_numpy(workloads.x_first(w)).cuda()
-    ctx = fi.Context(hdev, w.B, time_blocks=True, tau_split=args.tau_split)
-    del hdev
+    # the production path: graphs of whole chunks and of their FFT gray blocks,
+    # no per-kernel events
+    ctx = fi.Context(hdev, w.B, tau_split=args.tau_split)
     tau = ctx.tau_table()
+    split = next((q for (q, pth, _, _) in tau if pth == fi.PATH_FFT), w.P)
     log("bench: block paths", [(q, "fft" if p == fi.PATH_FFT else "direct") for (q, p, _, _) in tau])
 
-    def one_step():
-        ctx.reset()
-        ctx.set_input(x1)
+    def one_step(c):
+        c.reset()
+        c.set_input(x1)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ctx.generate(L, want_y=False)
+        c.generate(L, want_y=False)
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
     for i in range(args.warmup):
-        dt = one_step()
+        dt = one_step(ctx)
         log(f"bench: warmup {i + 1}/{args.warmup}: {dt:.3f}s")
-    ctx.block_times(clear=True)
-    ctx.chunk_times(clear=True)
     times, lat = [], []
-    chunk_ms, chunk_n = 0.0, 0
-    blk_ms = np.zeros(w.P)
-    blk_n = np.zeros(w.P, dtype=np.int64)
     for i in range(args.steps):
-        dt = one_step()
+        dt = one_step(ctx)
         times.append(dt)
         st = ctx.stamps(1, L).astype(np.float64)
         lat.append(np.diff(st) / 100.0)              # 100 MHz ticks -> us; positions 2..L
-        for q, ms, cnt in ctx.block_times(clear=True):
-            blk_ms[q] += ms
-            blk_n[q] += cnt
-        cms, cn = ctx.chunk_times(clear=True)
-        chunk_ms += cms
-        chunk_n += cn
         log(f"bench: step {i + 1}/{args.steps}: {dt:.3f}s ({L * w.B / dt:,.0f} tokens/s)")
     total = float(np.sum(times))
     value = L * w.B * args.steps / total
@@ -302,7 +383,34 @@ def main():
     cls = np.tile(cls, args.steps)
     per_class = {int(q): round(float(np.median(lat[cls == q])), 2) for q in np.unique(cls)}
 
-    # FFT gray-block roofline over the timed steps
+    # Kernel durations for the roofline: the same generation, with every chunk
+    # and FFT gray-block launch bracketed by HIP events that the dispatch
+    # itself stamps (direct launches: events cannot be stamped inside graphs).
+    # The kernels are the same; only the launches between them differ.
+    ev_steps = max(2, min(args.steps, 4))
+    ectx = fi.Context(hdev, w.B, time_blocks=True, tau_split=split)
+    one_step(ectx)
+    ectx.block_times(clear=True)
+    ectx.chunk_times(clear=True)
+    ev_times = []
+    chunk_ms, chunk_n = 0.0, 0
+    blk_ms = np.zeros(w.P)
+    blk_n = np.zeros(w.P, dtype=np.int64)
+    for i in range(ev_steps):
+        ev_times.append(one_step(ectx))
+        for q, ms, cnt in ectx.block_times(clear=True):
+            blk_ms[q] += ms
+            blk_n[q] += cnt
+        cms, cn = ectx.chunk_times(clear=True)
+        chunk_ms += cms
+        chunk_n += cn
+    ev_total = float(np.sum(ev_times))
+    log(f"bench: {ev_steps} event-timed generations: {L * w.B * ev_steps / ev_total:,.0f} tokens/s")
+    ectx.close()
+    del ectx, hdev
+    torch.cuda.empty_cache()
+
+    # FFT gray-block roofline over the event-timed generations
     rows = []
     tot_bytes = tot_ms = 0.0
     for q in range(w.P):
@@ -317,25 +425,40 @@ def main():
         tot_ms += blk_ms[q]
     launches = int(blk_n.sum())
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9 if tot_ms > 0 else 0.0
-    G = next((1 << q for (q, pth, _, _) in tau if pth == fi.PATH_FFT), L)   # chunks end at FFT positions
+    G = 1 << split if split < w.P else L                                  # chunks end at FFT positions
     chunk = None
     if chunk_n:
         avg_us = chunk_ms * 1e3 / chunk_n
-        # per-position latency inside chunks, by the position's place in its chunk
-        # (r = 2 .. G: a chunk's first position follows the FFT block before it)
+        # per-position latency inside chunks (timed steps), by the position's place
+        # in its chunk (r = 2 .. G-1; r = 1 follows the FFT block before the chunk,
+        # r = G ends with the FFT block after it)
         r = (npos - 1) % G + 1
         win = max(1, G // 8)
-        by_place = {}
+        by_place, mean_place = {}, {}
         for a in range(0, G, win):
-            sel = (r > max(a, 1)) & (r <= a + win)
+            sel = (r > max(a, 1)) & (r <= min(a + win, G - 1))
             if sel.any():
-                by_place[f"{max(a, 1) + 1}-{a + win}"] = round(float(np.median(lat[sel])), 3)
+                by_place[f"{max(a, 1) + 1}-{min(a + win, G - 1)}"] = round(float(np.median(lat[sel])), 3)
+                mean_place[f"{max(a, 1) + 1}-{min(a + win, G - 1)}"] = round(float(np.mean(lat[sel])), 3)
+        first = r == 1
+        in_chunk = (r >= 2) & (r <= G - 1)
+        # algorithmic bytes of a chunk launch: every direct gray block of edge U < G
+        # inside the chunk (per (l, c): B*12U + 4(2U-1)) and the red cells (12 bytes
+        # per (l, b, c) and position)
+        lg = G.bit_length() - 1
+        per_lc = sum((G >> (q + 1)) * (w.B * 12 * (1 << q) + 4 * (2 * (1 << q) - 1)) for q in range(lg))
+        chunk_bytes = w.M * w.D * per_lc + 12 * w.M * w.B * w.D * G
         chunk = {"kernel": "k_chunk (red cells and direct gray blocks of a chunk of positions)",
+                 "alg_bytes_per_launch": chunk_bytes,
+                 "hbm_frac_by_alg_bytes": round(chunk_bytes / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                  "launches": int(chunk_n), "positions_per_launch": G,
                  "avg_launch_us": round(avg_us, 2), "us_per_position": round(avg_us / G, 4),
                  "median_us_by_place_in_chunk": by_place,
-                 "share_of_step_time": round(chunk_ms * 1e-3 / total, 4),
-                 "fft_share_of_step_time": round(tot_ms * 1e-3 / total, 4),
+                 "mean_us_by_place_in_chunk": mean_place,
+                 "first_position_median_us": round(float(np.median(lat[first])), 2) if first.any() else None,
+                 "sum_of_mean_position_us_2_to_G-1": round(float(np.mean(lat[in_chunk])) * (G - 2), 1),
+                 "share_of_event_timed_step": round(chunk_ms * 1e-3 / ev_total, 4),
+                 "fft_share_of_event_timed_step": round(tot_ms * 1e-3 / ev_total, 4),
                  "bound": "latency: the serial red-cell chain (M layers of fma + tanh per position) "
                           "and one workgroup barrier per position, not bytes or flops"}
 
@@ -344,9 +467,8 @@ def main():
     defer = None
     if not args.no_defer_leg:
         ctx.set_defer_wide(True)
-        dt = one_step()
+        dt = one_step(ctx)
         dl = np.diff(ctx.stamps(1, L).astype(np.float64)) / 100.0
-        ctx.block_times(clear=True)
         ctx.set_defer_wide(False)
         top = w.P - 1
         dcls = cls[:L - 1]
@@ -370,10 +492,26 @@ def main():
         "alg_bytes_per_launch": round(tot_bytes / max(launches, 1)),
         "avg_launch_us": round(tot_ms * 1e3 / max(launches, 1), 2),
         "per_class": rows,
+        "measured": f"kernel durations from {ev_steps} generations run right after the timed steps, every FFT "
+                    f"gray-block launch bracketed by HIP events stamped by the dispatch on the context's stream "
+                    f"(direct launches; the timed steps replay the same kernels from graphs)",
+        "event_timed_tokens_per_s": round(L * w.B * ev_steps / ev_total, 1),
     }
     ctx.close()
     del ctx
     torch.cuda.empty_cache()
+
+    par = None
+    if not args.no_pareto_leg:
+        par = pareto(w, h, split)
+        log("bench: per-size path times " + ", ".join(
+            f"U={r['U']}: " + "/".join(f"{r[k]}" for k in ("direct_us", "fft_us") if k in r) for r in par))
+
+    hyena = None
+    if not args.no_hyena_leg:
+        hyena = hyena_run(workloads.WORKLOADS[5], args.hyena_positions)
+        log(f"bench: Hyena-style block workload, {args.hyena_positions} positions: "
+            f"{hyena['e2e_tokens_per_s']:,.0f} tokens/s end to end, block share {hyena['block_share']}")
 
     lazy = ablations = None
     if not args.no_lazy:
@@ -390,17 +528,22 @@ def main():
             A = np.vstack([np.ones(len(pts)), work]).T
             a, b = np.linalg.lstsq(A, np.array(tus), rcond=None)[0]
             total_s = (a * w.L + b * w.L * (w.L + 1) / 2 - (0 if name.startswith("lazy") else b * w.L)) * 1e-6
+            resid = np.abs(A @ np.array([a, b]) - np.array(tus)) / np.array(tus)
             fits[name] = {"tokens_per_s": w.L * w.B / total_s, "total_s_extrapolated": round(total_s, 2),
                           "sample_us": {str(n): round(t, 2) for n, t in zip(pts, tus)},
-                          "fit_us": [round(float(a), 3), float(b)]}
+                          "fit_us": [round(float(a), 3), float(b)],
+                          "fit_max_rel_residual": round(float(resid.max()), 4)}
         bl.close()
         del bl
         lazy = dict(fits["lazy"])
         lazy["speedup_vs_lazy"] = round(value / lazy["tokens_per_s"], 1)
         lazy["note"] = ("Lazy per-position device time measured at the sampled positions with HIP events "
-                        "and integrated over n = 1..L with an affine fit")
+                        "and integrated over n = 1..L with an affine fit (fit_max_rel_residual: the fit's "
+                        "largest relative miss at the sampled positions); a full Lazy generation of this "
+                        "workload would take total_s_extrapolated seconds")
         ablations = {k: {"tokens_per_s": round(v["tokens_per_s"], 2),
-                         "total_s_extrapolated": v["total_s_extrapolated"], "fit_us": v["fit_us"]}
+                         "total_s_extrapolated": v["total_s_extrapolated"], "fit_us": v["fit_us"],
+                         "fit_max_rel_residual": v["fit_max_rel_residual"]}
                      for k, v in fits.items()}
         # the tiled path without chunks (one position per launch), with and without graphs
         for name, graphs in (("tiled_per_position_graphs", True), ("tiled_per_position_no_graphs", False)):
@@ -525,6 +668,12 @@ def main():
         "ablations": ablations,
         "prefill": prefill,
         "data_dependent": dd,
+        "pareto": {"per_size": par,
+                   "note": "device time of one gray-block launch per block size at this shape, each path where "
+                           "it exists (direct: the per-position kernel with the red cells; fft: the transform "
+                           "kernels alone); inside chunks the direct blocks below the split run as per-target "
+                           "sums instead (chunk_kernel)"} if par else None,
+        "hyena_block": hyena,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

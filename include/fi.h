@@ -67,7 +67,7 @@ typedef enum fi_status {
  * fi_set_block_weights: [u|v|w] = x W, the mixer convolves q = u*w, its output
  * c gates m = v*c, z = GELU(m W1) W2 (exact-erf GELU, no biases),
  * a = z / sqrt(mean(z^2) + 1e-6), next layer input a, next position's layer-0
- * input fb(a^{M-1}).  Needs D % 8 == 0 and B <= 8.  Here "y" of fi_step /
+ * input fb(a^{M-1}).  Needs D % 8 == 0, D <= 768 and B <= 8.  Here "y" of fi_step /
  * fi_generate is a^{M-1}_n, the value the feedback is applied to. */
 enum { FI_MAP_TANH = 0, FI_MAP_IDENTITY = 1, FI_MAP_EXTERNAL = 2, FI_MAP_HYENA = 3 };
 enum { FI_FEEDBACK_TANH = 0, FI_FEEDBACK_IDENTITY = 1 };
@@ -236,13 +236,14 @@ fi_status fi_set_block_weights(fi_ctx *ctx, const uint16_t *W, const uint16_t *W
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same upload and the same result, but the staging buffer the
  * weights pass through on their way to the transposed layout is a fixed
- * device array of the library (8 MiB per device, taken when the first call on
- * a device looks up its address) instead of an allocation; no hipMalloc,
- * hipFree or other allocating call is made.  Limit: 4*D*D 16-bit values must
- * fit the array, i.e. D <= 1024 (FI_EINVAL with a message otherwise).  Every
- * call on one device shares that device's array and leaves its contents there:
- * calls that overlap on one device (other streams or threads) race.
- * Synchronises the stream, like fi_set_block_weights. */
+ * device array of the library (4.5 MiB per device, its address looked up at
+ * the first call on a device) instead of an allocation; no hipMalloc, hipFree
+ * or other allocating call is made.  Limit: 4*D*D 16-bit values must fit the
+ * array, i.e. D <= 768, the widest block FI_MAP_HYENA takes (FI_EINVAL with a
+ * message otherwise).  Every call on one device shares that device's array
+ * and leaves its contents there: calls that overlap on one device (other
+ * streams or threads) race.  Synchronises the stream, like
+ * fi_set_block_weights. */
 fi_status fi_set_block_weights_static(fi_ctx *ctx, const uint16_t *W, const uint16_t *W1, const uint16_t *W2,
                                       int on_device);
 
@@ -318,6 +319,16 @@ fi_status fi_chunk_times(fi_ctx *ctx, int clear, double *ms, int64_t *count);
  * exist for q.  Overwrites activation rows: fi_reset is required before any
  * further stepping (FI_ESTATE otherwise). */
 fi_status fi_time_block(fi_ctx *ctx, int q, int path, int reps, double *us);
+
+/* Benchmark support for the time split between mixer and block (summary page,
+ * "Zeit-Zerlegung (Abbildung 2a)"): the mean device time in microseconds of
+ * one position's block kernels in FI_MAP_HYENA mode -- every layer's
+ * projection (with its red cell), GELU up-projection and down-projection, then
+ * the RMSNorm'd output and feedback -- without the gray blocks, over `reps`
+ * launches timed with HIP events, without advancing.  Needs the block weights
+ * (FI_ESTATE otherwise).  The activation rows are overwritten: fi_reset is
+ * required before any further stepping (FI_ESTATE otherwise). */
+fi_status fi_time_hyena_block(fi_ctx *ctx, int reps, double *us);
 
 /* Benchmark support for the Lazy baseline: the mean device time in
  * microseconds of the Lazy work of position n (every layer's full O(n) sum

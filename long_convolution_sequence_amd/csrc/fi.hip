@@ -39,6 +39,7 @@ constexpr int kMaxP = 24;
 constexpr int kRing = 512;        // ring slots: pending sums reach at most W/2 = 256 ahead
 constexpr int kHeadTaps = 256;    // taps h[0..255] serve direct blocks up to U = 128
 constexpr int kChunkEv = -1;      // event-pair class of a timed chunk kernel
+constexpr int kChunkBlockLog = 4; // a chunk block graph spans 2^4 - 1 chunks
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -116,7 +117,7 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     const int vlog = o.fft_max_log2;
     if (vlog < kMinSubLog || vlog > kMaxLdsFftLog) return false;
     const bool hyena = o.map == FI_MAP_HYENA;
-    if (hyena && (D % 8 != 0 || B > kBlockMaxB)) return false;
+    if (hyena && (D % 8 != 0 || D > kBlockSpan || B > kBlockMaxB)) return false;
     if ((int64_t)B * D > (int64_t(1) << 24)) return false;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -193,6 +194,13 @@ struct fi_ctx {
     hipGraphExec_t gclass[kMaxP + 1] = {nullptr};
     hipGraphExec_t gblock = nullptr;
     int block_log = 0;
+    // chunk graphs: gchunk[q] = one chunk and the FFT gray blocks of class q at
+    // its end (q = P: the chunk that ends at L, no block); gchunks = the
+    // 2^chunk_block_log - 1 chunks of an aligned run of 2^chunk_block_log
+    // chunks with their FFT blocks (all but the run's last chunk)
+    hipGraphExec_t gchunk[kMaxP + 1] = {nullptr};
+    hipGraphExec_t gchunks = nullptr;
+    int chunk_block_log = 0;
     // FFT gray-block timing: recorded event pairs not yet read, and the sums
     std::vector<hipEvent_t> ev;
     std::vector<int> ev_class;
@@ -487,18 +495,25 @@ hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const floa
 
 // Hyena-style block position: per layer projection + red cell, GELU up,
 // down; then the output / feedback; then every layer's gray block.
-hipError_t launch_hyena_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
-                                 int advance, int64_t defer = 0) {
+// The block kernels of one position (every layer's projection with its red
+// cell, GELU up, down; then the output / feedback).
+hipError_t launch_hyena_block(fi_ctx *c, int rd, hipStream_t s, const float *xext, float *yext) {
     const int B = c->B, D = c->D;
-    const size_t lds_d = (size_t)B * D * sizeof(float), lds_4d = 4 * lds_d;
+    const HyProjK kp = hy_proj_k(B);
+    const HyStepK ku = hy_up_k(B), kd = hy_down_k(B);
+    if (!kp || !ku || !kd) return hipErrorInvalidValue;
     for (int l = 0; l < c->M; ++l) {
-        hipLaunchKernelGGL(k_hy_proj, dim3((D + 3) / 4), dim3(256), lds_d, s, c->dev, rd, l,
-                           l == 0 ? xext : nullptr);
-        hipLaunchKernelGGL(k_hy_up, dim3(D), dim3(256), lds_d, s, c->dev, rd, l);
-        hipLaunchKernelGGL(k_hy_down, dim3((D + 3) / 4), dim3(256), lds_4d, s, c->dev, rd, l);
+        hipLaunchKernelGGL(kp, dim3((D + 3) / 4), dim3(256), 0, s, c->dev, rd, l, l == 0 ? xext : nullptr);
+        hipLaunchKernelGGL(ku, dim3((4 * D / kBlockRows + 3) / 4), dim3(256), 0, s, c->dev, rd, l);
+        hipLaunchKernelGGL(kd, dim3((D + kBlockRows - 1) / kBlockRows), dim3(256), 0, s, c->dev, rd, l);
     }
     hipLaunchKernelGGL(k_hy_out, dim3(1), dim3(256), 0, s, c->dev, rd, yext);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_hyena_position(fi_ctx *c, int rd, int q, hipStream_t s, const float *xext, float *yext,
+                                 int advance, int64_t defer = 0) {
+    hipError_t e = launch_hyena_block(c, rd, s, xext, yext);
     if (e != hipSuccess) return e;
     return launch_position_t<false>(c, rd, q, s, nullptr, nullptr, advance, defer);
 }
@@ -620,6 +635,27 @@ fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<std::pair<in
     return FI_OK;
 }
 
+// Record chunk launches into one graph: for each entry, a chunk (its base read
+// from the published position) and, for q < P, the FFT gray blocks of class q
+// at its end.
+fi_status capture_chunks(fi_ctx *c, hipGraphExec_t *out, const std::vector<int> &classes) {
+    hipGraph_t g = nullptr;
+    HIPCK(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal));
+    hipError_t err = hipSuccess;
+    for (int q : classes) {
+        err = launch_chunk(c, -1, nullptr, c->cap);
+        if (err == hipSuccess && q < c->P) err = launch_fft(c, 1, q, c->cap, 2);
+        if (err != hipSuccess) break;
+    }
+    hipError_t e2 = hipStreamEndCapture(c->cap, &g);
+    if (err != hipSuccess) return fail(c, FI_EDEVICE, std::string("capture: ") + hipGetErrorString(err));
+    if (e2 != hipSuccess) return fail(c, FI_EDEVICE, std::string("end capture: ") + hipGetErrorString(e2));
+    hipError_t e3 = hipGraphInstantiate(out, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e3 != hipSuccess) return fail(c, FI_EDEVICE, std::string("instantiate: ") + hipGetErrorString(e3));
+    return FI_OK;
+}
+
 fi_status build_graphs(fi_ctx *c) {
     // class q: n odd iff q == 0; the last position L is even
     for (int q = 0; q <= c->P; ++q) {
@@ -636,6 +672,22 @@ fi_status build_graphs(fi_ctx *c) {
         if (s != FI_OK) return s;
         c->block_log = k;
     }
+    if (c->chunk_log >= 0) {
+        // chunk q_end = class of the position that ends it; chunks end at
+        // multiples of G = 2^chunk_log, so q_end >= chunk_log
+        for (int q = c->chunk_log; q <= c->P; ++q) {
+            fi_status s = capture_chunks(c, &c->gchunk[q], {q});
+            if (s != FI_OK) return s;
+        }
+        const int kb = std::min(kChunkBlockLog, c->P - c->chunk_log - 1);
+        if (kb >= 1) {
+            std::vector<int> classes;
+            for (int j = 1; j < (1 << kb); ++j) classes.push_back(c->chunk_log + ctz64(j));
+            fi_status s = capture_chunks(c, &c->gchunks, classes);
+            if (s != FI_OK) return s;
+            c->chunk_block_log = kb;
+        }
+    }
     return FI_OK;
 }
 
@@ -647,6 +699,13 @@ void destroy_graphs(fi_ctx *c) {
         }
     if (c->gblock) (void)hipGraphExecDestroy(c->gblock);
     c->gblock = nullptr;
+    for (auto &g : c->gchunk)
+        if (g) {
+            (void)hipGraphExecDestroy(g);
+            g = nullptr;
+        }
+    if (c->gchunks) (void)hipGraphExecDestroy(c->gchunks);
+    c->gchunks = nullptr;
     for (auto &e : c->ev)
         if (e) (void)hipEventDestroy(e);
     c->ev.clear();
@@ -933,10 +992,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         d.mb = (float *)(c->ws + lay.mb);
         d.hb = (float *)(c->ws + lay.hb);
         d.reca = o.record ? (float *)(c->ws + lay.reca) : nullptr;
-        const int lds_4d = (int)((size_t)batch * 4 * channels * sizeof(float));
-        if (hipFuncSetAttribute((const void *)k_hy_down, hipFuncAttributeMaxDynamicSharedMemorySize, lds_4d) !=
-            hipSuccess)
-            return bail(fail(c, FI_EDEVICE, "block kernel LDS attribute"));
+
     }
     d.fb = o.feedback == FI_FEEDBACK_IDENTITY ? 1 : 0;
     for (int q = 0; q < c->P; ++q)
@@ -1134,7 +1190,7 @@ fi_status load_block_weights(fi_ctx *c, const uint16_t *W, const uint16_t *W1, c
 // address, one per device, comes from hipGetSymbolAddress and is kept here.
 // Every call on a device shares that device's array: calls that overlap on one
 // device (different streams or threads) race.
-constexpr size_t kStaticStageBytes = size_t(8) << 20;
+constexpr size_t kStaticStageBytes = size_t(4) * kBlockSpan * kBlockSpan * sizeof(unsigned short);
 constexpr size_t kStaticStageElems = kStaticStageBytes / sizeof(unsigned short);
 static __device__ __align__(256) unsigned short scratch[kStaticStageElems];
 constexpr int kMaxDevices = 64;
@@ -1248,6 +1304,27 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
         if (chunk_fits(c, c->pos, end)) {
             // a split gray block deferred earlier feeds targets past side_until
             const int64_t G = int64_t(1) << c->chunk_log;
+            if (graphs && !c->opt.time_blocks && c->gchunk[c->chunk_log]) {
+                // an aligned run of 2^kb chunks: all but the last from one graph
+                const int kb = c->chunk_block_log;
+                const int64_t run = G << kb;
+                const bool split_in_run = c->opt.defer_wide && is_sub(c->chunk_log + kb - 1, c->opt.fft_max_log2);
+                if (kb && !split_in_run && (c->pos & (run - 1)) == 0 && c->pos + run <= end) {
+                    if ((s = join_side(c, c->pos + run - G - 1)) != FI_OK) return s;
+                    HIPCK(c, hipGraphLaunch(c->gchunks, c->stream));
+                    c->pos += run - G;
+                    c->ring_stale = true;
+                }
+                const int64_t n = c->pos + G;
+                const int q = class_of(c, n);
+                if (!(c->opt.defer_wide && q < c->P && is_sub(q, c->opt.fft_max_log2))) {
+                    if ((s = join_side(c, n - 1)) != FI_OK) return s;
+                    HIPCK(c, hipGraphLaunch(c->gchunk[q], c->stream));
+                    c->pos = n;
+                    c->ring_stale = true;
+                    continue;
+                }
+            }
             if ((s = join_side(c, c->pos + G - 1)) != FI_OK) return s;
             if ((s = run_chunk(c, c->pos, nullptr)) != FI_OK) return s;
             c->pos += G;
@@ -1343,7 +1420,7 @@ fi_status fi_set_block_weights_static(fi_ctx *c, const uint16_t *W, const uint16
                     "fi_set_block_weights_static: D = " + std::to_string(c->D) + " needs " +
                         std::to_string(block_stage_elems(c->D) * sizeof(unsigned short)) +
                         " bytes of staging, more than the " + std::to_string(kStaticStageBytes) +
-                        " of the static scratch (D <= 1024)");
+                        " of the static scratch (D <= " + std::to_string(kBlockSpan) + ")");
     unsigned short *stage = nullptr;
     if ((s = static_stage(c, &stage)) != FI_OK) return s;
     return load_block_weights(c, W, W1, W2, on_device, stage);
@@ -1506,6 +1583,31 @@ fi_status fi_time_block(fi_ctx *c, int q, int path, int reps, double *us) {
     HIPCK(c, once());  // warm-up
     HIPCK(c, hipEventRecord(a, c->stream));
     for (int r = 0; r < reps; ++r) HIPCK(c, once());
+    HIPCK(c, hipEventRecord(b, c->stream));
+    HIPCK(c, hipEventSynchronize(b));
+    float ms = 0.f;
+    HIPCK(c, hipEventElapsedTime(&ms, a, b));
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    *us = ms * 1000.0 / reps;
+    return FI_OK;
+}
+
+fi_status fi_time_hyena_block(fi_ctx *c, int reps, double *us) {
+    fi_status s = check_usable(c);
+    if (s != FI_OK) return s;
+    if ((s = join_side(c, -1)) != FI_OK) return s;
+    if (reps < 1 || !us) return FI_EINVAL;
+    if (c->opt.map != FI_MAP_HYENA) return fail(c, FI_ESTATE, "fi_time_hyena_block needs FI_MAP_HYENA");
+    if (!c->weights_set) return fail(c, FI_ESTATE, "block weights not set");
+    if ((s = set_state_pos(c, 0)) != FI_OK) return s;
+    c->mode = 3;  // rows now hold timing garbage: only fi_reset leaves this mode
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    HIPCK(c, launch_hyena_block(c, 0, c->stream, nullptr, nullptr));  // warm-up
+    HIPCK(c, hipEventRecord(a, c->stream));
+    for (int r = 0; r < reps; ++r) HIPCK(c, launch_hyena_block(c, 0, c->stream, nullptr, nullptr));
     HIPCK(c, hipEventRecord(b, c->stream));
     HIPCK(c, hipEventSynchronize(b));
     float ms = 0.f;

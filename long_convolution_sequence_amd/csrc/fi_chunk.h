@@ -253,7 +253,11 @@ __device__ __forceinline__ void helper_push(float *xp, const float *hreg, int ro
 }
 
 template <int MT, int MODE>
-__global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb, int G, int CH, const float *xseq) {
+__global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg, int G, int CH, const float *xseq) {
+    // cb < 0: the chunk follows the position published in the state (graph
+    // replays); a chunk starts after a multiple of G, so that position is even
+    // and sits in slot 0
+    const long long cb = cb_arg >= 0 ? cb_arg : p.st->pos[0];
     constexpr int S = 8;                       // helper lanes per row
     constexpr int SP = kChunkSlot;
     extern __shared__ float sm[];

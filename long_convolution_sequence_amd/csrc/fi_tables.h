@@ -23,6 +23,9 @@ using DDBandK = void (*)(Dev, DDev, float4 *, float4 *);                     // 
 using DDFftK = void (*)(Dev, DDev, const float4 *, const float4 *, long long);   // k_dd_fft
 using DDNearK = void (*)(DDev, long long, const float *, const float *, float *, bool);  // k_dd_near
 
+using HyProjK = void (*)(Dev, int, int, const float *);                      // k_hy_proj<B>
+using HyStepK = void (*)(Dev, int, int);                                    // k_hy_up<B>, k_hy_down<B>
+
 FftTileK fft_tile_k(int logn);     // one-workgroup transform, 2 <= logn <= 14
 FftTileK fft_tile2_k(int logm);    // two halves of 2^logm, 12 <= logm <= 14
 SubFwdK sub_fwd_k(int logv);       // split classes, sub-blocks of 2^logv, 12..14
@@ -34,5 +37,8 @@ ChunkK chunk_k(int mt, int mode);  // mt = depth up to kChunkRegLayers, or 0; mo
 DDBandK dd_band_k(int logp);       // 2..14
 DDFftK dd_fft_k(int logp);         // 2..14
 DDNearK dd_near_k(int pm);         // 1, 2, 4, .., 128
+HyProjK hy_proj_k(int B);          // Hyena-style block kernels for batch B, 1 <= B <= 8
+HyStepK hy_up_k(int B);
+HyStepK hy_down_k(int B);
 
 }  // namespace fi

@@ -88,6 +88,7 @@ def load_library():
         "fi_set_block_weights_static": (I, [P, P, P, P, I]),
         "fi_lazy_time": (I, [P, I64, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_time_block": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_double)]),
+        "fi_time_hyena_block": (I, [P, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_dd_workspace_bytes": (S, [I, I, I64, I]),
         "fi_dd_init": (I, [ctypes.POINTER(P), I, I, I64, I, P, P]),
         "fi_dd_step": (I, [P, P, P, P]),
@@ -350,6 +351,12 @@ class Context:
         """Mean microseconds of class q's gray-block kernels on one path (needs reset after)."""
         us = ctypes.c_double()
         self._check(self._lib.fi_time_block(self._h, int(q), int(path), int(reps), ctypes.byref(us)))
+        return us.value
+
+    def time_hyena_block(self, reps=10):
+        """Mean microseconds of one position's block kernels (Hyena-style block mode; needs reset after)."""
+        us = ctypes.c_double()
+        self._check(self._lib.fi_time_hyena_block(self._h, int(reps), ctypes.byref(us)))
         return us.value
 
     def lazy_time(self, n, reps=3):

@@ -101,3 +101,27 @@ def test_block_mode_full_size():
     assert conv <= 1.0
     assert wq <= 1e-4 and wa <= 1e-4
     assert rel <= 1e-3
+
+
+def test_block_kernel_timing_needs_reset():
+    """fi_time_hyena_block times one position's block kernels and leaves the
+    context needing a reset, like the other timing calls."""
+    w = workloads.custom(M=2, B=2, D=32, L=64, decay=16.0, seed=71, block="hyena")
+    say(f"case block kernel timing {w.name}")
+    bits, _ = _weights(w)
+    h = workloads.filters(w)
+    with fi.Context(torch.from_numpy(h).cuda(), w.B, map=fi.MAP_HYENA) as ctx:
+        with pytest.raises(fi.FiError) as e:
+            ctx.time_hyena_block(3)                  # no weights yet
+        assert e.value.status == fi.FI_ESTATE
+    with fi.Context(torch.from_numpy(h).cuda(), w.B, map=fi.MAP_HYENA) as ctx:
+        ctx.set_block_weights(bits["W"], bits["W1"], bits["W2"])
+        us = ctx.time_hyena_block(5)
+        assert 0.0 < us < 1e5
+        with pytest.raises(fi.FiError) as e:
+            ctx.step()
+        assert e.value.status == fi.FI_ESTATE
+        ctx.reset()
+        ctx.set_input(torch.from_numpy(workloads.x_first(w)).cuda())
+        ctx.generate(w.L, want_y=False)
+        assert ctx.position == w.L

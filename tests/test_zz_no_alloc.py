@@ -3,7 +3,7 @@ allocate device memory: through the C-ABI it must give exactly what
 fi_set_block_weights gives.  Two calls in a row share the library's static
 staging array, the second with a smaller input (its array still holds the
 first call's values past the second's end); host and device sources; and a
-width whose staging would not fit is refused with a message."""
+block wider than the array holds is refused."""
 import numpy as np
 import pytest
 import torch
@@ -39,12 +39,13 @@ def test_static_weight_upload_equals_allocating_one(on_device):
         assert np.array_equal(y_static, y_alloc)
 
 
-def test_static_weight_upload_rejects_too_wide_blocks():
-    w = workloads.custom(M=1, B=1, D=1032, L=8, decay=4.0, seed=5, block="hyena")
+def test_blocks_wider_than_the_static_scratch_are_refused():
+    """The block mode takes D <= 768, which is also what the static staging
+    array holds (4 * 768 * 768 16-bit values): a wider block is refused when the
+    context is made, before any upload could need more."""
+    w = workloads.custom(M=1, B=1, D=776, L=8, decay=4.0, seed=5, block="hyena")
     h = workloads.filters(w)
-    say("case static weight upload refuses D=1032")
-    with fi.Context(torch.from_numpy(h).cuda(), w.B, map=fi.MAP_HYENA, tau_split=2) as ctx:
-        bits = workloads.hyena_weights(w)
-        with pytest.raises(fi.FiError) as e:
-            ctx.set_block_weights_static(bits["W"], bits["W1"], bits["W2"])
-        assert e.value.status == fi.FI_EINVAL and "static scratch" in str(e.value)
+    say("case block wider than 768 refused")
+    with pytest.raises(fi.FiError) as e:
+        fi.Context(torch.from_numpy(h).cuda(), w.B, map=fi.MAP_HYENA, tau_split=2)
+    assert e.value.status == fi.FI_EINVAL
