@@ -354,6 +354,8 @@ def main():
     ctx = fi.Context(hdev, w.B, tau_split=args.tau_split)
     tau = ctx.tau_table()
     split = next((q for (q, pth, _, _) in tau if pth == fi.PATH_FFT), w.P)
+    calib = [{"first_fft_U": 1 << g, "chunk_and_fft_us": round(uc, 2), "modeled_run_ms": round(ur * 1e-3, 3)}
+             for (g, uc, ur) in ctx.chunk_table() if ur >= 0]
     log("bench: block paths", [(q, "fft" if p == fi.PATH_FFT else "direct") for (q, p, _, _) in tau])
 
     def one_step(c):
@@ -657,6 +659,10 @@ def main():
         "data": "synthetic (seeded random filters and first input, recipe in DESIGN.md)",
         "config": {"workload": w.name, "M": w.M, "B": w.B, "D": w.D, "L": L,
                    "block_paths": ["fft" if p == fi.PATH_FFT else "direct" for (_, p, _, _) in tau]},
+        "split_calibration": {"per_candidate": calib,
+                              "note": "fi_init timed one chunk of 2^g positions and the class-g FFT block "
+                                      "after it per candidate g (the hybrid rule on the chunk path); the "
+                                      "cheapest modeled run sets the split"} if calib else None,
         "latency_us": {"p50": round(float(np.percentile(lat, 50)), 2),
                        "p99": round(float(np.percentile(lat, 99)), 2),
                        "max": round(float(lat.max()), 1),

@@ -147,8 +147,11 @@ size_t fi_workspace_bytes(int layers, int batch, int channels, int64_t L,
  *            aligned, owned by the caller and untouched by it while the context
  *            lives; or NULL to let the library allocate (and free) its own.
  *   stream:  hipStream_t the context runs on (NULL = default stream).
- * Computes the filter spectra and, for FI_TAU_AUTO, times both block paths
- * per block size on the device; synchronises the stream before returning.
+ * Computes the filter spectra and, for FI_TAU_AUTO, times the block paths on
+ * the device: with chunked positions (fi_options.chunk_direct and a map that
+ * acts channel by channel), one chunk plus its FFT block per candidate split
+ * (fi_chunk_table); otherwise both paths per block size (fi_tau_table).
+ * Synchronises the stream before returning.
  * Returns FI_EINVAL / FI_ENOMEM / FI_EDEVICE on failure (*out is then NULL). */
 fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L,
                   const float *filters, const fi_options *opt, void *workspace,
@@ -217,6 +220,15 @@ fi_status fi_debug_schedule(const fi_ctx *ctx, int64_t n, int *q, int *path);
  * paths (negative where a path does not exist or was not timed).  Arrays hold
  * at least P entries; any pointer may be NULL. */
 fi_status fi_tau_table(const fi_ctx *ctx, int *path, double *us_direct, double *us_fft);
+
+/* Chunk-path calibration (FI_TAU_AUTO with chunked positions): for each
+ * candidate first FFT class g (chunks of 2^g positions carry every block below
+ * 2^g), us_chunk[g] = measured microseconds of one chunk and the class-g FFT
+ * gray blocks after it, us_run[g] = the modeled microseconds of the classes
+ * the choice affects over a whole run ((L / 2^g) chunks plus the FFT blocks of
+ * classes g .. 8); the candidate with the least us_run is the split used.  -1
+ * where not timed.  Arrays hold at least P + 1 entries; either may be NULL. */
+fi_status fi_chunk_table(const fi_ctx *ctx, double *us_chunk, double *us_run);
 
 /* Copy positions first..first+count-1 (first >= 1) of one layer into dst
  * (device fp32, [count][B][D]):

@@ -185,6 +185,9 @@ struct fi_ctx {
     int pre_stride = 0;
     int path[kMaxP] = {0};
     double us_direct[kMaxP], us_fft[kMaxP];
+    // chunk-path calibration, per candidate first FFT class g: one chunk of 2^g
+    // positions and the class-g FFT block after it (us_chunk), the modeled run
+    double us_chunk[kMaxP + 1], us_run[kMaxP + 1];
     int64_t pos = 0;
     int mode = 0;  // 0 fresh, 1 tiled, 2 lazy
     bool poisoned = false;
@@ -617,6 +620,107 @@ fi_status time_class(fi_ctx *c, int q, double &us_direct, double &us_fft) {
     return FI_OK;
 }
 
+// Chunks of 2^g positions for this context: chains per workgroup and the LDS
+// attribute.  False when a chunk cannot hold the stack (too deep).
+bool setup_chunks(fi_ctx *c, int g, int cus) {
+    c->chunk_log = g;
+    c->chunk_ch = choose_chunk_ch(c->M, c->B * c->D, g, cus);
+    if (c->chunk_ch < 1) {
+        c->chunk_log = -1;
+        return false;
+    }
+    return allow_chunk_lds(c) == hipSuccess;
+}
+
+// Mean microseconds of the FFT gray-block kernels of class q alone, at n = 2^q
+// (2 warm-up launches, then 4 batches of 8).
+fi_status time_fft_only(fi_ctx *c, int q, double &us) {
+    us = -1.0;
+    fi_status st = set_state_pos(c, (int64_t(1) << q) - 1);
+    if (st != FI_OK) return st;
+    const int rd = rd_of(int64_t(1) << q);
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    for (int w = 0; w < 2; ++w) HIPCK(c, launch_fft(c, rd, q, c->stream, 0));
+    double total = 0.0;
+    for (int rep = 0; rep < 4; ++rep) {
+        HIPCK(c, hipEventRecord(a, c->stream));
+        for (int k = 0; k < 8; ++k) HIPCK(c, launch_fft(c, rd, q, c->stream, 0));
+        HIPCK(c, hipEventRecord(b, c->stream));
+        HIPCK(c, hipEventSynchronize(b));
+        float ms = 0.f;
+        HIPCK(c, hipEventElapsedTime(&ms, a, b));
+        total += ms * 1000.0 / 8.0;
+    }
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    us = total / 4.0;
+    return FI_OK;
+}
+
+// Mean microseconds of one chunk of the first G = 2^chunk_log positions, then
+// the FFT gray blocks of class chunk_log at its end (none when the chunk ends
+// at L): launched back to back as in a generation, one warm-up and three timed
+// pairs, the chunk's pending sums cleared before each.
+fi_status time_chunk_pair(fi_ctx *c, double &us) {
+    us = -1.0;
+    const int g = c->chunk_log;
+    const int64_t G = int64_t(1) << g;
+    const size_t rows = (size_t)c->M * c->B * c->D;
+    hipEvent_t a, b;
+    HIPCK(c, hipEventCreate(&a));
+    HIPCK(c, hipEventCreate(&b));
+    double total = 0.0;
+    for (int rep = 0; rep < 4; ++rep) {
+        fi_status st = set_state_pos(c, 0);
+        if (st != FI_OK) return st;
+        HIPCK(c, hipMemset2DAsync(c->dev.buf, (size_t)c->L * sizeof(float), 0, (size_t)G * sizeof(float), rows,
+                                  c->stream));
+        HIPCK(c, hipEventRecord(a, c->stream));
+        HIPCK(c, launch_chunk(c, 0, nullptr, c->stream));
+        if (g < c->P) HIPCK(c, launch_fft(c, rd_of(G), g, c->stream, 2));
+        HIPCK(c, hipEventRecord(b, c->stream));
+        HIPCK(c, hipEventSynchronize(b));
+        float ms = 0.f;
+        HIPCK(c, hipEventElapsedTime(&ms, a, b));
+        if (rep > 0) total += ms * 1000.0;
+    }
+    HIPCK(c, hipEventDestroy(a));
+    HIPCK(c, hipEventDestroy(b));
+    us = total / 3.0;
+    return FI_OK;
+}
+
+// The hybrid split for chunked positions, timed on the path it configures
+// (rebuttal page: profile per shape and block size, pick the fastest): for
+// each candidate first FFT class g, a chunk of 2^g positions carries every
+// block below 2^g, and classes from g on run as FFT blocks.  The whole run
+// costs (L / 2^g) chunks plus 2^(P-1-q) FFT blocks of each class q >= g; the
+// classes above kMaxDirectLog + 1 are FFT blocks for every candidate and are
+// left out of the comparison.  Picks the cheapest g into qd.
+fi_status calibrate_chunks(fi_ctx *c, int cus, int &qd) {
+    const int qtop = std::min(kMaxDirectLog + 1, c->P - 1);      // FFT classes that may switch
+    for (int q = kMinFftLog; q <= qtop; ++q) {
+        fi_status st = time_fft_only(c, q, c->us_fft[q]);
+        if (st != FI_OK) return st;
+    }
+    double best = -1.0;
+    for (int g = kMinFftLog; g <= std::min(kMaxDirectLog + 1, c->P); ++g) {
+        if (!setup_chunks(c, g, cus)) continue;
+        fi_status st = time_chunk_pair(c, c->us_chunk[g]);
+        if (st != FI_OK) return st;
+        double cost = std::ldexp(c->us_chunk[g] - (g < c->P ? c->us_fft[g] : 0.0), c->P - g);
+        for (int q = g; q <= qtop; ++q) cost += std::ldexp(c->us_fft[q], c->P - 1 - q);
+        c->us_run[g] = cost;
+        if (best < 0 || cost < best) {
+            best = cost;
+            qd = g;
+        }
+    }
+    return clear_state(c);
+}
+
 // Record the positions (class, parity slot) into one graph.
 fi_status capture(fi_ctx *c, hipGraphExec_t *out, const std::vector<std::pair<int, int>> &positions) {
     hipGraph_t g = nullptr;
@@ -938,6 +1042,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     c->lay = lay;
     c->stream = (hipStream_t)stream;
     for (int q = 0; q < kMaxP; ++q) c->us_direct[q] = c->us_fft[q] = -1.0;
+    for (int q = 0; q <= kMaxP; ++q) c->us_chunk[q] = c->us_run[q] = -1.0;
 
     auto bail = [&](fi_status s) {
         fi_destroy(c);
@@ -1042,9 +1147,22 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     if (o.tau_mode == FI_TAU_FFT) qd = std::min(c->P, kMinFftLog);
     else if (o.tau_mode == FI_TAU_AUTO && o.tau_split >= 0)
         qd = std::min(c->P, std::max(kMinFftLog, std::min(o.tau_split, kMaxDirectLog + 1)));
-    if (o.tau_mode == FI_TAU_AUTO && o.tau_split < 0) {
-        // time both paths per class at the real shape, then pick the split that
-        // minimises the whole run: class q runs 2^(P-1-q) times
+    int cus = 0;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return bail(fail(c, FI_EDEVICE, "device query"));
+    }
+    const bool chunked = (o.map == FI_MAP_TANH || o.map == FI_MAP_IDENTITY) && o.chunk_direct &&
+                         choose_chunk_ch(c->M, c->B * c->D, 0, cus) >= 1;
+    if (o.tau_mode == FI_TAU_AUTO && o.tau_split < 0 && chunked) {
+        // chunked positions: time the chunk path itself per candidate split
+        if (calibrate_chunks(c, cus, qd) != FI_OK) return bail(FI_EDEVICE);
+    } else if (o.tau_mode == FI_TAU_AUTO && o.tau_split < 0) {
+        // one launch per position: time both paths per class at the real shape,
+        // then pick the split that minimises the whole run: class q runs
+        // 2^(P-1-q) times
         for (int q = kMinFftLog; q <= std::min(kMaxDirectLog, c->P - 1); ++q) {
             double ud, uf;
             if (time_class(c, q, ud, uf) != FI_OK) return bail(FI_EDEVICE);
@@ -1066,16 +1184,11 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     c->qd = qd;
     for (int q = 0; q < c->P; ++q) c->path[q] = q < qd ? FI_PATH_DIRECT : FI_PATH_FFT;
     c->dev.G = qd < c->P ? (1 << qd) : 0;
+    c->chunk_log = -1;
     if (o.map == FI_MAP_TANH || o.map == FI_MAP_IDENTITY) {
-        // chunks end at the FFT positions (or at L when every class is direct)
-        c->chunk_log = std::min(qd, c->P);
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-            return bail(fail(c, FI_EDEVICE, "device query"));
-        c->chunk_ch = choose_chunk_ch(c->M, c->B * c->D, c->chunk_log, cus);
-        if (c->chunk_ch < 1) c->chunk_log = -1;   // deeper than the helper rows of one workgroup
-        else if (allow_chunk_lds(c) != hipSuccess)
+        // chunks end at the FFT positions (or at L when every class is direct);
+        // none when the stack is deeper than the helper rows of one workgroup
+        if (!setup_chunks(c, std::min(qd, c->P), cus) && c->chunk_log >= 0)
             return bail(fail(c, FI_EDEVICE, "chunk kernel LDS attribute"));
     }
     if (o.use_graphs && o.map != FI_MAP_EXTERNAL) {
@@ -1374,6 +1487,15 @@ fi_status fi_tau_table(const fi_ctx *c, int *path, double *us_direct, double *us
         if (path) path[q] = c->path[q];
         if (us_direct) us_direct[q] = c->us_direct[q];
         if (us_fft) us_fft[q] = c->us_fft[q];
+    }
+    return FI_OK;
+}
+
+fi_status fi_chunk_table(const fi_ctx *c, double *us_chunk, double *us_run) {
+    if (!c) return FI_EINVAL;
+    for (int g = 0; g <= c->P; ++g) {
+        if (us_chunk) us_chunk[g] = c->us_chunk[g];
+        if (us_run) us_run[g] = c->us_run[g];
     }
     return FI_OK;
 }

@@ -74,6 +74,7 @@ def load_library():
         "fi_debug_schedule": (I, [P, I64, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "fi_tau_table": (I, [P, P, P, P]),
         "fi_history": (I, [P, I, I, I64, I64, P]),
+        "fi_chunk_table": (I, [P, P, P]),
         "fi_stamps": (I, [P, I64, I64, P]),
         "fi_layer_red": (I, [P, I, P, P]),
         "fi_tiles": (I, [P]),
@@ -331,6 +332,15 @@ class Context:
         uf = (ctypes.c_double * P)()
         self._check(self._lib.fi_tau_table(self._h, path, ud, uf))
         return [(q, path[q], ud[q], uf[q]) for q in range(self.P)]
+
+    def chunk_table(self):
+        """Chunk-path calibration per candidate first FFT class g: (g, us of one chunk + its FFT block,
+        modeled us of a run); -1 where not timed."""
+        n = self.P + 1
+        uc = (ctypes.c_double * n)()
+        ur = (ctypes.c_double * n)()
+        self._check(self._lib.fi_chunk_table(self._h, uc, ur))
+        return [(g, uc[g], ur[g]) for g in range(n)]
 
     def block_times(self, clear=False):
         """Per class q: (summed FFT gray-block ms, launches) measured with HIP events."""

@@ -341,3 +341,25 @@ def test_binding_rejects_mismatched_tensors():
         with pytest.raises(fi.FiError):
             dd.run(torch.zeros((4, B, D), device="cuda"), torch.zeros((3, B, D), device="cuda"))
         assert dd.position == 0
+
+
+def test_auto_split_is_timed_on_the_chunk_path():
+    """With chunked positions, the calibrated split is the candidate whose timed
+    chunk (and FFT block) gives the cheapest modeled run; the per-position path
+    keeps its per-class timing."""
+    M, B, D, L = 2, 1, 64, 4096
+    say(f"case chunk-path calibration M={M} B={B} D={D} L={L}")
+    h = _filters(M, D, L, 43, decay=512.0) * 0.1
+    with fi.Context(_cuda(h), B) as ctx:
+        table = ctx.chunk_table()
+        paths = [p for (_, p, _, _) in ctx.tau_table()]
+    timed = [(g, uc, ur) for (g, uc, ur) in table if ur >= 0]
+    assert [g for g, _, _ in timed] == list(range(2, 9))
+    assert all(uc > 0 for _, uc, _ in timed)
+    best = min(timed, key=lambda t: t[2])[0]
+    split = next(q for q, p in enumerate(paths) if p == fi.PATH_FFT)
+    say(f"  modeled run per candidate {[(g, round(ur)) for g, _, ur in timed]}; split {split}")
+    assert split == best
+    with fi.Context(_cuda(h), B, chunk_direct=False) as ctx:
+        assert all(ur < 0 for (_, _, ur) in ctx.chunk_table())
+        assert any(ud > 0 for (_, _, ud, _) in ctx.tau_table())
