@@ -571,30 +571,34 @@ def main():
 
     prefill = None
     if not args.no_prefill_leg:
-        # a prompt of P positions: eager (all positions of a layer at once) against P
-        # teacher-forced positions; each timed warm, on device events
-        P = min(16384, w.L // 8)
-        xp = torch.from_numpy(np.random.default_rng(5).standard_normal((P, w.B, w.D)).astype(np.float32)).cuda()
-        prefill = {"P": P}
-        for name, eager in (("eager", True), ("steps", False)):
-            pf = fi.Context(torch.from_numpy(h).cuda(), w.B, eager_prefill=eager)
-            ms = []
-            for _ in range(3):
-                pf.reset()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                pf.prefill(xp, want_y=False)
-                b.record()
-                torch.cuda.synchronize()
-                ms.append(a.elapsed_time(b))
-            pf.close()
-            del pf
-            prefill[f"{name}_ms"] = round(float(np.median(ms[1:])), 3)
-            prefill[f"{name}_tokens_per_s"] = round(P * w.B / (np.median(ms[1:]) * 1e-3), 1)
-        prefill["note"] = ("fi_prefill of a seeded N(0,1) prompt at position 0, eager (layer by layer, "
-                           "all positions at once) against P teacher-forced positions (chunks); median of "
-                           "two warm runs, HIP events on the stream")
-        log(f"bench: prefill P={P}: eager {prefill['eager_ms']} ms, steps {prefill['steps_ms']} ms")
+        # prompts of P positions: eager (all positions of a layer at once) against P
+        # teacher-forced positions (chunks); each timed warm, on device events
+        prefill = {}
+        for P in sorted({min(32768, w.L // 4), min(65536, w.L // 2)}):
+            xp = torch.from_numpy(np.random.default_rng(5).standard_normal((P, w.B, w.D)).astype(np.float32)).cuda()
+            row = {}
+            for name, eager in (("eager", True), ("steps", False)):
+                pf = fi.Context(torch.from_numpy(h).cuda(), w.B, eager_prefill=eager, tau_split=split)
+                ms = []
+                for _ in range(3):
+                    pf.reset()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    pf.prefill(xp, want_y=False)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ms.append(a.elapsed_time(b))
+                pf.close()
+                del pf
+                row[f"{name}_ms"] = round(float(np.median(ms[1:])), 3)
+                row[f"{name}_tokens_per_s"] = round(P * w.B / (np.median(ms[1:]) * 1e-3), 1)
+            prefill[f"P={P}"] = row
+            del xp
+            log(f"bench: prefill P={P}: eager {row['eager_ms']} ms, steps {row['steps_ms']} ms")
+        prefill["note"] = ("fi_prefill of a seeded N(0,1) prompt at position 0, eager (layer by layer, all "
+                           "positions at once; the gray blocks after n <= P batched per class, the widest "
+                           "after the layers) against P teacher-forced positions (chunks); median of two warm "
+                           "runs, HIP events on the stream")
 
     dd = None
     if not args.no_dd_leg:

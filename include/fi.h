@@ -117,10 +117,12 @@ typedef struct fi_options {
                               prompt layer by layer with all of a layer's
                               positions at once (direct sums inside blocks of G,
                               FFT blocks above), when the map acts channel by
-                              channel, P is a multiple of G and every gray block
-                              after n <= P fits one workgroup transform
-                              (P < 2^(fft_max_log2+1)); otherwise, or with 0, P
-                              teacher-forced positions */
+                              channel, P is a multiple of G, P <= L/2, and every
+                              gray block after n <= P wider than one workgroup
+                              transform either starts at n = P or (the two-half
+                              class) ends inside the prompt -- e.g. at
+                              L = 2^17, P = 16384, 32768, 65536 -- otherwise, or
+                              with 0, P teacher-forced positions */
     int reserved[3];       /* must be zero */
 } fi_options;
 

@@ -67,7 +67,7 @@ struct Layout {
     size_t filt = 0, hh = 0, htap = 0, pre = 0, buf = 0, xr = 0, ar = 0, recx = 0, recy = 0, twid = 0, xin = 0, ylast = 0,
            stamps = 0, state = 0, scratch = 0, wt = 0, w1t = 0, w2t = 0, zb = 0, mb = 0, hb = 0, reca = 0;
     int HK = 0;
-    int pre_stride = 0;              // prefill sums per (b, c): positions below 2^(fft_max_log2+1)
+    int pre_stride = 0;              // prefill sums per (b, c): positions of a prompt up to L/2
     size_t spec[kMaxP] = {0};
     size_t total = 0;
     int logNT = 0;
@@ -130,7 +130,7 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.filt = take(rowsMD * L * sizeof(float));
     lay.hh = take(rowsMD * lay.HK * sizeof(float));
     lay.htap = take(rowsMD * kChunkTapRow * sizeof(float));
-    lay.pre_stride = (int)std::min<int64_t>(L, int64_t(1) << (vlog + 1));
+    lay.pre_stride = (int)std::min<int64_t>(L, std::max<int64_t>(L / 2, int64_t(1) << (vlog + 1)));
     lay.pre = take((size_t)B * D * lay.pre_stride * sizeof(float));
     lay.buf = take(rowsMBD * L * sizeof(float));
     lay.xr = take((size_t)kRing * rowsMBD * sizeof(float));
@@ -1325,12 +1325,40 @@ fi_status static_stage(fi_ctx *c, unsigned short **out) {
     return FI_OK;
 }
 
-// Whether fi_prefill may take the eager path (see fi_options.eager_prefill).
+// Whether fi_prefill may take the eager path (see fi_options.eager_prefill):
+// every gray block after a position n <= P must have a prefill form.  Blocks
+// of one-workgroup width may end anywhere (their targets past P go to the
+// pending sums); two-half blocks must end inside the prompt (k_pre_fft2) or
+// start at n = P; wider blocks must start at n = P (both run after the layer
+// loop with the generation kernels, since their targets all lie past P).
 bool eager_prefill_ok(const fi_ctx *c, int64_t P) {
     const int64_t G = c->dev.G;
-    return c->opt.eager_prefill && c->pos == 0 && P > 0 && P < c->L && G >= 4 && G <= kPreNearMax && P % G == 0 &&
-           (c->opt.map == FI_MAP_TANH || c->opt.map == FI_MAP_IDENTITY) &&
-           P < (int64_t(1) << (c->opt.fft_max_log2 + 1)) && P <= c->pre_stride;
+    const int vlog = c->opt.fft_max_log2;
+    if (!(c->opt.eager_prefill && c->pos == 0 && P > 0 && P < c->L && G >= 4 && G <= kPreNearMax && P % G == 0 &&
+          (c->opt.map == FI_MAP_TANH || c->opt.map == FI_MAP_IDENTITY) && P <= c->pre_stride))
+        return false;
+    for (int q = ilog2_exact(G); (int64_t(1) << q) <= P; ++q) {
+        const int64_t U = int64_t(1) << q;
+        for (int64_t n = U; n <= P; n += 2 * U) {
+            if (q <= vlog || n == P) continue;
+            if (is_pair(q, vlog) && n + U <= P) continue;
+            return false;
+        }
+    }
+    return true;
+}
+
+// Two-half blocks of class q inside the prompt (n + 2^q <= P), layer l.
+hipError_t launch_pre_fft2(fi_ctx *c, int q, int l, int64_t P) {
+    const int logm = q - 1;
+    const PreFftK k = pre_fft2_k(logm);
+    if (!k) return hipErrorInvalidValue;
+    const long long BD = (long long)c->B * c->D, pb = fft_per_block(logm);
+    const unsigned nb = (unsigned)(((P >> q) + 1) >> 1);   // odd multiples of 2^q up to P
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(k, dim3((unsigned)((BD + pb - 1) / pb), nb), dim3(fft_tpb(logm)), 0, c->stream, c->dev,
+                       (const float4 *)c->spec[q], l, (long long)P, c->pre, c->pre_stride);
+    return hipGetLastError();
 }
 
 hipError_t launch_pre_fft(fi_ctx *c, int q, int l, int64_t P) {
@@ -1356,13 +1384,24 @@ fi_status eager_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
         hipLaunchKernelGGL(k_pre_near, dim3((unsigned)(BD * (P / G))), dim3(kPreNearMax), 0, c->stream, c->dev, l,
                            (long long)P, G, c->pre, c->pre_stride);
         HIPCK(c, hipGetLastError());
-        for (int q = qg; (int64_t(1) << q) <= P; ++q) HIPCK(c, launch_pre_fft(c, q, l, P));
+        for (int q = qg; (int64_t(1) << q) <= P; ++q) {
+            if (q <= c->opt.fft_max_log2) HIPCK(c, launch_pre_fft(c, q, l, P));
+            else if (is_pair(q, c->opt.fft_max_log2)) HIPCK(c, launch_pre_fft2(c, q, l, P));
+        }
         hipLaunchKernelGGL(k_pre_red, dim3(cells), dim3(256), 0, c->stream, c->dev, l, (long long)P,
                            (const float *)c->pre, c->pre_stride, y);
         HIPCK(c, hipGetLastError());
     }
-    fi_status s = set_state_pos(c, P);
-    if (s != FI_OK) return s;
+    // the block after P itself when it is wider than one workgroup transform:
+    // its targets all lie past the prompt, so every layer's block runs now,
+    // with the kernels of a generation
+    const int qp = ctz64(P);
+    fi_status s = FI_OK;
+    if (qp > c->opt.fft_max_log2) {
+        if ((s = set_state_pos(c, P - 1)) != FI_OK) return s;
+        HIPCK(c, launch_fft(c, rd_of(P), qp, c->stream, 0));
+    }
+    if ((s = set_state_pos(c, P)) != FI_OK) return s;
     c->pos = P;
     c->ring_stale = true;          // the next per-position launch rebuilds the ring
     return FI_OK;

@@ -378,6 +378,35 @@ k_fft_tile2(Dev p, int rd, const float4 *__restrict__ spec, int advance) {
     finish_position(p, n, advance);
 }
 
+// Eager prefill, far part for the two-half class (U = 2M): the gray blocks of
+// edge U after positions n = (2j+1) U <= P (j = blockIdx.y) whose targets all
+// lie inside the prompt (n + U <= P), for the B*D rows of layer l, added into
+// the prefill sums pre[(b, c)][t-1].  Same transform as k_fft_tile2.
+template <int LOGM>
+__global__ void __launch_bounds__(FftShape<LOGM>::TPB) __attribute__((amdgpu_waves_per_eu(4)))
+k_pre_fft2(Dev p, const float4 *__restrict__ spec, int l, long long P, float *pre, int pstride) {
+    using S = FftShape<LOGM>;
+    constexpr int M = S::N, TT = S::TT;
+    constexpr long long U = 2LL * M;
+    __shared__ float2 smem[S::LDS];
+    const int team = threadIdx.x / TT, lt = threadIdx.x % TT;
+    const long long n = (2LL * blockIdx.y + 1) * U;
+    if (n + U > P) return;                         // uniform guard: targets past the prompt are not ours
+    const long long BD = (long long)p.B * p.D;
+    const long long k = (long long)blockIdx.x * S::PER_BLOCK + team;   // (b, c) of layer l
+    const bool active = k < BD;
+    float2 *X = smem + team * lds_len(M);
+    const long long kk = active ? k : 0;
+    const int c = (int)(kk % p.D);
+    const size_t row = ((size_t)l * BD + kk) * (size_t)p.L;
+    const float2 *xsrc = reinterpret_cast<const float2 *>(p.buf + row + n - U);
+    float2 *adst = reinterpret_cast<float2 *>(pre + (size_t)kk * pstride + n);
+    const float4 *sp = spec + ((size_t)l * p.D + c) * M;
+    tile2_half<LOGM, true>(p, X, lt, active, xsrc, adst, sp);
+    __syncthreads();  // the even half reuses the LDS
+    tile2_half<LOGM, false>(p, X, lt, active, xsrc, adst, sp);
+}
+
 // Filter spectra in the two-half item order: for every (l, c) row the taps
 // g_r = h[goff + r], r in [0, 4M), packed into 2M complex points, scaled by
 // 1/(2M), at spec + row * row_stride.

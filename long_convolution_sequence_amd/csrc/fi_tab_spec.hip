@@ -51,4 +51,13 @@ PreFftK pre_fft_k(int logn) {
     }
 }
 
+PreFftK pre_fft2_k(int logm) {
+    switch (logm) {
+        case 12: return &k_pre_fft2<12>;
+        case 13: return &k_pre_fft2<13>;
+        case 14: return &k_pre_fft2<14>;
+        default: return nullptr;
+    }
+}
+
 }  // namespace fi

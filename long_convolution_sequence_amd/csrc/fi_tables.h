@@ -33,6 +33,7 @@ SubInvK sub_inv_k(int logv);
 SpectrumK spectrum_k(int logn);    // 2..14
 SpectrumK spectrum2_k(int logm);   // 12..14
 PreFftK pre_fft_k(int logn);       // 2..14
+PreFftK pre_fft2_k(int logm);      // two-half class of 2^(logm+1), 12..14
 ChunkK chunk_k(int mt, int mode);  // mt = depth up to kChunkRegLayers, or 0; mode 0..3
 DDBandK dd_band_k(int logp);       // 2..14
 DDFftK dd_fft_k(int logp);         // 2..14

@@ -54,10 +54,41 @@ def test_eager_prefill_falls_back_where_it_does_not_apply():
             assert torch.equal(a.prefill(_cuda(x)), b.prefill(_cuda(x)))
 
 
-def test_eager_prefill_full_size_workload():
-    """18 layers, B=1, D=864, L=2^17 (the bench workload), P = 16384."""
+def test_eager_prefill_long_prompts_wide_blocks():
+    """Prompts past one workgroup transform (width 2^12 here): at P = L/2 the
+    two-half blocks after n = 2^13 end inside the prompt (their prefill kernel)
+    and the split block after n = P starts at the prompt's end (run after the
+    layer loop with the generation kernels)."""
+    M, B, D, L, P = 2, 2, 3, 32768, 16384
+    say(f"case eager prefill wide blocks M={M} B={B} D={D} L={L} P={P} width 2^12")
+    r = np.random.default_rng(34)
+    h = (r.standard_normal((M, D, L)) * np.exp(-np.arange(L) / 4096.0) * 0.05).astype(np.float32)
+    x = r.standard_normal((P, B, D)).astype(np.float32)
+    kw = dict(tau_split=4, record=True, fft_max_log2=12)
+    with fi.Context(_cuda(h), B, **kw) as e, fi.Context(_cuda(h), B, eager_prefill=False, **kw) as s:
+        assert e.schedule(8192)[0] == 13 and e.schedule(16384)[0] == 14
+        ye = e.prefill(_cuda(x)).cpu().numpy()
+        ys = s.prefill(_cuda(x)).cpu().numpy()
+        rel = np.abs(ye - ys).max() / np.abs(ys).max()
+        worst = check_replay(h, e, count=P)
+        say(f"  prefill: eager vs steps rel {rel:.2e}; replay worst error/tolerance {worst:.3e}")
+        assert rel <= 1e-5
+        assert worst <= 1.0
+        ge = e.generate(L - P).cpu().numpy()
+        gs = s.generate(L - P).cpu().numpy()
+        relg = np.abs(ge - gs).max() / np.abs(gs).max()
+        worst = check_replay(h, e)
+        say(f"  then generation: eager vs steps rel {relg:.2e}; replay worst error/tolerance {worst:.3e}")
+        assert relg <= 1e-4
+        assert worst <= 1.0
+
+
+@pytest.mark.parametrize("P", [16384, 32768, 65536])
+def test_eager_prefill_full_size_workload(P):
+    """18 layers, B=1, D=864, L=2^17 (the bench workload): P = 16384 (every
+    block after n <= P one workgroup wide), 32768 (the two-half block after P)
+    and 65536 (two-half blocks inside the prompt, the split block after P)."""
     w = workloads.WORKLOADS[4]
-    P = 16384
     say(f"case eager prefill {w.name} P={P}")
     h = workloads.filters(w)
     x = np.random.default_rng(33).standard_normal((P, w.B, w.D)).astype(np.float32)
