@@ -48,13 +48,18 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         return obj
 
     jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(compile_one, srcs))
+    objs = [os.path.join(OBJ, os.path.basename(s)[:-4] + "." + tag + ".o") for s in srcs]
     tmp = LIB + ".tmp" + tag
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    for o in objs:
-        os.remove(o)
+    try:
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(compile_one, srcs))
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    finally:
+        # this build's objects go, whether it succeeded or not
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     if verbose:

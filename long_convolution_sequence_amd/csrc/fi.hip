@@ -155,7 +155,7 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
     lay.twid = take((size_t(2) << lay.logNT) * sizeof(float2));  // twiddles, pair and odd-pair twiddles
     lay.xin = take((size_t)2 * B * D * sizeof(float));
     lay.ylast = take((size_t)L * B * D * sizeof(float));
-    lay.stamps = take((size_t)(L + 1) * sizeof(long long));
+    lay.stamps = take((size_t)2 * (L + 1) * sizeof(long long));
     lay.state = take(sizeof(State));
     lay.total = off;
     return true;
@@ -564,7 +564,7 @@ fi_status clear_state(fi_ctx *c) {
     if (c->dev.reca) HIPCK(c, hipMemsetAsync(c->dev.reca, 0, rowsMBD * c->L * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.xin, 0, 2 * (size_t)c->B * c->D * sizeof(float), c->stream));
     HIPCK(c, hipMemsetAsync(c->dev.ylast, 0, (size_t)c->L * c->B * c->D * sizeof(float), c->stream));
-    HIPCK(c, hipMemsetAsync(c->dev.stamps, 0, (size_t)(c->L + 1) * sizeof(long long), c->stream));
+    HIPCK(c, hipMemsetAsync(c->dev.stamps, 0, (size_t)2 * (c->L + 1) * sizeof(long long), c->stream));
     fi_status s = set_state_pos(c, 0);
     if (s != FI_OK) return s;
     c->pos = 0;
@@ -1592,7 +1592,15 @@ fi_status fi_stamps(fi_ctx *c, int64_t first, int64_t count, int64_t *dst) {
     if (s != FI_OK) return s;
     if (first < 0 || count < 0 || first + count > c->L + 1 || (!dst && count)) return FI_EINVAL;
     HIPCK(c, hipStreamSynchronize(c->stream));
-    if (count) HIPCK(c, hipMemcpy(dst, c->dev.stamps + first, count * sizeof(long long), hipMemcpyDeviceToHost));
+    if (count) {
+        // the later of the two rows (the second is written only where a
+        // position ends in several workgroups at once, zero elsewhere)
+        std::vector<int64_t> second((size_t)count);
+        HIPCK(c, hipMemcpy(dst, c->dev.stamps + first, count * sizeof(long long), hipMemcpyDeviceToHost));
+        HIPCK(c, hipMemcpy(second.data(), c->dev.stamps + (c->L + 1) + first, count * sizeof(long long),
+                           hipMemcpyDeviceToHost));
+        for (int64_t k = 0; k < count; ++k) dst[k] = std::max(dst[k], second[(size_t)k]);
+    }
     return FI_OK;
 }
 

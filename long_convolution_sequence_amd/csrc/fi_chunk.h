@@ -40,7 +40,7 @@ constexpr int kChunkThreads = 1024;  // chunk workgroups: wave 0 + up to 15 help
 //
 // LDS: heads h01[R] (h[0], h[1]); slots xp[G][kChunkSlot], slot s at row
 // G-1-s (reversed, so that the taps of a helper lie at increasing addresses:
-// immediate offsets, read in pairs); zero rows G .. G+63; teacher-forced
+// immediate offsets); zero rows G .. G+63; teacher-forced
 // inputs xs[G][CH].  Rows rho = j * M + l for chain c0 + j, layer l.
 //
 // Global memory inside the position loop: the chain's last-layer output, the
@@ -52,9 +52,15 @@ constexpr int kChunkTapRow = 8 * kChunkTaps;   // tap-table floats per (l, c): t
 constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's layers in registers
 constexpr int kChunkHelperWaves = 12;
 constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
-// floats per slot: >= the rows, and 8 slots apart = 15 x 256 bytes (one
-// read2st64 reaches two taps); the eight lanes of a row then hit distinct banks
-constexpr int kChunkSlot = 120;
+static_assert(kChunkMaxRows <= kChunkThreads - kLanes, "one head row per set-up thread");
+// Floats per slot: >= the rows, and 4 mod 8, so that the taps of the eight
+// lanes of a row (slots seg apart, seg < 8) fall on eight banks 4 apart (of
+// 32), which the four rows of a half-wave fill without a conflict.  (A slot
+// of a multiple of 8 floats would let one read2st64 fetch two taps of a lane,
+// but puts lanes seg and seg + 4 of a row on one bank: every read and write
+// of the pulls and pushes twice as long.)
+constexpr int kChunkSlot = 100;
+static_assert(kChunkSlot >= kChunkMaxRows && kChunkSlot % 8 == 4, "slot width");
 // zero rows after the slots: the helper taps that lie before the chunk read them
 constexpr int kChunkZeroRows = 64;
 // positions a chain stays on the full tanh after its polynomial pass failed
@@ -70,7 +76,7 @@ constexpr int kChunkRec = 1, kChunkTanh = 2;
 // 0's data and store nothing.  MT = 0: any depth, one layer at a time from LDS.
 template <int MT, bool REC, bool TANH_ALL>
 __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
-                                          int chain, bool on, const float *xs, int CH) {
+                                          int chain, bool on, const float *xs, int CH, float xf) {
     const int BD = p.B * p.D, M = p.M;
     const int jr = on ? j : 0;                 // the chain whose LDS data this lane reads
     constexpr int NR = MT > 0 ? MT : 1;
@@ -82,7 +88,6 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
         h1[k] = v.y;
         xq[k] = 0.f;                           // slot -1: its tap-1 term is in the FFT sums
     }
-    float xf = on ? p.xin[(size_t)((cb + 1) & 1) * BD + chain] : 0.f;   // feedback input
     const bool map_id = !TANH_ALL && p.map != 0, fb_id = !TANH_ALL && p.fb != 0;
     int full_left = 0;                         // wave-uniform: positions left on the full tanh
     for (int i = 0; i < G; ++i) {
@@ -235,7 +240,7 @@ __device__ __forceinline__ void helper_push(float *xp, const float *hreg, int ro
     constexpr int S = 8, SP = kChunkSlot, P = kChunkPullTaps;
     if constexpr (C > 0) {
         // from the lowest row up, so that every access is the base plus a
-        // non-negative immediate (rows 8 apart: pairs of 15 x 256 bytes)
+        // non-negative immediate
         float *b = xp + (size_t)(rowp - S * (C - 1)) * SP + hrho;
         float v[C];
 #pragma unroll
@@ -268,6 +273,10 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     float *xs = xz + kChunkZeroRows * SP;                  // [G][CH] teacher-forced inputs
     const int c0 = blockIdx.x * CH;
     const int lane = threadIdx.x & (kLanes - 1), wave = threadIdx.x / kLanes;
+    // the chain's feedback input, loaded first.  The first touch of its page
+    // after the FFT blocks can take several microseconds: wave 0 loads nothing
+    // else before the position loop, and the other waves' set-up below hides it
+    const float xf0 = wave == 0 && lane < CH && c0 + lane < BD ? p.xin[(size_t)((cb + 1) & 1) * BD + c0 + lane] : 0.f;
     const int logG = 31 - __clz(G);
     auto grow = [&](int rho) {                             // history row of local row rho
         return ((size_t)(rho % M) * BD + c0 + rho / M) * (size_t)p.L;
@@ -287,7 +296,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     const int hrho = hid / S, seg = hid & (S - 1);
     const bool helper = hw >= 0 && hrho < R && live(hrho);
     float hreg[kChunkTaps];
-    {
+    if (hw >= 0) {
         // the lane's 32 taps lie together in the tap table: eight 16-byte loads
         const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
                                             seg * kChunkTaps);
@@ -306,35 +315,64 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
         }
     }
 
-    // pending sums of the chunk's positions (rows of the history, G slots
-    // each: coalesced reads), the heads, the teacher-forced inputs
-    if (G >= 4) {
-        const int g4 = logG - 2;                           // float4 per row: G / 4
-        for (int e = threadIdx.x; e < (R * G) >> 2; e += blockDim.x) {
-            const int rho = e >> g4, s0 = (e & ((G >> 2) - 1)) * 4;
-            const float4 v = live(rho) ? *(const float4 *)(p.buf + grow(rho) + cb + s0)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-            float *d = xp + (size_t)(G - 1 - s0) * SP + rho;
-            d[0] = v.x;
-            d[-SP] = v.y;
-            d[-2 * SP] = v.z;
-            d[-3 * SP] = v.w;
+    // Set-up by waves 1..15: the pending sums of the chunk's positions (rows
+    // of the history, G slots each), the heads, the zero rows, the
+    // teacher-forced inputs.
+    const int pt = threadIdx.x - kLanes, npt = blockDim.x - kLanes;
+    if (wave > 0) {
+        // the heads, one row per thread (R <= kChunkMaxRows < npt), in flight
+        // together with the pending sums
+        float2 hv = make_float2(0.f, 0.f);
+        if (pt < R && live(pt)) hv = make_float2(p.filt[frow(pt)], p.L > 1 ? p.filt[frow(pt) + 1] : 0.f);
+        if (G >= 16) {
+            // Items of 16 rows x 4 float4 per wave: the loads read 64
+            // contiguous bytes of each of 16 rows, and the stores (four slots
+            // per float4; items of one row lie 4 kChunkSlot floats apart,
+            // 16 banks) meet at most two lanes per bank, where an item per
+            // row-major lane would put 32 lanes of a store on one bank.  A
+            // thread's loads all go out before its first store.
+            constexpr int NB = 8, RW = 16, KW = 4;
+            const int rg = (R + RW - 1) / RW;              // groups of 16 rows
+            const int total = rg * (G >> 2) * RW;          // items, padded to whole row groups
+            for (int e0 = pt; e0 < total; e0 += NB * npt) {
+                float4 v[NB];
+                int rho[NB], s0[NB];
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const int e = e0 + k * npt;
+                    const int blk = e >> 6, ln = e & 63;
+                    rho[k] = (blk % rg) * RW + (ln & (RW - 1));
+                    s0[k] = ((blk / rg) * KW + (ln >> 4)) * 4;
+                    v[k] = e < total && rho[k] < R && live(rho[k])
+                               ? *(const float4 *)(p.buf + grow(rho[k]) + cb + s0[k])
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const int e = e0 + k * npt;
+                    if (e >= total) break;
+                    if (rho[k] >= R) continue;
+                    float *d = xp + (size_t)(G - 1 - s0[k]) * SP + rho[k];
+                    d[0] = v[k].x;
+                    d[-SP] = v[k].y;
+                    d[-2 * SP] = v[k].z;
+                    d[-3 * SP] = v[k].w;
+                }
+            }
+        } else {
+            for (int e = pt; e < R * G; e += npt) {
+                const int rho = e >> logG;
+                xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho] = live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
+            }
         }
-    } else {
-        for (int e = threadIdx.x; e < R * G; e += blockDim.x) {
-            const int rho = e >> logG;
-            xp[(size_t)(G - 1 - (e & (G - 1))) * SP + rho] = live(rho) ? p.buf[grow(rho) + cb + (e & (G - 1))] : 0.f;
-        }
+        for (int e = pt; e < kChunkZeroRows * SP; e += npt) xz[e] = 0.f;
+        if (pt < R) h01[pt] = hv;
+        if (xseq)
+            for (int e = pt; e < G * CH; e += npt) {
+                const int i = e / CH, j = e % CH;
+                xs[e] = c0 + j < BD ? xseq[(size_t)i * BD + c0 + j] : 0.f;
+            }
     }
-    for (int e = threadIdx.x; e < kChunkZeroRows * SP; e += blockDim.x) xz[e] = 0.f;
-    for (int rho = threadIdx.x; rho < R; rho += blockDim.x)
-        h01[rho] = live(rho) ? make_float2(p.filt[frow(rho)], p.L > 1 ? p.filt[frow(rho) + 1] : 0.f)
-                             : make_float2(0.f, 0.f);
-    if (xseq)
-        for (int e = threadIdx.x; e < G * CH; e += blockDim.x) {
-            const int i = e / CH, j = e % CH;
-            xs[e] = c0 + j < BD ? xseq[(size_t)i * BD + c0 + j] : 0.f;
-        }
     __syncthreads();
 
     float *hist = p.buf + (helper ? grow(hrho) + cb : 0);   // a helper row's positions of the chunk
@@ -342,13 +380,19 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
         // ---- red cells; the helpers do not share this wave's SIMD
         __builtin_amdgcn_s_setprio(3);
         chain_run<MT, (MODE & kChunkRec) != 0, (MODE & kChunkTanh) != 0>(
-            p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH);
+            p, xp, G, h01, cb, lane, c0 + lane, lane < CH && c0 + lane < BD, xseq ? xs : nullptr, CH, xf0);
     } else if (hw < 0) {
-        // ---- waves 4, 8, 12: barriers only; wave 4 stamps each position's end
+        // ---- waves 4, 8, 12: barriers only.  Wave 4 of the first and of the
+        // last workgroup in dispatch order stamps each position's end, into
+        // the stamps and their second row; the reader takes the later of the
+        // two.  (An atomic maximum from every workgroup puts a hundred and
+        // more atomics on one address per position, which the memory side
+        // serialises: their backlog stalled whole positions.)
+        const bool first_wg = blockIdx.x == 0, last_wg = blockIdx.x == gridDim.x - 1;
+        long long *sp = p.stamps + (first_wg ? 0 : p.L + 1) + cb + 1;
         for (int i = 0; i < G; ++i) {
             __syncthreads();
-            if (wave == 4 && lane == 0)
-                atomicMax((unsigned long long *)&p.stamps[cb + 1 + i], (unsigned long long)wall_clock64());
+            if (wave == 4 && lane == 0 && (first_wg || last_wg)) sp[i] = (long long)wall_clock64();
         }
     } else {
         // ---- helpers, during position i.  Pull: the pending sum of slot i+1

@@ -18,7 +18,9 @@
 //   Wt, W1t, W2t, zb, mb, hb, reca   Hyena-style block (see fi_block.h)
 //   xin   [2][B][D]      next layer-0 input, double-buffered by position parity
 //   ylast [L][B][D]      last layer's mixer output per position
-//   stamps[L+1] (i64)    device wall clock at the end of each position
+//   stamps[2][L+1] (i64) device wall clock at the end of each position; row 1
+//                        holds a second sample where a position ends in
+//                        several workgroups at once (the reader takes the max)
 //   twid  [NT] (float2)  exp(-2 pi i k / NT), generated in fp64 on the host
 //   ptw   [NT/2] (float2) per transform size N: W_{2N}^j of real-spectrum item e
 //         (pair_slot) at N/2 + e, also fp64 on the host
