@@ -100,9 +100,13 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
 #pragma unroll
             for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
             const float x0 = x;
-            unsigned long long far = 0;                // lanes with some |y| >= 0.8
+            // largest y^2 of the polynomial pass: every |y| < 0.8 exactly when
+            // every rounded y^2 < 0.64f (rounding is monotone; 0.8f^2 rounds
+            // above 0.64f, its predecessor's square below), so one vote per
+            // position, on squares the polynomial forms anyway, decides
+            float s2max = 0.f;
             // the position's layers; FULL = false: tanh by its polynomial half
-            // alone, with a vote on whether every |y| stayed below 0.8
+            // alone, for positions where every |y| stays below 0.8
             auto layers = [&](auto full) {
                 constexpr bool FULL = decltype(full)::value;
                 x = x0;
@@ -118,7 +122,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                         }
                     }
                     const float th = FULL ? tanh_chain(y) : tanh_small(y);
-                    if constexpr (!FULL) far |= __builtin_amdgcn_ballot_w64(!(fabsf(y) < 0.8f));
+                    if constexpr (!FULL) s2max = fmaxf(s2max, y * y);
                     if constexpr (TANH_ALL) {
                         x = th;
                     } else {
@@ -135,9 +139,9 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                 // is tried again (activations that stay large then cost one
                 // extra pass per kChainFullRun positions).
                 if (full_left == 0) {
-                    far = 0;
+                    s2max = 0.f;
                     layers(std::false_type{});
-                    if (far) full_left = kChainFullRun + 1;
+                    if (__builtin_amdgcn_ballot_w64(!(s2max < 0.64f))) full_left = kChainFullRun + 1;
                 }
                 if (full_left > 0) {
                     layers(std::true_type{});
@@ -394,6 +398,10 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
             __syncthreads();
             if (wave == 4 && lane == 0 && (first_wg || last_wg)) sp[i] = (long long)wall_clock64();
         }
+    } else if (hw * (kLanes / S) >= R) {
+        // ---- helper waves without a row (fewer rows than helper lanes):
+        // barriers only, so they take no LDS or VALU time from the others
+        for (int i = 0; i < G; ++i) __syncthreads();
     } else {
         // ---- helpers, during position i.  Pull: the pending sum of slot i+1
         // but for its tap-1 term, over lags 2 .. K-1 (K = 8 kChunkPullTaps):

@@ -90,19 +90,20 @@ __device__ __forceinline__ float apply_map(int kind, float y) { return kind == 0
 // from the hardware base-2 exponential and the reciprocal.  |y| < 0.8, where
 // that difference cancels: y + y^3 P(y^2), P of degree 5 fitted for least
 // relative error (Lawson's iteratively reweighted least squares, in double on
-// Chebyshev nodes; coefficients rounded to float).  P is evaluated in Estrin's
-// scheme and the result formed in y itself (odd, so no sign fix-up): from y to
-// the result is six dependent operations (y*y, its square, two fma levels of
-// P, the final fma), against nine in Horner's form, which matters because a
-// chain runs one tanh per layer back to back.  Error under 1 ulp.  Both halves
-// are evaluated and one selected, so lanes on either side never diverge.
+// Chebyshev nodes; coefficients rounded to float).  P is evaluated in Horner's
+// form and the result formed in y itself (odd, so no sign fix-up): eight
+// operations in all.  A chain's wave runs alone on its SIMD and issues every
+// operation of the layer, so the count of operations, not the depth of their
+// dependences, sets the time per layer (Estrin's scheme is two steps shallower
+// and one operation longer).  Error under 1 ulp.  Both halves are evaluated
+// and one selected, so lanes on either side never diverge.
 __device__ __forceinline__ float tanh_small(float y) {   // y + y^3 P(y^2); meaningful for |y| < 0.8
     const float s = y * y;
-    const float s2 = s * s;
-    const float p01 = fmaf(s, 0.13332220911979675f, -0.33333298563957214f);
-    const float p23 = fmaf(s, 0.021302949637174606f, -0.05385231971740723f);
-    const float p45 = fmaf(s, 0.0015847263857722282f, -0.007409499958157539f);
-    const float q = fmaf(fmaf(p45, s2, p23), s2, p01);
+    float q = fmaf(s, 0.0015847263857722282f, -0.007409499958157539f);
+    q = fmaf(q, s, 0.021302949637174606f);
+    q = fmaf(q, s, -0.05385231971740723f);
+    q = fmaf(q, s, 0.13332220911979675f);
+    q = fmaf(q, s, -0.33333298563957214f);
     return fmaf(y * s, q, y);
 }
 // The full tanh: equal to tanh_small(y) for |y| < 0.8 (bit for bit).
