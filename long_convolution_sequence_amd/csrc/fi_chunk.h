@@ -73,7 +73,11 @@ constexpr int kChunkRec = 1, kChunkTanh = 2;
 // heads and the previous position's inputs in registers, the pending sums of
 // the position read from LDS in one batch, then straight-line code with no
 // branch between layers.  Lanes without a chain run the same code on chain
-// 0's data and store nothing.  MT = 0: any depth, one layer at a time from LDS.
+// 0's data, feedback input included (so their values, and the range vote,
+// are chain 0's), and store nothing.  A position's slot inputs are written
+// after its last pass: the helpers' pulls read this position's slot with a
+// zero tap, which must not meet a polynomial pass's out-of-range values.
+// MT = 0: any depth, one layer at a time from LDS.
 template <int MT, bool REC, bool TANH_ALL>
 __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
                                           int chain, bool on, const float *xs, int CH, float xf) {
@@ -280,7 +284,8 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     // the chain's feedback input, loaded first.  The first touch of its page
     // after the FFT blocks can take several microseconds: wave 0 loads nothing
     // else before the position loop, and the other waves' set-up below hides it
-    const float xf0 = wave == 0 && lane < CH && c0 + lane < BD ? p.xin[(size_t)((cb + 1) & 1) * BD + c0 + lane] : 0.f;
+    const int jin = lane < CH && c0 + lane < BD ? lane : 0;
+    const float xf0 = wave == 0 ? p.xin[(size_t)((cb + 1) & 1) * BD + c0 + jin] : 0.f;
     const int logG = 31 - __clz(G);
     auto grow = [&](int rho) {                             // history row of local row rho
         return ((size_t)(rho % M) * BD + c0 + rho / M) * (size_t)p.L;
