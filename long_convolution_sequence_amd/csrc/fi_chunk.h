@@ -74,10 +74,8 @@ constexpr int kChunkRec = 1, kChunkTanh = 2;
 // the position read from LDS in one batch, then straight-line code with no
 // branch between layers.  Lanes without a chain run the same code on chain
 // 0's data, feedback input included (so their values, and the range vote,
-// are chain 0's), and store nothing.  A position's slot inputs are written
-// after its last pass: the helpers' pulls read this position's slot with a
-// zero tap, which must not meet a polynomial pass's out-of-range values.
-// MT = 0: any depth, one layer at a time from LDS.
+// are chain 0's), and store nothing.  MT = 0: any depth, one layer at a time
+// from LDS.
 template <int MT, bool REC, bool TANH_ALL>
 __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const float2 *hz, long long cb, int j,
                                           int chain, bool on, const float *xs, int CH, float xf) {
@@ -221,7 +219,7 @@ __device__ __forceinline__ void dispatch(int v, F &&f) {
 // NF = min((i+2)/64, kChunkPullTaps/8 - 1), row0 + 8m never passes G+63), so
 // every tap is a plain read at a fixed offset.
 template <int NF>
-__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho) {
+__device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, int row0, int hrho, bool lag01) {
     constexpr int S = 8, SP = kChunkSlot;
     constexpr int NT = 8 * (NF + 1);
     static_assert(NT <= kChunkPullTaps, "pulled taps");
@@ -229,6 +227,10 @@ __device__ __forceinline__ float helper_sum(const float *xp, const float *hreg, 
     const float *base = xp + (size_t)row0 * SP + hrho;
 #pragma unroll
     for (int m = 0; m < NT; ++m) v[m] = base[(size_t)m * S * SP];
+    // lags 0 and 1 (tap 0 of lanes 0 and 1) are the slots of the target and
+    // of the position being computed, whose values are not settled: their
+    // zero taps must not meet an infinity there
+    if (lag01) v[0] = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NT; ++m) acc[m & 3] = fmaf(hreg[m], v[m], acc[m & 3]);
@@ -432,7 +434,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
                 const int row0 = G - 2 - i + seg;
                 float acc = 0.f;
                 dispatch<kChunkPullTaps / 8 - 1>(min((i + 2) >> 6, kChunkPullTaps / 8 - 1), [&](auto nf) {
-                    acc = helper_sum<decltype(nf)::value>(xp, hreg, row0, hrho);
+                    acc = helper_sum<decltype(nf)::value>(xp, hreg, row0, hrho, seg < 2);
                 });
                 acc = sum8(acc);
                 if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
