@@ -53,14 +53,13 @@ constexpr int kChunkRegLayers = 20;  // stacks up to this depth keep a chain's l
 constexpr int kChunkHelperWaves = 12;
 constexpr int kChunkMaxRows = kChunkHelperWaves * kLanes / 8;   // 96
 static_assert(kChunkMaxRows <= kChunkThreads - kLanes, "one head row per set-up thread");
-// Floats per slot: >= the rows, and 4 mod 8, so that the taps of the eight
-// lanes of a row (slots seg apart, seg < 8) fall on eight banks 4 apart (of
-// 32), which the four rows of a half-wave fill without a conflict.  (A slot
-// of a multiple of 8 floats would let one read2st64 fetch two taps of a lane,
-// but puts lanes seg and seg + 4 of a row on one bank: every read and write
-// of the pulls and pushes twice as long.)
-constexpr int kChunkSlot = 100;
-static_assert(kChunkSlot >= kChunkMaxRows && kChunkSlot % 8 == 4, "slot width");
+// Floats per slot: >= the rows, and 8 mod 32.  A multiple of 8 lets one
+// read2st64 fetch two taps of a lane (taps 8 slots apart: 13 x 256 bytes);
+// 8 mod 32 puts the four lanes of a row that share a half-wave (slots seg
+// apart, seg = 0..3 or 4..7) on four banks 8 apart, which the eight rows of
+// the half-wave fill without a conflict (see the helper lanes in k_chunk).
+constexpr int kChunkSlot = 104;
+static_assert(kChunkSlot >= kChunkMaxRows && kChunkSlot % 32 == 8, "slot width");
 // zero rows after the slots: the helper taps that lie before the chunk read them
 constexpr int kChunkZeroRows = 64;
 // positions a chain stays on the full tanh after its polynomial pass failed
@@ -102,13 +101,13 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
 #pragma unroll
             for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
             const float x0 = x;
-            // largest y^2 of the polynomial pass: every |y| < 0.8 exactly when
-            // every rounded y^2 < 0.64f (rounding is monotone; 0.8f^2 rounds
-            // above 0.64f, its predecessor's square below), so one vote per
-            // position, on squares the polynomial forms anyway, decides
+            // largest y^2 of the polynomial pass: every |y| < 0.72 exactly when
+            // every rounded y^2 < kTanhSmallSq (rounding is monotone, and the
+            // rounded square of 0.72f's predecessor lies below it), so one vote
+            // per position, on squares the polynomial forms anyway, decides
             float s2max = 0.f;
             // the position's layers; FULL = false: tanh by its polynomial half
-            // alone, for positions where every |y| stays below 0.8
+            // alone, for positions where every |y| stays below 0.72
             auto layers = [&](auto full) {
                 constexpr bool FULL = decltype(full)::value;
                 x = x0;
@@ -143,7 +142,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                 if (full_left == 0) {
                     s2max = 0.f;
                     layers(std::false_type{});
-                    if (__builtin_amdgcn_ballot_w64(!(s2max < 0.64f))) full_left = kChainFullRun + 1;
+                    if (__builtin_amdgcn_ballot_w64(!(s2max < kTanhSmallSq))) full_left = kChainFullRun + 1;
                 }
                 if (full_left > 0) {
                     layers(std::true_type{});
@@ -177,17 +176,19 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
     if (on) p.xin[(size_t)((cb + G + 1) & 1) * BD + chain] = xf;
 }
 
-// Sum over each aligned group of eight lanes, in every lane of the group:
-// swaps within quads (lane ^ 1, lane ^ 2), then the mirror within the group.
+// Sum over the eight lanes of a helper row (lanes 4q..4q+3 and 32+4q..+3 of
+// the wave), valid in the row's lanes of the lower half: swaps within quads
+// (lane ^ 1, lane ^ 2), then the quad of the upper half (v_permlane32_swap:
+// its second result holds lanes 32..63 in lanes 0..31).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float sum8(float v) {
+__device__ __forceinline__ float row_sum8(float v) {
     v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_move<0x141>(v);   // row_half_mirror
-    return v;
+    const auto hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return v + __uint_as_float(hi[1]);
 }
 
 // Lags of a chunk split between the two kinds of helper work: a lane's taps
@@ -302,9 +303,12 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
 
     // helper lanes: row hrho, taps h[seg + 8m] (zero for k < 2: the chain
     // adds tap 1, tap 0 is the red cell's own term); loads issued first
+    // a helper wave holds 8 rows, each in lanes 4q..4q+3 (segments 0..3) and
+    // 32+4q..+3 (segments 4..7): every half-wave then reads 8 rows x 4
+    // segments, 32 distinct banks (slot width 8 mod 32)
     const int hw = (wave & 3) ? wave - 1 - wave / 4 : -1;
-    const int hid = hw * kLanes + lane;
-    const int hrho = hid / S, seg = hid & (S - 1);
+    const int hrho = hw * (kLanes / S) + ((lane >> 2) & 7);
+    const int seg = (lane & 3) | ((lane >> 5) << 2);
     const bool helper = hw >= 0 && hrho < R && live(hrho);
     float hreg[kChunkTaps];
     if (hw >= 0) {
@@ -436,7 +440,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
                 dispatch<kChunkPullTaps / 8 - 1>(min((i + 2) >> 6, kChunkPullTaps / 8 - 1), [&](auto nf) {
                     acc = helper_sum<decltype(nf)::value>(xp, hreg, row0, hrho, seg < 2);
                 });
-                acc = sum8(acc);
+                acc = row_sum8(acc);
                 if (helper && seg == 0) xp[(size_t)(G - 2 - i) * SP + hrho] += acc;
             }
             if (G > 8 * kChunkPullTaps && i >= 1 && i <= G - 8 * kChunkPullTaps && helper) {

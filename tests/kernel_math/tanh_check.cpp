@@ -4,7 +4,7 @@
 // reciprocal are replaced by the C library's, so this checks the formula, the
 // polynomial and the branch point; on the GPU each adds about 1 ulp more.
 // Also: the polynomial half alone (tanh_small, the chains' first pass) gives
-// the same bits as tanh_chain wherever |y| < 0.8, the range it is kept for,
+// the same bits as tanh_chain wherever |y| < 0.72, the range it is kept for,
 // and the result is odd bit for bit (tanh(-y) = -tanh(y)).
 #include <cmath>
 #include <cstdint>
@@ -36,13 +36,13 @@ int main() {
                 const float pos = fi::tanh_chain(y);
                 if (!(got == -pos)) ++odd_diff;
             }
-            if (y < 0.8f) {
+            if (y < fi::kTanhSmall) {
                 const float alt = fi::tanh_small(v);
                 if (std::memcmp(&alt, &got, 4) != 0) ++small_diff;
             }
             const long double ref = tanhl((long double)v);
             const double e = (double)std::fabs((long double)got - ref) / ulp_of((float)ref);
-            if (y < 0.8f) {
+            if (y < fi::kTanhSmall) {
                 if (e > worst_small) worst_small = e, at_small = v;
             } else if (e > worst_big) {
                 worst_big = e, at_big = v;
@@ -58,8 +58,8 @@ int main() {
                      fi::tanh_chain(INFINITY) == 1.f && fi::tanh_chain(-INFINITY) == -1.f &&
                      fi::tanh_chain(-0.f) == 0.f && fi::tanh_chain(0.f) == 0.f &&
                      fi::tanh_chain(-tiny) == -tiny && fi::tanh_chain(tiny) == tiny;
-    std::printf("tanh_chain: %ld points; |y| < 0.8: %.3f ulp (at %.8g); |y| >= 0.8: %.3f ulp (at %.8g); "
-                "saturation %s; tanh_small differs at %ld points below 0.8; not odd at %ld points\n", n, worst_small,
+    std::printf("tanh_chain: %ld points; |y| < 0.72: %.3f ulp (at %.8g); |y| >= 0.72: %.3f ulp (at %.8g); "
+                "saturation %s; tanh_small differs at %ld points below 0.72; not odd at %ld points\n", n, worst_small,
                 at_small, worst_big, at_big, sat ? "ok" : "WRONG", small_diff, odd_diff);
-    return (worst_small <= 1.0 && worst_big <= 1.5 && sat && small_diff == 0 && odd_diff == 0) ? 0 : 1;
+    return (worst_small <= 1.0 && worst_big <= 1.6 && sat && small_diff == 0 && odd_diff == 0) ? 0 : 1;
 }
