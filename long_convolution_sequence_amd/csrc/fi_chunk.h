@@ -9,6 +9,7 @@
 #include <type_traits>
 
 #include "fi_device.h"
+#include "fi_tanh.h"
 
 namespace fi {
 

@@ -1,4 +1,4 @@
-// The tanh of the chunk kernels' red-cell chains (csrc/fi_device.h,
+// The tanh of the chunk kernels' red-cell chains (csrc/fi_tanh.h,
 // tanh_chain), compiled for the CPU: its error against tanh in long double over
 // every 7th float of [2^-30, 12], both signs.  The hardware exponential and
 // reciprocal are replaced by the C library's, so this checks the formula, the
@@ -12,7 +12,7 @@
 #include <cstring>
 
 #include "hip/hip_runtime.h"
-#include "../../long_convolution_sequence_amd/csrc/fi_device.h"
+#include "../../long_convolution_sequence_amd/csrc/fi_tanh.h"
 
 static double ulp_of(float v) {
     const float a = std::fabs(v);
