@@ -343,10 +343,10 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
         if (G >= 16) {
             // Items of 16 rows x 4 float4 per wave: the loads read 64
             // contiguous bytes of each of 16 rows, and the stores (four slots
-            // per float4; items of one row lie 4 kChunkSlot floats apart,
-            // 16 banks) meet at most two lanes per bank, where an item per
-            // row-major lane would put 32 lanes of a store on one bank.  A
-            // thread's loads all go out before its first store.
+            // per float4; the items of one row lie 4 kChunkSlot floats apart,
+            // on one bank) meet at most four lanes per bank, where an item
+            // per row-major lane would put all 64 lanes of a store on one
+            // bank.  A thread's loads all go out before its first store.
             constexpr int NB = 8, RW = 16, KW = 4;
             const int rg = (R + RW - 1) / RW;              // groups of 16 rows
             const int total = rg * (G >> 2) * RW;          // items, padded to whole row groups
