@@ -241,6 +241,31 @@ def test_chunk_workgroups_with_ragged_chain_counts(D):
     assert worst <= 1.0
 
 
+@pytest.mark.parametrize("M", [20, 23])
+def test_deep_stacks_in_chunks(M):
+    """The deepest stack kept in registers (M = 20) and one past it (M = 23: the chain reads its layers
+    from LDS), three chains per chunk workgroup: 60 and 69 rows, so the last helper wave holds a part
+    of a row group.  Teacher-forced prefill (positions in chunks) and a free-running generation with
+    both maps tanh, each replayed layer by layer against the oracle."""
+    B, D, L = 1, 700, 1024
+    say(f"case deep stack in chunks M={M} B={B} D={D} L={L} G=256")
+    h = _filters(M, D, L, 51, decay=150.0) * 0.1
+    x = np.random.default_rng(52).standard_normal((L, B, D)).astype(np.float32)
+    chans = [0, 1, 2, 3, 4, 5, 350, 696, 697, 698, 699]
+    with fi.Context(_cuda(h), B, tau_split=8, record=True, map=fi.MAP_IDENTITY) as ctx:
+        ctx.prefill(_cuda(x))
+        worst = check_replay(h, ctx, chans=chans)
+    say(f"  teacher-forced replay worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+    with fi.Context(_cuda(h), B, tau_split=8, record=True) as ctx:
+        ctx.set_input(_cuda(x[0]))
+        y = ctx.generate(L).cpu().numpy()
+        worst = check_replay(h, ctx, chans=chans)
+    say(f"  free-running replay worst error/tolerance {worst:.3e}, max |y| {np.abs(y).max():.3g}")
+    assert worst <= 1.0
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("L", [1, 2, 4, 8, 32])
 def test_edge_lengths_and_ragged_chain_counts(L):
     M, B, D = 2, 3, 7
