@@ -167,7 +167,7 @@ def traffic_summary(args):
             if "copyBuffer" in name:
                 copies.append((int(r["Dispatch_Id"]), v))
                 continue
-            m = re.search(r"k_fft_(tile2|tile|sub_fwd|sub_inv)<(\d+)>", name)
+            m = re.search(r"k_fft_(tile2|tile|sub_fwd|sub_inv)<(\d+)(?:, *\d+)?>", name)
             if not m:
                 continue
             kind, lg = m.group(1), int(m.group(2))

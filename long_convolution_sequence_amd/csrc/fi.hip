@@ -403,10 +403,10 @@ hipError_t launch_spectrum_n(fi_ctx *c, int logn, hipStream_t s, float4 *dst, lo
 hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
                           int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
     const int LOGV = c->opt.fft_max_log2;
-    const SubFwdK kf = sub_fwd_k(LOGV);
-    const SubInvK ki = sub_inv_k(LOGV);
-    if (!kf || !ki) return hipErrorInvalidValue;
     const int K = sub_k(q, LOGV);
+    const SubFwdK kf = sub_fwd_k(LOGV);
+    const SubInvK ki = sub_inv_k(LOGV, K);
+    if (!kf || !ki) return hipErrorInvalidValue;
     const long long rows = (long long)c->M * c->B * c->D;
     const dim3 blk(fft_tpb(LOGV));
     launch_k(kf, dim3((unsigned)(rows * K)), blk, s, ev0, nullptr, c->dev, rd, c->scratch, K);

@@ -517,19 +517,39 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
     }
 }
 
+// Raw buffer load of 16 bytes at byte offset voff + soff of resource r
+// (voff per lane, soff scalar); reads past the resource's size return zeros.
+// Word 3 of a raw buffer resource on this architecture.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ float4 buffer_load4(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+// An empty statement that the compiler must place after the values of Z are
+// formed and that no memory access crosses.
+template <int CH>
+__device__ __forceinline__ void hold_after(float4 (&Z)[CH]) {
+#pragma unroll
+    for (int m = 0; m < CH; ++m) asm volatile("" : "+v"(Z[m].x), "+v"(Z[m].y), "+v"(Z[m].z), "+v"(Z[m].w)::"memory");
+}
+
 // k_fft_sub_inv: per (l, b, c, o), Z = sum_i A_i * G_{K+o-i}, then the inverse
 // transform and accumulation of its exact upper half into output sub-block o.
 // One launch covers output sub-blocks o0 .. o0+nO-1.  nfix > 0 names the
 // position directly (a launch that runs after later positions have already
 // overwritten the position slots).
-template <int LOGV>
+// KT > 0 fixes K = KT at compile time (the products then run as straight-line
+// code, with no loop-carried loads in flight); KT = 0 takes K at run time.
+template <int LOGV, int KT>
 __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int rd, const float4 *__restrict__ scratch,
-                                                                     const float4 *__restrict__ spec, int K,
+                                                                     const float4 *__restrict__ spec, int Kr,
                                                                      int o0, int nO, long long nfix, int advance) {
     using S = FftShape<LOGV>;
     constexpr int N = S::N, TT = S::TT, R0 = S::R0, QLOG0 = S::QLOG0, HALF0 = S::HALF0;
     __shared__ float2 smem[S::LDS];
     const int lt = threadIdx.x;
+    const int K = KT > 0 ? KT : Kr;
     const long long U = (long long)K * N;
     const long long n = nfix > 0 ? nfix : position_of(p, rd);
     const long long t = n - 1;
@@ -537,38 +557,51 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
     long long tile;
     int o;
     xcd_tile(blockIdx.x, (long long)p.M * p.B * p.D, nO, tile, o);
-    o += o0;
-    const int c = (int)(tile % p.D);
-    const int l = (int)(tile / ((long long)p.D * p.B));
+    // uniform: kept in scalar registers, so the loads below take scalar bases
+    tile = __builtin_amdgcn_readfirstlane((int)tile);
+    o = __builtin_amdgcn_readfirstlane(o + o0);
+    const int c = __builtin_amdgcn_readfirstlane((int)(tile % p.D));
+    const int l = __builtin_amdgcn_readfirstlane((int)(tile / ((long long)p.D * p.B)));
     const size_t row = (size_t)tile * (size_t)p.L;
     float2 *adst = reinterpret_cast<float2 *>(p.buf + row + t + 1 + (long long)o * N);
     const float4 *A = scratch + (size_t)tile * K * (N / 2);
     const float4 *G = spec + ((size_t)l * p.D + c) * (size_t)(2 * K - 1) * (N / 2);
     float2 *X = smem;
-    // Z = sum_i A_i * G_{K+o-i} for this thread's pairs, four pairs at a time.
-    // Step s covers chunk s / K and sub-block i = s % K; the loads of step
-    // s + 1 are in flight while step s multiplies (K is even).
+    // Z = sum_i A_i * G_{K+o-i} for this thread's pairs, four pairs at a time:
+    // chunk c (pairs c*CH .. c*CH+CH-1) runs the K sub-blocks in steps
+    // s = c*K + i.  The loads of step s + 1 are in flight while step s
+    // multiplies; the prefetch is issued every time (the last one repeats the
+    // final step's loads), so that the wait before each step's products
+    // leaves the next step's loads outstanding.  K is a power of two.
     constexpr int PAIRS = (N / 2 + TT - 1) / TT;
-    constexpr int CH = 4;
+    constexpr int CH = 4, NCH = PAIRS / CH;
     static_assert(PAIRS % CH == 0, "pairs per thread");
-    const int steps = (PAIRS / CH) * K;
+    const int kl = __builtin_ctz((unsigned)K);
+    const int steps = NCH * K;
+    // buffer loads: a resource over the tile's bins and one over the row's
+    // offset spectra, the step's offset in a scalar register and one lane
+    // offset, so no load needs vector address arithmetic
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)A, 0, (int)((size_t)K * (N / 2) * sizeof(float4)), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)G, 0, (int)((size_t)(2 * K - 1) * (N / 2) * sizeof(float4)), kBufferWord3);
+    const unsigned vo = (unsigned)lt * (unsigned)sizeof(float4);
     auto load = [&](int st, float4(&a)[CH], float4(&g)[CH]) {
-        const int m0 = (st / K) * CH, i = st % K;
-        const float4 *Ai = A + (size_t)i * (N / 2);
-        const float4 *Gi = G + (size_t)(K + o - i - 1) * (N / 2);
+        const int i = st & (K - 1);
+        const int off = (st >> kl) * CH * TT;
+        const int sa = (i * (N / 2) + off) * (int)sizeof(float4);
+        const int sg = ((K + o - i - 1) * (N / 2) + off) * (int)sizeof(float4);
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            const int j = lt + (m0 + m) * TT;
-            a[m] = Ai[j];
-            g[m] = Gi[j];
+            a[m] = buffer_load4(rA, vo, sa + m * TT * (int)sizeof(float4));
+            g[m] = buffer_load4(rG, vo, sg + m * TT * (int)sizeof(float4));
         }
     };
     float4 Z[CH];
-    auto mac = [&](int st, const float4(&a)[CH], const float4(&g)[CH]) {
-        const int m0 = (st / K) * CH;
+    auto mac = [&](int c, const float4(&a)[CH], const float4(&g)[CH]) {
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            if (lt + (m0 + m) * TT == 0) {  // (G_0, G_N) real, G_{N/2} complex
+            if (lt + (c * CH + m) * TT == 0) {  // (G_0, G_N) real, G_{N/2} complex
                 Z[m].x = fmaf(a[m].x, g[m].x, Z[m].x);
                 Z[m].y = fmaf(a[m].y, g[m].y, Z[m].y);
                 const float2 h = cmul(make_float2(a[m].z, a[m].w), make_float2(g[m].z, g[m].w));
@@ -581,11 +614,36 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
             }
         }
     };
-    // re-pack the finished chunk for the inverse transform
-    auto flush = [&](int m0) {
+    float4 a0[CH], g0[CH], a1[CH], g1[CH];
+    load(0, a0, g0);
+    static_for<0, NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        // this chunk's pair twiddles for the re-packing, read with its first
+        // loads, so that no wait on them drains the step loads in flight
+        float2 wc[CH];
+#pragma unroll
+        for (int m = 0; m < CH; ++m) wc[m] = p.ptw[N / 2 + lt + (c * CH + m) * TT];
+#pragma unroll
+        for (int m = 0; m < CH; ++m) Z[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < K; i += 2) {
+            const int st = c * K + i;
+            load(st + 1, a1, g1);
+            mac(c, a0, g0);
+            // each prefetch lands in the registers the products before it have
+            // just read: the empty statement takes the sums as operands and
+            // orders memory, so no load is hoisted above the products that free
+            // its registers (hoisted, the loads need registers of their own and
+            // spill)
+            hold_after(Z);
+            load(st + 2 < steps ? st + 2 : st + 1, a0, g0);
+            mac(c, a1, g1);
+            hold_after(Z);
+        }
+        // re-pack the finished chunk for the inverse transform
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            const int j = lt + (m0 + m) * TT;
+            const int j = lt + (c * CH + m) * TT;
             if (j == 0) {
                 const float Z0 = Z[m].x, ZN = Z[m].y;
                 X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
@@ -593,34 +651,23 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
             } else {
                 const PairSlot ps = pair_slot(LOGV, j);
                 float2 D1, D2;
-                pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w), p.ptw[N / 2 + j], D1, D2);
+                pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w), wc[m], D1, D2);
                 X[lpad(ps.pj)] = D1;
                 X[lpad(ps.pm)] = D2;
             }
-            Z[m] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    };
-#pragma unroll
-    for (int m = 0; m < CH; ++m) Z[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 a0[CH], g0[CH], a1[CH], g1[CH];
-    load(0, a0, g0);
-    for (int st = 0; st < steps; st += 2) {
-        load(st + 1, a1, g1);
-        mac(st, a0, g0);
-        if (st + 2 < steps) load(st + 2, a0, g0);
-        mac(st + 1, a1, g1);
-        if ((st + 1) % K == K - 1) flush(((st + 1) / K) * CH);
-    }
+    });
     const float2 wi = group_root<LOGV, S::NPASS - 1>(lt, p.twid, p.logNT);
     __syncthreads();
     const float2 w0 = inverse_groups<LOGV, S::NPASS - 1>(X, lt, p.twid, p.logNT, wi);
+    // the pending sums of the output sub-block, read during the last group
+    float2 acc[HALF0];
+#pragma unroll
+    for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
     float2 v[1 << R0];
 #pragma unroll
     for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
     dit_group_w<R0>(v, w0);
-    float2 acc[HALF0];
-#pragma unroll
-    for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
     finish_position(p, n, advance);

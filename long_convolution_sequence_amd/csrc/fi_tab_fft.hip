@@ -42,11 +42,20 @@ SubFwdK sub_fwd_k(int logv) {
     }
 }
 
-SubInvK sub_inv_k(int logv) {
+template <int LOGV>
+SubInvK sub_inv_kk(int K) {
+    switch (K) {
+        case 4: return &k_fft_sub_inv<LOGV, 4>;
+        case 8: return &k_fft_sub_inv<LOGV, 8>;
+        default: return &k_fft_sub_inv<LOGV, 0>;
+    }
+}
+
+SubInvK sub_inv_k(int logv, int K) {
     switch (logv) {
-        case 12: return &k_fft_sub_inv<12>;
-        case 13: return &k_fft_sub_inv<13>;
-        case 14: return &k_fft_sub_inv<14>;
+        case 12: return sub_inv_kk<12>(K);
+        case 13: return sub_inv_kk<13>(K);
+        case 14: return sub_inv_kk<14>(K);
         default: return nullptr;
     }
 }

@@ -29,7 +29,7 @@ using HyStepK = void (*)(Dev, int, int);                                    // k
 FftTileK fft_tile_k(int logn);     // one-workgroup transform, 2 <= logn <= 14
 FftTileK fft_tile2_k(int logm);    // two halves of 2^logm, 12 <= logm <= 14
 SubFwdK sub_fwd_k(int logv);       // split classes, sub-blocks of 2^logv, 12..14
-SubInvK sub_inv_k(int logv);
+SubInvK sub_inv_k(int logv, int K);   // K sub-blocks (a power of two, >= 4)
 SpectrumK spectrum_k(int logn);    // 2..14
 SpectrumK spectrum2_k(int logm);   // 12..14
 PreFftK pre_fft_k(int logn);       // 2..14

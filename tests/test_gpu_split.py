@@ -60,6 +60,16 @@ def test_split_blocks_default_width_full_length():
     assert worst <= 1.0
 
 
+def test_split_blocks_k16_full_length():
+    """Width 2^12 at L = 2^17: split blocks with K = 4, 8 and 16 sub-blocks
+    (K = 16 takes the kernel whose sub-block count is not fixed at compile time)."""
+    M, B, D, L = 1, 1, 2, 131072
+    say(f"case two-half block 2^13, split blocks 2^14, 2^15, 2^16 (K=4, 8, 16) M={M} B={B} D={D} L={L}")
+    worst = _run_teacher_forced(M, B, D, L, 12, 23)
+    say(f"  worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+
+
 @pytest.mark.parametrize("graphs", [True, False])
 def test_deferred_split_sub_blocks_change_nothing(graphs):
     """Feedback stack with split classes 2^14 and 2^15 (width 2^12): generation
