@@ -63,7 +63,7 @@ constexpr int kChunkSlot = 104;
 static_assert(kChunkSlot >= kChunkMaxRows && kChunkSlot % 32 == 8, "slot width");
 // zero rows after the slots: the helper taps that lie before the chunk read them
 constexpr int kChunkZeroRows = 64;
-// positions a chain stays on the full tanh after its polynomial pass failed
+// positions a chain stays on a costlier tanh pass after the cheaper one failed
 constexpr int kChainFullRun = 128;
 // chunk kernel variants: records every layer's input and output; both maps tanh
 constexpr int kChunkRec = 1, kChunkTanh = 2;
@@ -92,6 +92,7 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
     }
     const bool map_id = !TANH_ALL && p.map != 0, fb_id = !TANH_ALL && p.fb != 0;
     int full_left = 0;                         // wave-uniform: positions left on the full tanh
+    int small_left = 0;                        // and on the polynomial pieces
     for (int i = 0; i < G; ++i) {
         const long long t = cb + 1 + i;        // position
         float x = xs ? xs[i * CH + jr] : xf;   // teacher-forced inputs, staged in LDS
@@ -102,15 +103,17 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
 #pragma unroll
             for (int k = 0; k < MT; ++k) a[k] = fmaf(h1[k], xq[k], cur[k]);   // + tap 1 of slot i-1
             const float x0 = x;
-            // largest y^2 of the polynomial pass: every |y| < 0.72 exactly when
+            // largest y^2 of a polynomial pass: every |y| < 0.72 exactly when
             // every rounded y^2 < kTanhSmallSq (rounding is monotone, and the
-            // rounded square of 0.72f's predecessor lies below it), so one vote
-            // per position, on squares the polynomial forms anyway, decides
+            // rounded square of 0.72f's predecessor lies below it), and every
+            // |y| < 0.125 exactly when every rounded y^2 < 2^-6; so one vote per
+            // position, on squares the polynomials form anyway, decides
             float s2max = 0.f;
-            // the position's layers; FULL = false: tanh by its polynomial half
-            // alone, for positions where every |y| stays below 0.72
-            auto layers = [&](auto full) {
-                constexpr bool FULL = decltype(full)::value;
+            // the position's layers with tanh by piece TIER: 0 the first piece
+            // alone (for positions where every |y| stays below 0.125), 1 the
+            // polynomial pieces (below 0.72), 2 the full tanh
+            auto layers = [&](auto tier) {
+                constexpr int TIER = decltype(tier)::value;
                 x = x0;
 #pragma unroll
                 for (int k = 0; k < MT; ++k) {
@@ -123,8 +126,8 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                             p.recy[r] = y;
                         }
                     }
-                    const float th = FULL ? tanh_chain(y) : tanh_small(y);
-                    if constexpr (!FULL) s2max = fmaxf(s2max, y * y);
+                    const float th = TIER == 2 ? tanh_chain(y) : TIER == 1 ? tanh_small(y) : tanh_tiny(y);
+                    if constexpr (TIER < 2) s2max = fmaxf(s2max, y * y);
                     if constexpr (TANH_ALL) {
                         x = th;
                     } else {
@@ -133,24 +136,40 @@ __device__ __forceinline__ void chain_run(const Dev &p, float *xp, int G, const 
                 }
             };
             if constexpr (TANH_ALL) {
-                // Both maps tanh.  The polynomial pass runs first, which keeps
-                // the exponential's two transcendental steps off the chain; if
-                // some lane of the wave left its range, the position runs again
-                // with the full tanh (same values where both apply), and so do
-                // the next kChainFullRun positions before the polynomial pass
-                // is tried again (activations that stay large then cost one
-                // extra pass per kChainFullRun positions).
+                // Both maps tanh.  A position runs the cheapest pass first: the
+                // first piece alone, which keeps the polynomial's higher terms
+                // and the exponential off the chain.  If some lane of the wave
+                // left its range, the position runs again with the next pass
+                // (same values where both apply), and so do the next
+                // kChainFullRun positions before the cheaper pass is tried
+                // again (activations that stay large then cost one extra pass
+                // per kChainFullRun positions).
+                using T0 = std::integral_constant<int, 0>;
+                using T1 = std::integral_constant<int, 1>;
+                using T2 = std::integral_constant<int, 2>;
                 if (full_left == 0) {
-                    s2max = 0.f;
-                    layers(std::false_type{});
-                    if (__builtin_amdgcn_ballot_w64(!(s2max < kTanhSmallSq))) full_left = kChainFullRun + 1;
+                    if (small_left == 0) {
+                        s2max = 0.f;
+                        layers(T0{});
+                        if (__builtin_amdgcn_ballot_w64(!(s2max < kTanhTinySq))) small_left = kChainFullRun + 1;
+                    }
+                    if (small_left > 0) {
+                        s2max = 0.f;
+                        layers(T1{});
+                        if (__builtin_amdgcn_ballot_w64(!(s2max < kTanhSmallSq))) {
+                            // after the full run, the polynomial pass is the one tried again
+                            full_left = kChainFullRun + 1;
+                            small_left = kChainFullRun + 1;
+                        }
+                        --small_left;
+                    }
                 }
                 if (full_left > 0) {
-                    layers(std::true_type{});
+                    layers(T2{});
                     --full_left;
                 }
             } else {
-                layers(std::true_type{});
+                layers(std::integral_constant<int, 2>{});
             }
             if (on) {
 #pragma unroll
@@ -313,12 +332,14 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     const bool helper = hw >= 0 && hrho < R && live(hrho);
     float hreg[kChunkTaps];
     if (hw >= 0) {
-        // the lane's 32 taps lie together in the tap table: eight 16-byte loads
+        // the lane's 32 taps lie together in the tap table: eight 16-byte loads,
+        // of which a chunk of G positions needs the first G/32 (taps 4q..4q+3 of
+        // a lane are lags seg + 32q + 8j, all at least G from q = G/32 on)
         const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
                                             seg * kChunkTaps);
 #pragma unroll
         for (int q = 0; q < kChunkTaps / 4; ++q) {
-            const float4 v = tp[q];
+            const float4 v = 32 * q < G ? tp[q] : make_float4(0.f, 0.f, 0.f, 0.f);
             hreg[4 * q] = v.x;
             hreg[4 * q + 1] = v.y;
             hreg[4 * q + 2] = v.z;

@@ -568,8 +568,8 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
     const float4 *G = spec + ((size_t)l * p.D + c) * (size_t)(2 * K - 1) * (N / 2);
     float2 *X = smem;
     // Z = sum_i A_i * G_{K+o-i} for this thread's pairs, four pairs at a time:
-    // chunk c (pairs c*CH .. c*CH+CH-1) runs the K sub-blocks in steps
-    // s = c*K + i.  The loads of step s + 1 are in flight while step s
+    // chunk q (pairs q*CH .. q*CH+CH-1) runs the K sub-blocks in steps
+    // s = q*K + i.  The loads of step s + 1 are in flight while step s
     // multiplies; the prefetch is issued every time (the last one repeats the
     // final step's loads), so that the wait before each step's products
     // leaves the next step's loads outstanding.  K is a power of two.
@@ -598,10 +598,10 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
         }
     };
     float4 Z[CH];
-    auto mac = [&](int c, const float4(&a)[CH], const float4(&g)[CH]) {
+    auto mac = [&](int q, const float4(&a)[CH], const float4(&g)[CH]) {
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            if (lt + (c * CH + m) * TT == 0) {  // (G_0, G_N) real, G_{N/2} complex
+            if (lt + (q * CH + m) * TT == 0) {  // (G_0, G_N) real, G_{N/2} complex
                 Z[m].x = fmaf(a[m].x, g[m].x, Z[m].x);
                 Z[m].y = fmaf(a[m].y, g[m].y, Z[m].y);
                 const float2 h = cmul(make_float2(a[m].z, a[m].w), make_float2(g[m].z, g[m].w));
@@ -616,20 +616,20 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
     };
     float4 a0[CH], g0[CH], a1[CH], g1[CH];
     load(0, a0, g0);
-    static_for<0, NCH>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
+    static_for<0, NCH>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
         // this chunk's pair twiddles for the re-packing, read with its first
         // loads, so that no wait on them drains the step loads in flight
         float2 wc[CH];
 #pragma unroll
-        for (int m = 0; m < CH; ++m) wc[m] = p.ptw[N / 2 + lt + (c * CH + m) * TT];
+        for (int m = 0; m < CH; ++m) wc[m] = p.ptw[N / 2 + lt + (q * CH + m) * TT];
 #pragma unroll
         for (int m = 0; m < CH; ++m) Z[m] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < K; i += 2) {
-            const int st = c * K + i;
+            const int st = q * K + i;
             load(st + 1, a1, g1);
-            mac(c, a0, g0);
+            mac(q, a0, g0);
             // each prefetch lands in the registers the products before it have
             // just read: the empty statement takes the sums as operands and
             // orders memory, so no load is hoisted above the products that free
@@ -637,13 +637,13 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
             // spill)
             hold_after(Z);
             load(st + 2 < steps ? st + 2 : st + 1, a0, g0);
-            mac(c, a1, g1);
+            mac(q, a1, g1);
             hold_after(Z);
         }
         // re-pack the finished chunk for the inverse transform
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            const int j = lt + (c * CH + m) * TT;
+            const int j = lt + (q * CH + m) * TT;
             if (j == 0) {
                 const float Z0 = Z[m].x, ZN = Z[m].y;
                 X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));

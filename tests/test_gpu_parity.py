@@ -280,13 +280,16 @@ def test_edge_lengths_and_ragged_chain_counts(L):
                 ctx.step(_cuda(x[0]))
 
 
-@pytest.mark.parametrize("scale", [0.02, 1.0])
+@pytest.mark.parametrize("scale", [0.002, 0.05, 1.0])
 def test_chunk_kernel_with_and_without_records_agree(scale):
-    """The chunk kernel the bench runs (no records) against the one the oracle replays check (records
-    on): the same arithmetic, so the outputs agree bit for bit.  scale 0.02 keeps every |y| below 0.8
-    (the chains' polynomial pass holds); scale 1.0 leaves that range (the full-tanh reruns).  The
-    split is pinned: a calibrated one is timed per context and can differ between the two, and with
-    it the chunk length and the order of the additions."""
+    """The chunk kernel the bench runs (no records) against the one the oracle replay checks (records
+    on): the same arithmetic, so the outputs agree bit for bit; and the recorded run replays against
+    the oracle, with every layer's input (and the fed-back input) the tanh of the output before it
+    to 2 ulp.  The scale picks the
+    chains' tanh passes: 0.002 keeps every |y| below 0.125 (the first piece alone holds), 0.05 leaves
+    that range but stays below 0.72 (the polynomial pass), 1.0 leaves that too (the full-tanh runs).
+    The split is pinned: a calibrated one is timed per context and can differ between the two, and
+    with it the chunk length and the order of the additions."""
     M, B, D, L = 3, 2, 37, 2048
     say(f"case chunk kernel records on/off scale={scale} M={M} B={B} D={D} L={L}")
     h = _filters(M, D, L, 31, decay=200.0) * scale
@@ -296,9 +299,23 @@ def test_chunk_kernel_with_and_without_records_agree(scale):
         with fi.Context(_cuda(h), B, record=rec, tau_split=8) as ctx:
             ctx.set_input(_cuda(x1))
             outs.append(ctx.generate(L).cpu().numpy())
-    big = float(np.abs(outs[0]).max())
-    say(f"  max |y| {big:.3g}")
-    assert (big < 0.8) == (scale < 0.5)
+            if rec:
+                worst = check_replay(h, ctx)
+                ulps = 0.0
+                big = 0.0
+                for l in range(M):
+                    yl = ctx.history(l, 1).cpu().numpy().astype(np.float64)
+                    big = max(big, float(np.abs(yl).max()))
+                    # the next layer's inputs, or for the last layer the fed-back input of the next position
+                    t = np.tanh(yl) if l + 1 < M else np.tanh(yl[:-1])
+                    xn = ctx.history(l + 1, 0).cpu().numpy() if l + 1 < M else ctx.history(0, 0).cpu().numpy()[1:]
+                    ulps = max(ulps, float((np.abs(xn - t) / np.maximum(np.abs(t) * 2.0 ** -23, 1e-45)).max()))
+    say(f"  max |y| over all layers {big:.3g}; replay worst error/tolerance {worst:.3e}; "
+        f"layer inputs vs tanh of the layer before: {ulps:.2f} x 2^-23 relative")
+    assert worst <= 1.0
+    assert ulps <= 2.0
+    lo, hi = {0.002: (0.0, 0.125), 0.05: (0.125, 0.72), 1.0: (0.72, np.inf)}[scale]
+    assert lo <= big < hi
     assert np.array_equal(outs[0], outs[1])
 
 
