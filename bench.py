@@ -306,6 +306,8 @@ def main():
     ap.add_argument("--no-dd-leg", action="store_true", help="skip the data-dependent-filter timing")
     ap.add_argument("--no-pareto-leg", action="store_true", help="skip the per-size path timing")
     ap.add_argument("--no-hyena-leg", action="store_true", help="skip the Hyena-style block workload leg")
+    ap.add_argument("--no-chunk-leg", action="store_true",
+                    help="skip the generation with chunks twice as long (throughput against p99 latency)")
     ap.add_argument("--hyena-positions", type=int, default=4096,
                     help="positions of the Hyena-style block leg (the whole L with --workload 5)")
     ap.add_argument("--positions", type=int, default=0, help="profile aid: generate only a prefix")
@@ -482,6 +484,30 @@ def main():
                  "note": "one generation with fi_options.defer_wide on: a split gray block computes its "
                          "first output sub-block before the next position and the rest on a second "
                          "stream; not part of the timed steps above"}
+    # one generation with chunks twice as long (one more direct class): the
+    # calibration picks the chunk length for throughput, but the first position
+    # of a chunk and the one whose FFT block ends it take the boundary's cost,
+    # two of every G positions, which sets the p99 once 2/G passes 1%
+    longer = None
+    G2 = 1 << (split + 1)
+    if not args.no_chunk_leg and args.tau_split < 0 and split + 1 < w.P and G2 <= 256:
+        hd2 = torch.from_numpy(h).cuda()
+        lctx = fi.Context(hd2, w.B, tau_split=split + 1)
+        del hd2
+        one_step(lctx)
+        dt = one_step(lctx)
+        ll = np.diff(lctx.stamps(1, L).astype(np.float64)) / 100.0
+        lctx.close()
+        del lctx
+        torch.cuda.empty_cache()
+        longer = {"chunk_positions": G2, "tokens_per_s": round(L * w.B / dt, 1),
+                  "latency_us": {"p50": round(float(np.percentile(ll, 50)), 2),
+                                 "p99": round(float(np.percentile(ll, 99)), 2),
+                                 "max": round(float(ll.max()), 1)},
+                  "note": f"one generation (after one warm-up) with the first FFT class pinned to 2^{split + 1}: "
+                          f"chunks of {G2} positions instead of the calibrated {1 << split}; not part of the "
+                          f"timed steps above"}
+        log(f"bench: chunks of {G2}: {longer['tokens_per_s']:,.0f} tokens/s, p99 {longer['latency_us']['p99']} us")
     traffic = measured_traffic(w, {q: int(blk_n[q]) for q in range(w.P) if blk_n[q] > 0})
     roofline = {
         "bound": "hbm",
@@ -674,6 +700,7 @@ def main():
         "roofline": roofline,
         "chunk_kernel": chunk,
         "defer_wide": defer,
+        "longer_chunks": longer,
         "lazy_gpu": lazy,
         "ablations": ablations,
         "prefill": prefill,
