@@ -510,7 +510,7 @@ hipError_t launch_hyena_block(fi_ctx *c, int rd, hipStream_t s, const float *xex
         hipLaunchKernelGGL(ku, dim3((4 * D / kBlockRows + 3) / 4), dim3(256), 0, s, c->dev, rd, l);
         hipLaunchKernelGGL(kd, dim3((D + kBlockRows - 1) / kBlockRows), dim3(256), 0, s, c->dev, rd, l);
     }
-    hipLaunchKernelGGL(k_hy_out, dim3(1), dim3(256), 0, s, c->dev, rd, yext);
+    hipLaunchKernelGGL(k_hy_out, dim3((unsigned)((B * D + 255) / 256)), dim3(256), 0, s, c->dev, rd, yext);
     return hipGetLastError();
 }
 

@@ -112,6 +112,11 @@ __global__ void __launch_bounds__(256) k_hy_proj(Dev p, int rd, int l, const flo
     const int lane = threadIdx.x & 63;
     const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (c >= D) return;                            // no barrier below
+    // the red cell's head and pending sum (lane b: chain b*D + c), read first so
+    // that their latency passes under the input and weight loads
+    const size_t rcell = ring(p, n, l) + (size_t)(lane < B ? lane : 0) * D + c;
+    const float h0 = p.hh[head(p, l, 0, c)];
+    const float pend = lane < B ? p.ar[rcell] : 0.f;
     WaveIn<B> in;
     if (l == 0) {
         load_in<B>(in, xext ? xext : p.xin + (size_t)(n & 1) * BD, D, 0, D, nullptr, lane);
@@ -152,14 +157,13 @@ __global__ void __launch_bounds__(256) k_hy_proj(Dev p, int rd, int l, const flo
     wave_dot<B>(W + (size_t)c * D, in, D, lane, u);
     wave_dot<B>(W + (size_t)(D + c) * D, in, D, lane, v);
     wave_dot<B>(W + (size_t)(2 * D + c) * D, in, D, lane, w);
-    const float h0 = p.hh[head(p, l, 0, c)];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         if (lane == b) {
             const int chain = b * D + c;
-            const size_t r = ring(p, n, l) + chain;
+            const size_t r = rcell;
             const float q = u[b] * w[b];
-            const float cv = fmaf(h0, q, p.ar[r]);
+            const float cv = fmaf(h0, q, pend);
             p.xr[r] = q;
             if (p.recx) {
                 const size_t rr = ((size_t)(n - 1) * p.M + l) * BD + chain;
@@ -241,6 +245,8 @@ __device__ __forceinline__ void row_rms(const float *z, float *rs, int B, int D)
 }
 
 // After the last layer: a^{M-1} = RMSNorm(z); output, record, next input tanh(a).
+// Each workgroup takes its stretch of the B*D outputs (and forms every row's
+// norm itself: B*D values, far less than the outputs' own latency).
 static __global__ void __launch_bounds__(256) k_hy_out(Dev p, int rd, float *yext) {
     __shared__ float rs[kBlockMaxB];
     const long long n = position_of(p, rd);
@@ -248,7 +254,7 @@ static __global__ void __launch_bounds__(256) k_hy_out(Dev p, int rd, float *yex
     const int B = p.B, D = p.D, BD = B * D;
     row_rms(p.zb, rs, B, D);
     __syncthreads();
-    for (int i = threadIdx.x; i < BD; i += blockDim.x) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < BD; i += gridDim.x * blockDim.x) {
         const float a = p.zb[i] * rs[i / D];
         p.ylast[(size_t)(n - 1) * BD + i] = a;
         if (yext) yext[i] = a;
