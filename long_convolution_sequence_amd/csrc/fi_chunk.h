@@ -217,6 +217,9 @@ __device__ __forceinline__ float row_sum8(float v) {
 // lags, only in chunks longer than 8 kChunkPullTaps) are pushed from each
 // source one position after it is known.
 constexpr int kChunkPullTaps = 24;
+// s_waitcnt vmcnt(0), the other counters left free (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = 0x0F70;
 static_assert(kChunkPullTaps % 8 == 0 && kChunkPullTaps <= kChunkTaps, "pulled taps come in groups of eight");
 
 // f(std::integral_constant<int, v>) for the v in [0, N] equal to the runtime
@@ -331,24 +334,34 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     const int seg = (lane & 3) | ((lane >> 5) << 2);
     const bool helper = hw >= 0 && hrho < R && live(hrho);
     float hreg[kChunkTaps];
+    // the lane's 32 taps lie together in the tap table: eight 16-byte loads,
+    // of which a chunk of G positions needs the first G/32 (taps 4q..4q+3 of
+    // a lane are lags seg + 32q + 8j, all at least G from q = G/32 on).  The
+    // groups used from the first position on (q < 2: lags below 64; the
+    // pushed taps) are loaded here; the later pulled groups after the set-up's
+    // loads, so that the set-up does not wait for them: their first use is at
+    // position 62.  No mask waits for a load either: the table holds zeros at
+    // lags 0 and 1, a lane without a helper row discards its sums, and a
+    // group is loaded only when its lags lie in the chunk, but for the one
+    // group of chunks shorter than 32, whose lags past the chunk are zeroed.
+    constexpr int QP = kChunkPullTaps / 4;                 // groups q >= QP are pushed
+    const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
+                                        seg * kChunkTaps);
+    auto tap_group = [&](int q) {
+        const float4 v = 32 * q < G ? tp[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        hreg[4 * q] = v.x;
+        hreg[4 * q + 1] = v.y;
+        hreg[4 * q + 2] = v.z;
+        hreg[4 * q + 3] = v.w;
+    };
     if (hw >= 0) {
-        // the lane's 32 taps lie together in the tap table: eight 16-byte loads,
-        // of which a chunk of G positions needs the first G/32 (taps 4q..4q+3 of
-        // a lane are lags seg + 32q + 8j, all at least G from q = G/32 on)
-        const float4 *tp = (const float4 *)(p.htap + (size_t)(helper ? trow(hrho) : 0) * kChunkTapRow +
-                                            seg * kChunkTaps);
 #pragma unroll
-        for (int q = 0; q < kChunkTaps / 4; ++q) {
-            const float4 v = 32 * q < G ? tp[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            hreg[4 * q] = v.x;
-            hreg[4 * q + 1] = v.y;
-            hreg[4 * q + 2] = v.z;
-            hreg[4 * q + 3] = v.w;
-        }
+        for (int q = 0; q < kChunkTaps / 4; ++q)
+            if (q < 2 || q >= QP) tap_group(q);
+        if (G < 32) {
 #pragma unroll
-        for (int m = 0; m < kChunkTaps; ++m) {
-            const int k = seg + S * m;
-            if (!(helper && k >= 2 && k < G)) hreg[m] = 0.f;
+            for (int m = 0; m < 4; ++m)
+                if (seg + S * m >= G) hreg[m] = 0.f;
         }
     }
 
@@ -410,6 +423,13 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
                 xs[e] = c0 + j < BD ? xseq[(size_t)i * BD + c0 + j] : 0.f;
             }
     }
+    // every load so far is in, on every path (so that no use of the early
+    // groups waits for the groups loaded next)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (hw >= 0) {
+#pragma unroll
+        for (int q = 2; q < QP; ++q) tap_group(q);
+    }
     __syncthreads();
 
     float *hist = p.buf + (helper ? grow(hrho) + cb : 0);   // a helper row's positions of the chunk
@@ -448,7 +468,7 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
         // per row, the last positions of a chunk with 255; split this way the
         // pulled lags stop growing at K-1 and the pushed ones shrink as the
         // chunk proceeds (a push costs a read and a write per tap).
-        for (int i = 0; i < G; ++i) {
+        auto position = [&](int i) {
             // every 32 positions, the inputs of the last 32 into the history,
             // for the FFT block at the chunk's end: one whole 128-byte line per
             // row, 16 bytes per lane (slots i-32+4seg .. +3, from row G-i+31-4seg down)
@@ -475,7 +495,14 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
                 });
             }
             __syncthreads();                   // the chain has written slot i
-        }
+        };
+        // the pulled groups q >= 2, loaded after the set-up, are first read at
+        // position 62: one wait for them there (inside the loop it would also
+        // wait for the history stores of the same position)
+        const int i1 = min(G, 62);
+        for (int i = 0; i < i1; ++i) position(i);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        for (int i = i1; i < G; ++i) position(i);
     }
 
     // the remaining inputs into the history: the last 32 slots as above, or

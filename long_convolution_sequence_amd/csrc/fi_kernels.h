@@ -265,13 +265,14 @@ __global__ void __launch_bounds__(kRingThreads) k_drain(Dev p, int rd, int advan
 namespace fi {
 
 // Tap table of the chunk kernels' helper lanes: per (l, c), 8 runs of 32
-// floats, run s holding taps s, s+8, .., s+248 (zero past L).
+// floats, run s holding taps s, s+8, .., s+248 (zero past L, and zero at lags
+// 0 and 1, which the red cells add themselves).
 __global__ void __launch_bounds__(256) k_taps(Dev p, float *htap) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)p.M * p.D * kChunkTapRow) return;
     const size_t row = i / kChunkTapRow;
     const int e = (int)(i % kChunkTapRow), k = (e / kChunkTaps) + 8 * (e % kChunkTaps);
-    htap[i] = k < p.L ? p.filt[row * (size_t)p.L + k] : 0.f;
+    htap[i] = k >= 2 && k < p.L ? p.filt[row * (size_t)p.L + k] : 0.f;
 }
 
 // Filter heads h^l[c][0..HK-1], channel innermost.
