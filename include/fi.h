@@ -228,8 +228,9 @@ fi_status fi_tau_table(const fi_ctx *ctx, int *path, double *us_direct, double *
  * 2^g), us_chunk[g] = measured microseconds of one chunk and the class-g FFT
  * gray blocks after it, us_run[g] = the modeled microseconds of the classes
  * the choice affects over a whole run ((L / 2^g) chunks plus the FFT blocks of
- * classes g .. 8); the candidate with the least us_run is the split used.  -1
- * where not timed.  Arrays hold at least P + 1 entries; either may be NULL. */
+ * classes g .. 8); the split used is the shortest chunk whose us_run is within
+ * 1.5% of the least (closer than the timing repeats), so repeated
+ * calibrations agree.  -1 where not timed.  Arrays hold at least P + 1 entries; either may be NULL. */
 fi_status fi_chunk_table(const fi_ctx *ctx, double *us_chunk, double *us_run);
 
 /* Copy positions first..first+count-1 (first >= 1) of one layer into dst

@@ -698,7 +698,15 @@ fi_status time_chunk_pair(fi_ctx *c, double &us) {
 // block below 2^g, and classes from g on run as FFT blocks.  The whole run
 // costs (L / 2^g) chunks plus 2^(P-1-q) FFT blocks of each class q >= g; the
 // classes above kMaxDirectLog + 1 are FFT blocks for every candidate and are
-// left out of the comparison.  Picks the cheapest g into qd.
+// left out of the comparison.  Picks into qd the least g whose modeled run is
+// within kSplitTie of the cheapest: one chunk pair is timed to about 1%, and
+// candidates that close (chunks of 128 and 256 on the 18 x 864 x 2^17 stack,
+// 0.2-1% apart either way from one calibration to the next) would otherwise
+// be chosen by noise.  Of two such, the shorter chunk runs every position at
+// the red-cell chain's pace; the longer has positions bound by its helpers,
+// which one timed pair weighs less than whole generations do (there the
+// shorter was 0.4-0.6% faster).
+constexpr double kSplitTie = 0.015;
 fi_status calibrate_chunks(fi_ctx *c, int cus, int &qd) {
     const int qtop = std::min(kMaxDirectLog + 1, c->P - 1);      // FFT classes that may switch
     for (int q = kMinFftLog; q <= qtop; ++q) {
@@ -713,11 +721,13 @@ fi_status calibrate_chunks(fi_ctx *c, int cus, int &qd) {
         double cost = std::ldexp(c->us_chunk[g] - (g < c->P ? c->us_fft[g] : 0.0), c->P - g);
         for (int q = g; q <= qtop; ++q) cost += std::ldexp(c->us_fft[q], c->P - 1 - q);
         c->us_run[g] = cost;
-        if (best < 0 || cost < best) {
-            best = cost;
-            qd = g;
-        }
+        if (best < 0 || cost < best) best = cost;
     }
+    for (int g = kMinFftLog; g <= std::min(kMaxDirectLog + 1, c->P); ++g)
+        if (c->us_run[g] >= 0 && c->us_run[g] <= best * (1.0 + kSplitTie)) {
+            qd = g;
+            break;
+        }
     return clear_state(c);
 }
 

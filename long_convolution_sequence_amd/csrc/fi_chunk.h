@@ -316,9 +316,6 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
     auto grow = [&](int rho) {                             // history row of local row rho
         return ((size_t)(rho % M) * BD + c0 + rho / M) * (size_t)p.L;
     };
-    auto frow = [&](int rho) {                             // filter row
-        return ((size_t)(rho % M) * p.D + (c0 + rho / M) % p.D) * (size_t)p.L;
-    };
     auto trow = [&](int rho) {                             // tap-table row
         return (size_t)(rho % M) * p.D + (c0 + rho / M) % p.D;
     };
@@ -373,7 +370,10 @@ __global__ void __launch_bounds__(kChunkThreads) k_chunk(Dev p, long long cb_arg
         // the heads, one row per thread (R <= kChunkMaxRows < npt), in flight
         // together with the pending sums
         float2 hv = make_float2(0.f, 0.f);
-        if (pt < R && live(pt)) hv = make_float2(p.filt[frow(pt)], p.L > 1 ? p.filt[frow(pt) + 1] : 0.f);
+        if (pt < R && live(pt)) {
+            const int l = pt % M, c = (c0 + pt / M) % p.D;   // from the heads table: 8 rows per line
+            hv = make_float2(p.hh[head(p, l, 0, c)], p.HK > 1 ? p.hh[head(p, l, 1, c)] : 0.f);
+        }
         if (G >= 16) {
             // Items of 16 rows x 4 float4 per wave: the loads read 64
             // contiguous bytes of each of 16 rows, and the stores (four slots
