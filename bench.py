@@ -353,7 +353,11 @@ def main():
     x1 = torch.from_numpy(workloads.x_first(w)).cuda()
     # the production path: graphs of whole chunks and of their FFT gray blocks,
     # no per-kernel events
-    ctx = fi.Context(hdev, w.B, tau_split=args.tau_split)
+    # made with defer_wide = 2 so that the deferral leg below can defer the
+    # two-half class too (its offset spectra live in the workspace); the timed
+    # steps run with deferral off
+    ctx = fi.Context(hdev, w.B, tau_split=args.tau_split, defer_wide=0 if args.no_defer_leg else 2)
+    ctx.set_defer_wide(0)
     tau = ctx.tau_table()
     split = next((q for (q, pth, _, _) in tau if pth == fi.PATH_FFT), w.P)
     calib = [{"first_fft_U": 1 << g, "chunk_and_fft_us": round(uc, 2), "modeled_run_ms": round(ur * 1e-3, 3)}
@@ -470,20 +474,33 @@ def main():
     # deferred to the context's second stream (large-block latency smoothing)
     defer = None
     if not args.no_defer_leg:
-        ctx.set_defer_wide(True)
-        dt = one_step(ctx)
-        dl = np.diff(ctx.stamps(1, L).astype(np.float64)) / 100.0
-        ctx.set_defer_wide(False)
         top = w.P - 1
         dcls = cls[:L - 1]
-        defer = {"tokens_per_s": round(L * w.B / dt, 1),
-                 "latency_us": {"p50": round(float(np.percentile(dl, 50)), 2),
-                                "p99": round(float(np.percentile(dl, 99)), 2),
-                                "max": round(float(dl.max()), 1),
-                                f"class_{top}_median": round(float(np.median(dl[dcls == top])), 1)},
-                 "note": "one generation with fi_options.defer_wide on: a split gray block computes its "
+
+        def deferred_generation(level):
+            ctx.set_defer_wide(level)
+            dt = one_step(ctx)
+            dl = np.diff(ctx.stamps(1, L).astype(np.float64)) / 100.0
+            ctx.set_defer_wide(0)
+            lat_us = {"p50": round(float(np.percentile(dl, 50)), 2),
+                      "p99": round(float(np.percentile(dl, 99)), 2),
+                      "max": round(float(dl.max()), 1)}
+            for q in (top - 1, top):
+                lat_us[f"class_{q}_median"] = round(float(np.median(dl[dcls == q])), 1)
+            return {"tokens_per_s": round(L * w.B / dt, 1), "latency_us": lat_us}
+
+        defer = deferred_generation(1)
+        defer["note"] = ("one generation with fi_options.defer_wide = 1: a split gray block computes its "
                          "first output sub-block before the next position and the rest on a second "
-                         "stream; not part of the timed steps above"}
+                         "stream; not part of the timed steps above")
+        defer["undeferred_class_medians_us"] = {f"class_{q}": per_class.get(q) for q in (top - 1, top)}
+        two = deferred_generation(2)
+        two["note"] = ("one generation with fi_options.defer_wide = 2: the two-half class as well, run as 4 "
+                       "sub-blocks of half the one-workgroup width with sub-blocks 1..3 on the second stream")
+        defer["level_2"] = two
+        log(f"bench: deferral: class {top - 1}/{top} medians {defer['latency_us'][f'class_{top - 1}_median']}/"
+            f"{defer['latency_us'][f'class_{top}_median']} us (level 1), "
+            f"{two['latency_us'][f'class_{top - 1}_median']}/{two['latency_us'][f'class_{top}_median']} us (level 2)")
     # one generation with chunks twice as long (one more direct class): the
     # calibration picks the chunk length for throughput, but the first position
     # of a chunk and the one whose FFT block ends it take the boundary's cost,

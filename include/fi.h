@@ -102,7 +102,16 @@ typedef struct fi_options {
                               n+1; the others run on a second stream of the context,
                               overlapping positions n+1 .. n+V-1, and the context
                               stream waits for them before position n+V.  Cuts the
-                              latency of that position; default 0 */
+                              latency of that position; results are bit for bit
+                              those without it.  2: the same, and the two-half
+                              class (twice fft_max_log2) is deferred too, run as 4
+                              sub-blocks of half the one-workgroup width (V =
+                              2^(fft_max_log2-1)); its results then differ from the
+                              two-half kernel's by rounding.  Level 2 needs
+                              fft_max_log2 >= 13, adds the offset spectra of that
+                              width to the workspace (7 * V/2 float4 per (l, c)),
+                              and where no two-half class exists acts as 1.
+                              Default 0 */
     int chunk_direct;      /* 1 (default): for maps that act channel by channel
                               (FI_MAP_TANH, FI_MAP_IDENTITY), fi_generate and
                               fi_prefill run the G = 2^q positions between two
@@ -166,12 +175,14 @@ fi_status fi_destroy(fi_ctx *ctx);
  * block-path table are kept. */
 fi_status fi_reset(fi_ctx *ctx);
 
-/* Turn fi_options.defer_wide on (1) or off (0) for the following positions.
+/* Set fi_options.defer_wide (0, 1 or 2) for the following positions.
  * Large-block latency (Flash Inference summary page, "Hauptergebnisse": the
  * per-token time spikes at the positions of the widest blocks): with it on, a
- * split gray block puts its later output sub-blocks on the context's second
- * stream.  Any deferred work still running is joined into the context stream
- * first.  FI_EINVAL for other values. */
+ * split gray block (level 2: also a two-half block) puts its later output
+ * sub-blocks on the context's second stream.  Any deferred work still running
+ * is joined into the context stream first.  FI_EINVAL for other values;
+ * FI_ESTATE for 2 when the context has a two-half class that fi_init did not
+ * prepare (fi_options.defer_wide was not 2 there). */
 fi_status fi_set_defer_wide(fi_ctx *ctx, int on);
 
 /* Produce the next position n = fi_position()+1 (Algorithm 2 for one i).

@@ -69,6 +69,7 @@ struct Layout {
     int HK = 0;
     int pre_stride = 0;              // prefill sums per (b, c): positions of a prompt up to L/2
     size_t spec[kMaxP] = {0};
+    size_t spec_pair = 0;            // offset spectra for the deferred two-half class (defer_wide = 2)
     size_t total = 0;
     int logNT = 0;
 };
@@ -84,6 +85,13 @@ int sub_k(int q, int vlog) { return 1 << (q - vlog); }
 size_t spec_row_f4(int q, int vlog) {
     return is_sub(q, vlog) ? (size_t)(2 * sub_k(q, vlog) - 1) * ((size_t(1) << vlog) / 2) : (size_t(1) << q) / 2;
 }
+// Deferral of the two-half class (defer_wide = 2): its block runs as
+// kPairSubK sub-blocks of half the one-workgroup width, which needs offset
+// spectra of that width (kPairSubK * 2 - 1 per (l, c) row) and exists only
+// when that width is one the split kernels take.
+constexpr int kPairSubK = 4;
+bool pair_defer_exists(int P, int vlog) { return vlog - 1 >= kMinSubLog && vlog + 1 <= P - 1; }
+size_t pair_spec_row_f4(int vlog) { return (size_t)(2 * kPairSubK - 1) * ((size_t(1) << (vlog - 1)) / 2); }
 
 // Twiddle tables, fp64 on the host (2 NT float2, NT = 2^logNT): W_NT^k, then
 // for every transform size N = 2^logn the pair twiddle W_{2N}^j of each
@@ -148,8 +156,14 @@ bool make_layout(int M, int B, int D, int64_t L, const fi_options &o, Layout &la
         lay.reca = o.record ? take(rowsMBD * L * sizeof(float)) : 0;
     }
     for (int q = 0; q < P; ++q) lay.spec[q] = fft_exists(q, P) ? take(rowsMD * spec_row_f4(q, vlog) * 16) : 0;
+    const bool pair_defer = o.defer_wide == 2 && pair_defer_exists(P, vlog);
+    lay.spec_pair = pair_defer ? take(rowsMD * pair_spec_row_f4(vlog) * 16) : 0;
     // forward sub-block spectra of the widest split class: [M*B*D][U/2] float4
-    lay.scratch = is_sub(P - 1, vlog) ? take(rowsMBD * ((size_t(1) << (P - 1)) / 2) * 16) : 0;
+    // (a deferred two-half block needs [M*B*D][kPairSubK * 2^(vlog-1) / 2], less than any split class)
+    const size_t scratch_f4 = is_sub(P - 1, vlog) ? (size_t(1) << (P - 1)) / 2
+                              : pair_defer            ? kPairSubK * ((size_t(1) << (vlog - 1)) / 2)
+                                                      : 0;
+    lay.scratch = scratch_f4 ? take(rowsMBD * scratch_f4 * 16) : 0;
     const int nmax_log = std::min(P - 1, vlog);
     lay.logNT = std::max(2, nmax_log + 1);
     lay.twid = take((size_t(2) << lay.logNT) * sizeof(float2));  // twiddles, pair and odd-pair twiddles
@@ -180,6 +194,7 @@ struct fi_ctx {
     Layout lay;
     Dev dev{};
     float4 *spec[kMaxP] = {nullptr};
+    float4 *spec_pair = nullptr;     // offset spectra of the deferred two-half class, or NULL
     float4 *scratch = nullptr;
     float *pre = nullptr;            // eager prefill sums [B*D][pre_stride]
     int pre_stride = 0;
@@ -396,14 +411,28 @@ hipError_t launch_spectrum_n(fi_ctx *c, int logn, hipStream_t s, float4 *dst, lo
     return hipGetLastError();
 }
 
+// True when the gray block of class q leaves output sub-blocks to the side
+// stream: the split classes with defer_wide on, and the two-half class too
+// with defer_wide = 2.
+bool defers(const fi_ctx *c, int q) {
+    const int vlog = c->opt.fft_max_log2;
+    if (!c->opt.defer_wide || q >= c->P) return false;
+    return is_sub(q, vlog) || (c->opt.defer_wide == 2 && is_pair(q, vlog) && c->spec_pair);
+}
+
 // Split class q.  Without `defer`: both kernels on s.  With `defer` (the
 // position n known): the forward kernel and output sub-block 0 on s, output
 // sub-blocks 1..K-1 on the side stream after the forward kernel, timed by
 // dv0/dv1 when given.
+// The two-half class runs here too when it is deferred (defer_wide = 2): as
+// kPairSubK sub-blocks of half the one-workgroup width, against the offset
+// spectra of that width.
 hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, hipEvent_t ev0, hipEvent_t ev1,
                           int64_t defer = 0, hipEvent_t dv0 = nullptr, hipEvent_t dv1 = nullptr) {
-    const int LOGV = c->opt.fft_max_log2;
-    const int K = sub_k(q, LOGV);
+    const bool pair = is_pair(q, c->opt.fft_max_log2);
+    if (pair && !c->spec_pair) return hipErrorInvalidValue;
+    const int LOGV = pair ? c->opt.fft_max_log2 - 1 : c->opt.fft_max_log2;
+    const int K = pair ? kPairSubK : sub_k(q, LOGV);
     const SubFwdK kf = sub_fwd_k(LOGV);
     const SubInvK ki = sub_inv_k(LOGV, K);
     if (!kf || !ki) return hipErrorInvalidValue;
@@ -412,7 +441,7 @@ hipError_t launch_fft_sub(fi_ctx *c, int rd, int q, hipStream_t s, int advance, 
     launch_k(kf, dim3((unsigned)(rows * K)), blk, s, ev0, nullptr, c->dev, rd, c->scratch, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const float4 *A = c->scratch, *G = c->spec[q];
+    const float4 *A = c->scratch, *G = pair ? c->spec_pair : c->spec[q];
     if (!defer) {
         launch_k(ki, dim3((unsigned)(rows * K)), blk, s, nullptr, ev1, c->dev, rd, A, G, K, 0, K, 0LL, advance);
         return hipGetLastError();
@@ -490,7 +519,7 @@ hipError_t launch_position_t(fi_ctx *c, int rd, int q, hipStream_t s, const floa
     hipError_t e = launch_red_fft<CHAIN>(c, rd, s, xext, yext);
     if (defer && !c->opt.defer_wide) defer = 0;
     if (e == hipSuccess)
-        e = defer && is_sub(q, c->opt.fft_max_log2) ? launch_fft_sub(c, rd, q, s, 0, nullptr, nullptr, defer)
+        e = defer && defers(c, q) ? launch_fft_sub(c, rd, q, s, 0, nullptr, nullptr, defer)
                                                     : launch_fft(c, rd, q, s, 0);
     if (e == hipSuccess) e = launch_drain(c, rd, s, advance);
     return e;
@@ -867,7 +896,7 @@ fi_status launch_timed_fft(fi_ctx *c, int64_t n, int q, int advance) {
     const size_t i = c->ev_used++;
     c->ev_class[i] = q;
     c->ev_count[i] = 1;
-    if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
+    if (defers(c, q)) {
         // the deferred sub-blocks' kernel time adds to this launch
         const size_t j = c->ev_used++;
         c->ev_class[j] = q;
@@ -912,7 +941,7 @@ fi_status run_chunk(fi_ctx *c, int64_t cb, const float *xseq) {
     if (c->opt.time_blocks) {
         fi_status s = launch_timed_fft(c, n, q, 2);
         if (s != FI_OK) return s;
-    } else if (c->opt.defer_wide && is_sub(q, c->opt.fft_max_log2)) {
+    } else if (defers(c, q)) {
         HIPCK(c, launch_fft_sub(c, rd_of(n), q, c->stream, 2, nullptr, nullptr, n));
     } else {
         HIPCK(c, launch_fft(c, rd_of(n), q, c->stream, 2));
@@ -1033,7 +1062,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
         fi_default_options(&o);
     if (o.map < FI_MAP_TANH || o.map > FI_MAP_HYENA) return FI_EINVAL;
     if (o.feedback < FI_FEEDBACK_TANH || o.feedback > FI_FEEDBACK_IDENTITY) return FI_EINVAL;
-    if (o.defer_wide != 0 && o.defer_wide != 1) return FI_EINVAL;
+    if (o.defer_wide < 0 || o.defer_wide > 2) return FI_EINVAL;
     if (o.chunk_direct != 0 && o.chunk_direct != 1) return FI_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return FI_EINVAL;
@@ -1112,6 +1141,7 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     d.fb = o.feedback == FI_FEEDBACK_IDENTITY ? 1 : 0;
     for (int q = 0; q < c->P; ++q)
         c->spec[q] = fft_exists(q, c->P) ? (float4 *)(c->ws + lay.spec[q]) : nullptr;
+    c->spec_pair = lay.spec_pair ? (float4 *)(c->ws + lay.spec_pair) : nullptr;
     c->scratch = lay.scratch ? (float4 *)(c->ws + lay.scratch) : nullptr;
     c->pre = (float *)(c->ws + lay.pre);
     c->pre_stride = lay.pre_stride;
@@ -1148,6 +1178,15 @@ fi_status fi_init(fi_ctx **out, int layers, int batch, int channels, int64_t L, 
     for (int q = 0; q < c->P; ++q) {
         if (!c->spec[q]) continue;
         if (launch_spectrum(c, q, c->stream) != hipSuccess) return bail(fail(c, FI_EDEVICE, "spectrum launch"));
+    }
+    if (c->spec_pair) {
+        // offset spectra d = 1 .. 2 kPairSubK - 1 of width V = 2^(vlog-1): taps h[(d-1)V .. (d+1)V-1]
+        const int plog = o.fft_max_log2 - 1;
+        const long long V = 1LL << plog, stride = (long long)pair_spec_row_f4(o.fft_max_log2);
+        for (int d = 1; d <= 2 * kPairSubK - 1; ++d)
+            if (launch_spectrum_n(c, plog, c->stream, c->spec_pair + (d - 1) * (V / 2), (d - 1) * V, stride) !=
+                hipSuccess)
+                return bail(fail(c, FI_EDEVICE, "spectrum launch"));
     }
 
     // Path table.  Blocks of edge 2^q with q < qd are direct, the rest FFT (direct
@@ -1233,7 +1272,9 @@ fi_status fi_reset(fi_ctx *c) {
 fi_status fi_set_defer_wide(fi_ctx *c, int on) {
     fi_status s = check_usable(c);
     if (s != FI_OK) return s;
-    if (on != 0 && on != 1) return FI_EINVAL;
+    if (on < 0 || on > 2) return FI_EINVAL;
+    if (on == 2 && !c->spec_pair && pair_defer_exists(c->P, c->opt.fft_max_log2))
+        return fail(c, FI_ESTATE, "defer_wide = 2 needs fi_options.defer_wide = 2 at fi_init (its spectra)");
     if ((s = join_side(c, -1)) != FI_OK) return s;
     c->opt.defer_wide = on;
     return FI_OK;
@@ -1470,7 +1511,7 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
                 // an aligned run of 2^kb chunks: all but the last from one graph
                 const int kb = c->chunk_block_log;
                 const int64_t run = G << kb;
-                const bool split_in_run = c->opt.defer_wide && is_sub(c->chunk_log + kb - 1, c->opt.fft_max_log2);
+                const bool split_in_run = defers(c, c->chunk_log + kb - 1);
                 if (kb && !split_in_run && (c->pos & (run - 1)) == 0 && c->pos + run <= end) {
                     if ((s = join_side(c, c->pos + run - G - 1)) != FI_OK) return s;
                     HIPCK(c, hipGraphLaunch(c->gchunks, c->stream));
@@ -1479,7 +1520,7 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
                 }
                 const int64_t n = c->pos + G;
                 const int q = class_of(c, n);
-                if (!(c->opt.defer_wide && q < c->P && is_sub(q, c->opt.fft_max_log2))) {
+                if (!defers(c, q)) {
                     if ((s = join_side(c, n - 1)) != FI_OK) return s;
                     HIPCK(c, hipGraphLaunch(c->gchunk[q], c->stream));
                     c->pos = n;
@@ -1505,8 +1546,7 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
         if (c->opt.time_blocks && q < c->P && c->path[q] == FI_PATH_FFT && c->opt.map != FI_MAP_HYENA) {
             s = launch_timed_position(c, n, q);
             if (s != FI_OK) return s;
-        } else if (graphs && !(c->opt.defer_wide && q < c->P && c->path[q] == FI_PATH_FFT &&
-                               is_sub(q, c->opt.fft_max_log2))) {
+        } else if (graphs && !(c->path[q] == FI_PATH_FFT && defers(c, q))) {
             HIPCK(c, hipGraphLaunch(c->gclass[q], c->stream));
         } else {
             // split gray blocks launch directly, leaving their later sub-blocks to the side stream

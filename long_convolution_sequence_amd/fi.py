@@ -223,9 +223,11 @@ class Context:
             raise FiError(FI_EINVAL, "x0: required")
         self._check(self._lib.fi_set_input(self._h, self._p(x0, name="x0")))
 
-    def set_defer_wide(self, on):
-        """Defer the later sub-blocks of split gray blocks to a second stream (or not)."""
-        self._check(self._lib.fi_set_defer_wide(self._h, int(bool(on))))
+    def set_defer_wide(self, level):
+        """Defer the later sub-blocks of wide gray blocks to a second stream: 0 off,
+        1 (or True) the split classes, 2 the two-half class too (the context must
+        have been made with defer_wide=2)."""
+        self._check(self._lib.fi_set_defer_wide(self._h, int(level)))
 
     def step(self, x=None, y=None):
         """One position; x: [B][D] device tensor or None (feedback). Returns y [B][D]."""

@@ -53,6 +53,22 @@ def test_workspace_bytes_shapes(lib):
     assert 5e9 < big < 40e9
 
 
+def test_workspace_for_deferred_two_half_blocks(lib):
+    """defer_wide = 2 adds the two-half class's offset spectra: 7 spectra of width
+    V = 2^(fft_max_log2-1), V/2 float4 each, per (l, c) row (the scratch of a split
+    class already covers its forward bins); no two-half class, nothing added."""
+    def ws(level, L, vlog=14, M=18, B=1, D=864):
+        o = fi.default_options()
+        o.defer_wide, o.fft_max_log2 = level, vlog
+        return fi.workspace_bytes(M, B, D, L, o)
+    V = 1 << 13
+    extra = ws(2, 1 << 17) - ws(0, 1 << 17)
+    assert 18 * 864 * 7 * (V // 2) * 16 <= extra < 18 * 864 * 7 * (V // 2) * 16 + 512
+    assert ws(1, 1 << 17) == ws(0, 1 << 17)
+    assert ws(2, 1 << 15) == ws(0, 1 << 15)            # largest class 2^14: no two-half class
+    assert ws(2, 1 << 17, vlog=12) == ws(0, 1 << 17, vlog=12)   # half width 2^11: no split kernel
+
+
 @pytest.mark.parametrize("M,B,D,L", [(0, 1, 1, 8), (1, 0, 1, 8), (1, 1, 0, 8), (1, 1, 1, 1000),
                                      (1, 1, 1, 0), (65, 1, 1, 8), (1, 1, 1, -4)])
 def test_workspace_bytes_rejects_bad_shapes(lib, M, B, D, L):
@@ -76,7 +92,7 @@ def test_init_rejects_bad_arguments_without_a_device(lib):
     o.map = 7
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
     o = fi.default_options()
-    o.defer_wide = 2
+    o.defer_wide = 3
     assert lib.fi_init(ctypes.byref(h), 1, 1, 1, 8, f, ctypes.byref(o), None, None) == fi.FI_EINVAL
     o = fi.default_options()
     o.chunk_direct = 2

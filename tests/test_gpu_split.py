@@ -109,3 +109,49 @@ def test_deferred_split_sub_blocks_change_nothing(graphs):
     assert worst <= 1.0
     assert np.array_equal(outs[0], outs[1])
     assert np.abs(outs[0]).max() > 0
+
+
+@pytest.mark.parametrize("graphs", [True, False])
+def test_deferred_two_half_blocks_against_oracle(graphs):
+    """defer_wide = 2 with width 2^13 at L = 2^16: the two-half class 2^14 runs
+    as 4 sub-blocks of 2^12 with sub-blocks 1..3 on the side stream, the split
+    class 2^15 as with level 1.  Every layer of the free-running stack is
+    replayed from its recorded inputs against the oracle (at the ends of every
+    dyadic range, the sub-block boundaries after each wide block, and random
+    positions), also when a run stops inside a deferral; graphs on and off give
+    the same outputs; a context made without level 2 refuses it."""
+    M, B, D, L = 2, 2, 5, 65536
+    say(f"case deferred two-half blocks M={M} B={B} D={D} L={L} graphs={graphs}")
+    rng = np.random.default_rng(37)
+    h = (rng.standard_normal((M, D, L)) * np.exp(-np.arange(L) / 8192.0) / np.sqrt(L)).astype(np.float32)
+    x1 = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).cuda()
+    with fi.Context(torch.from_numpy(h).cuda(), B, tau_split=6, fft_max_log2=13, use_graphs=graphs,
+                    defer_wide=1) as ctx:
+        with pytest.raises(fi.FiError):
+            ctx.set_defer_wide(2)
+    with fi.Context(torch.from_numpy(h).cuda(), B, tau_split=6, fft_max_log2=13, use_graphs=graphs,
+                    defer_wide=2, record=True) as ctx:
+        ctx.set_input(x1)
+        a = ctx.generate(16384 + 100)              # stops 100 positions into the first two-half deferral
+        b = torch.stack([ctx.step() for _ in range(200)])
+        c = ctx.generate(49152 - 16384 - 300)      # up to the second two-half block
+        d = ctx.generate(L - 49152)
+        y = torch.cat([a, b, c, d]).cpu().numpy()
+        ts = _positions(L, rng, 200)
+        ends = np.concatenate([np.arange(16384, 16384 + 16384 + 1, 4096), np.arange(49152, L + 1, 4096),
+                               np.arange(32768, L + 1, 8192)])
+        ts = np.unique(np.concatenate([ts, ends - 1, ends[ends < L]]))
+        worst = 0.0
+        for l in range(M):
+            xs = ctx.history(l, 0).cpu().numpy()
+            ys = ctx.history(l, 1).cpu().numpy()
+            for bb in range(B):
+                for cc in range(D):
+                    xrow = np.ascontiguousarray(xs[:, bb, cc])
+                    ref = oracle.conv_points(h[l, cc], xrow, ts)
+                    tol = TF_TOL * np.abs(h[l, cc].astype(np.float64)).sum() * np.abs(xrow).max()
+                    worst = max(worst, float(np.abs(ys[ts, bb, cc] - ref).max() / tol))
+    say(f"  level-2 deferred run vs oracle (replay at {len(ts)} positions): worst error/tolerance {worst:.3e}")
+    assert worst <= 1.0
+    assert np.abs(y).max() > 0
+    assert np.isfinite(y).all()
