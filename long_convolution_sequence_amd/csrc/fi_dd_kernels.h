@@ -151,7 +151,7 @@ k_dd_band(Dev p, DDev q, float4 *__restrict__ spx, float4 *__restrict__ sph) {
     }
     dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt) + lpad_off(m, QLOG0)] = v[m];
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     if (!active) return;

@@ -29,6 +29,12 @@ namespace fi {
 // stages spread over the LDS banks.
 __device__ __forceinline__ int lpad(int i) { return i + (i >> 4); }
 __host__ __device__ constexpr int lds_len(int n) { return n + (n >> 4); }
+// lpad(b + (m << q)) = lpad(b) + lpad_off(m, q) whenever b mod 16 plus
+// (m << q) mod 16 stays below 16.  That holds for every access of a stage
+// group (b its base, r < 2^q, the rest of b a multiple of 16 or of 2^(q+R))
+// and of the outer group (b = lt): with m unrolled, each access then takes an
+// immediate offset from one address instead of address arithmetic of its own.
+__host__ __device__ constexpr int lpad_off(int m, int q) { return (m << q) + ((m << q) >> 4); }
 
 // W_S^j = exp(-2 pi i j / S), S = 2^slog, from the table of NT = 2^logNT roots.
 __device__ __forceinline__ float2 twiddle(const float2 *__restrict__ tw, int logNT, int slog, int j) {
@@ -238,16 +244,16 @@ __device__ __forceinline__ void lds_group(float2 *X, int lt, float2 w) {
     static_assert(QLOG == 0 || G == TT, "a twiddled group is the only one of its thread");
     for (int g = lt; g < G; g += TT) {
         const int r = g & ((1 << QLOG) - 1);
-        const int base = ((g >> QLOG) << SLOG) + r;
+        float2 *Xb = X + lpad(((g >> QLOG) << SLOG) + r);
         float2 v[1 << R];
 #pragma unroll
-        for (int m = 0; m < (1 << R); ++m) v[m] = X[lpad(base + (m << QLOG))];
+        for (int m = 0; m < (1 << R); ++m) v[m] = Xb[lpad_off(m, QLOG)];
         if constexpr (FWD)
             dif_group_w<R, false, (QLOG > 0)>(v, w);
         else
             dit_group_w<R, (QLOG > 0)>(v, w);
 #pragma unroll
-        for (int m = 0; m < (1 << R); ++m) X[lpad(base + (m << QLOG))] = v[m];
+        for (int m = 0; m < (1 << R); ++m) Xb[lpad_off(m, QLOG)] = v[m];
     }
 }
 

@@ -40,7 +40,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     }
     dif_group<R0, true>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt) + lpad_off(m, QLOG0)] = v[m];
     // this thread's spectrum pairs, loaded late: held across the whole forward
     // transform they would cost the registers of a fourth wave per SIMD.  When
     // the last stage group is short (fewer than four stages), they are issued
@@ -92,7 +92,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     const float2 w0 = inverse_groups<LOGN, S::NPASS - 1>(X, lt, p.twid, p.logNT, wi);
     before_last();
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
+    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt) + lpad_off(m, QLOG0)];
     dit_group_w<R0>(v, w0);
 }
 
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(FftShape<LOGN>::TPB) k_spectrum(Dev p, float4 
     for (int m = 0; m < (1 << R0); ++m) v[m] = active ? src[lt + (m << QLOG0)] : make_float2(0.f, 0.f);
     dif_group<R0>(v, lt, LOGN, p.twid, p.logNT);
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt) + lpad_off(m, QLOG0)] = v[m];
     forward_groups<LOGN, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     const float inv = 1.0f / (float)N;
@@ -245,7 +245,7 @@ __device__ __forceinline__ void half_forward(const Dev &p, float2 *X, int lt, bo
     });
     dif_group<R0>(v, lt, LOGM, p.twid, p.logNT);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    for (int m = 0; m < 16; ++m) X[lpad(lt) + lpad_off(m, QLOG0)] = v[m];
     forward_groups<LOGM, 1, S::NPASS, false>(X, lt, p.twid, p.logNT);
 }
 
@@ -260,7 +260,7 @@ __device__ __forceinline__ void half_inverse_acc(const Dev &p, float2 *X, int lt
     const float2 w0 = inverse_groups<LOGM, S::NPASS - 1, false>(X, lt, p.twid, p.logNT, make_float2(1.f, 0.f));
     float2 v[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) v[m] = X[lpad(lt + (m << QLOG0))];
+    for (int m = 0; m < 16; ++m) v[m] = X[lpad(lt) + lpad_off(m, QLOG0)];
     dit_group_w<R0>(v, w0);
     if (!active) return;
     const float2 wl = ODD ? twiddle(p.twid, p.logNT, LOGM + 1, lt) : make_float2(1.f, 0.f);
@@ -491,7 +491,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
     }
     dif_group<R0, true>(v, lt, LOGV, p.twid, p.logNT);
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt + (m << QLOG0))] = v[m];
+    for (int m = 0; m < (1 << R0); ++m) X[lpad(lt) + lpad_off(m, QLOG0)] = v[m];
     forward_groups<LOGV, 1>(X, lt, p.twid, p.logNT);
     __syncthreads();
     float4 *dst = scratch + ((size_t)tile * K + i) * (N / 2);
@@ -666,7 +666,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
     for (int m = 0; m < HALF0; ++m) acc[m] = adst[lt + (m << QLOG0)];
     float2 v[1 << R0];
 #pragma unroll
-    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt + (m << QLOG0))];
+    for (int m = 0; m < (1 << R0); ++m) v[m] = X[lpad(lt) + lpad_off(m, QLOG0)];
     dit_group_w<R0>(v, w0);
 #pragma unroll
     for (int m = 0; m < HALF0; ++m) adst[lt + (m << QLOG0)] = cadd(acc[m], v[m + HALF0]);
