@@ -348,6 +348,70 @@ __host__ __device__ inline PairSlot pair_slot(int logn, int e) {
     return {p2, p1, N - k1};
 }
 
+// pair_slot of the items e = lt + m*TT of one thread (TT = N/16 >= 16, so
+// N >= 256; m < 8) as a part fixed per thread plus a part that depends on m
+// alone, so that with m unrolled the slots cost no arithmetic per item.  For
+// e >= 16, e >> 4 = (lt >> 4) + m*2^(w-4) (w = log2 N - 4): its w-bit
+// reversal is rev(lt >> 4) << 4 | rev4(m), and 2^w - (e >> 4) has the high
+// four bits 15 - m over the low part 2^(w-4) - (lt >> 4) when lt >> 4 > 0,
+// or 16 - m over zero when lt < 16.  Which of the pair comes first is bit 0
+// of p1 (the top bit of its bin), i = lt & 15 for every m.  Item m = 0 of the
+// threads lt < 16 has e < 16: the caller takes pair_slot there.
+struct PairBase {
+    int p1, p2;      // per-thread parts of the two slots
+    bool lo, swap;   // lt >= 16; the bin of p1 is in the upper half
+};
+template <int LOGN>
+__host__ __device__ inline PairBase pair_base(int lt) {
+    static_assert(LOGN >= 8, "sixteen or more threads per transform");
+    constexpr int W4 = LOGN - 8;   // bits of lt >> 4
+    const int bl = lt >> 4, i = lt & 15;
+    const int r1 = W4 > 0 ? rbits(W4, bl) : 0;
+    const int r2 = (W4 > 0 && bl > 0) ? rbits(W4, (1 << W4) - bl) : 0;
+    return {256 * r1 + i, 256 * r2 + 15 - i, bl > 0, (i & 1) != 0};
+}
+template <int LOGN>
+__host__ __device__ inline PairSlot pair_slot_m(const PairBase &b, int m) {
+    const int p1 = b.p1 + 16 * rbits(4, m);
+    const int p2 = b.p2 + 16 * (b.lo ? rbits(4, 15 - m) : rbits(4, 16 - m));
+    return b.swap ? PairSlot{p2, p1, 0} : PairSlot{p1, p2, 0};
+}
+
+// LDS slots (lpad applied) of the pair of item e = lt + m*TT: a = bin j,
+// b = bin N - j.  From N = 256 on, the per-thread parts are padded once
+// (lpad(x + 16c) = lpad(x) + 17c) and an item adds compile-time constants.
+struct SlotPair {
+    int a, b;
+};
+struct PairLds {
+    int l1, l2;
+    bool lo, swap;
+};
+template <int LOGN>
+__host__ __device__ inline PairLds pair_lds(int lt) {
+    if constexpr (LOGN >= 8) {
+        const PairBase b = pair_base<LOGN>(lt);
+        return {lpad(b.p1), lpad(b.p2), b.lo, b.swap};
+    } else {
+        return {0, 0, false, false};
+    }
+}
+template <int LOGN, int TT>
+__host__ __device__ inline SlotPair item_lds(const PairLds &b, int lt, int m) {
+    if constexpr (LOGN >= 8) {
+        const int s1 = b.l1 + 17 * rbits(4, m);
+        const int s2 = b.l2 + 17 * (b.lo ? rbits(4, 15 - m) : rbits(4, 16 - m));
+        const SlotPair f = b.swap ? SlotPair{s2, s1} : SlotPair{s1, s2};
+        if (m != 0) return f;
+        // item 0 of the threads lt < 16 (e = lt < 16) follows the first groups' order
+        const PairSlot ps = pair_slot(LOGN, lt);
+        return lt < 16 ? SlotPair{lpad(ps.pj), lpad(ps.pm)} : f;
+    } else {
+        const PairSlot ps = pair_slot(LOGN, lt + m * TT);
+        return {lpad(ps.pj), lpad(ps.pm)};
+    }
+}
+
 // Transforms of N = 2M points done as two M-point halves.  The first radix-2
 // stage of a decimation in frequency splits the bins by parity: the even bins
 // are the M-point transform of (c_lo + c_hi), the odd bins that of

@@ -65,6 +65,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     float2 wp[PAIRS];
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) wp[m] = p.ptw[N / 2 + lt + m * TT];
+    const PairLds pl = pair_lds<LOGN>(lt);
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
         const int e = lt + m * TT;
@@ -77,8 +78,8 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
             X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
             X[lpad(1)] = cmulc(Ch, make_float2(g.z, g.w));
         } else {
-            const PairSlot ps = pair_slot(LOGN, e);
-            const int p1 = lpad(ps.pj), p2 = lpad(ps.pm);
+            const SlotPair sl = item_lds<LOGN, TT>(pl, lt, m);
+            const int p1 = sl.a, p2 = sl.b;
             const float2 W = wp[m];
             float2 A1, A2, D1, D2;
             real_bins(X[p1], X[p2], W, A1, A2);
@@ -323,6 +324,7 @@ __device__ __forceinline__ void tile2_half(const Dev &p, float2 *X, int lt, bool
         const int e = lt + m * TT;
         gs[m] = (active && e < M / 2) ? sp[(ODD ? M / 2 : 0) + e] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const PairLds pl = pair_lds<LOGM>(lt);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
@@ -337,8 +339,16 @@ __device__ __forceinline__ void tile2_half(const Dev &p, float2 *X, int lt, bool
             X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
             X[lpad(1)] = cmulc(Ch, make_float2(g.z, g.w));
         } else {
-            const PairSlot ps = half_slot<LOGM, ODD>(e);
-            const int p1 = lpad(ps.pj), p2 = lpad(ps.pm);
+            int p1, p2;
+            if constexpr (ODD) {
+                // odd half: positions 2e and M-1-2e (odd_slot), linear in m
+                p1 = lpad(2 * lt) + lpad_off(m, FftShape<LOGM>::QLOG0 + 1);
+                p2 = lpad(M - 1 - 2 * lt) - lpad_off(m, FftShape<LOGM>::QLOG0 + 1);
+            } else {
+                const SlotPair sl = item_lds<LOGM, TT>(pl, lt, m);
+                p1 = sl.a;
+                p2 = sl.b;
+            }
             const float2 W = half_w<LOGM, ODD>(p, e);
             float2 A1, A2, D1, D2;
             real_bins(X[p1], X[p2], W, A1, A2);
@@ -501,6 +511,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
     float2 wp[PAIRS];
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) wp[m] = p.ptw[N / 2 + lt + m * TT];
+    const PairLds pl = pair_lds<LOGV>(lt);
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
         const int e = lt + m * TT;
@@ -509,9 +520,9 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_fwd(Dev p, int 
             const float2 Ch = X[lpad(1)];
             dst[0] = make_float4(C0.x + C0.y, C0.x - C0.y, Ch.x, -Ch.y);
         } else {
-            const PairSlot ps = pair_slot(LOGV, e);
+            const SlotPair sl = item_lds<LOGV, TT>(pl, lt, m);
             float2 A1, A2;
-            real_bins(X[lpad(ps.pj)], X[lpad(ps.pm)], wp[m], A1, A2);
+            real_bins(X[sl.a], X[sl.b], wp[m], A1, A2);
             dst[e] = make_float4(A1.x, A1.y, A2.x, A2.y);
         }
     }
@@ -614,6 +625,7 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
             }
         }
     };
+    const PairLds pl = pair_lds<LOGV>(lt);
     float4 a0[CH], g0[CH], a1[CH], g1[CH];
     load(0, a0, g0);
     static_for<0, NCH>([&](auto qc) {
@@ -649,11 +661,11 @@ __global__ void __launch_bounds__(FftShape<LOGV>::TPB) k_fft_sub_inv(Dev p, int 
                 X[0] = make_float2(0.5f * (Z0 + ZN), 0.5f * (Z0 - ZN));
                 X[lpad(1)] = make_float2(Z[m].z, -Z[m].w);
             } else {
-                const PairSlot ps = pair_slot(LOGV, j);
+                const SlotPair sl = item_lds<LOGV, TT>(pl, lt, q * CH + m);
                 float2 D1, D2;
                 pack_inverse(make_float2(Z[m].x, Z[m].y), make_float2(Z[m].z, Z[m].w), wc[m], D1, D2);
-                X[lpad(ps.pj)] = D1;
-                X[lpad(ps.pm)] = D2;
+                X[sl.a] = D1;
+                X[sl.b] = D2;
             }
         }
     });

@@ -180,9 +180,55 @@ static int check_pairs(int logn) {
   printf("pairs LOGN=%d %s\n", logn, bad ? "BAD" : "ok");
   return bad;
 }
+// The per-thread form of the pair slots (pair_base / pair_slot_m) against pair_slot for every
+// thread and item m >= 1, and for item 0 of the threads lt >= 16.
+template <int LOGN> int check_pair_base() {
+  const int N = 1 << LOGN, TT = N / 16;
+  int bad = 0;
+  for (int lt = 0; lt < TT; ++lt) {
+    const PairBase b = pair_base<LOGN>(lt);
+    for (int m = (lt < 16 ? 1 : 0); m < (N / 2) / TT; ++m) {
+      const PairSlot f = pair_slot_m<LOGN>(b, m), r = pair_slot(LOGN, lt + m * TT);
+      if (f.pj != r.pj || f.pm != r.pm) ++bad;
+    }
+  }
+  // the padded slots every kernel item uses (item_lds), for every item but e = 0
+  const PairLds L = pair_lds<LOGN>(0);
+  (void)L;
+  for (int lt = 0; lt < TT; ++lt) {
+    const PairLds pl = pair_lds<LOGN>(lt);
+    for (int m = 0; m < (N / 2) / TT; ++m) {
+      if (lt + m * TT == 0) continue;
+      const SlotPair f = item_lds<LOGN, N / 16>(pl, lt, m);
+      const PairSlot r = pair_slot(LOGN, lt + m * TT);
+      if (f.a != lpad(r.pj) || f.b != lpad(r.pm)) ++bad;
+    }
+  }
+  printf("pair base LOGN=%d %s\n", LOGN, bad ? "BAD" : "ok");
+  return bad != 0;
+}
+// item_lds below the per-thread form (N < 256): pair_slot itself
+template <int LOGN> int check_small_items() {
+  constexpr int N = 1 << LOGN, TT = N >= 16 ? N / 16 : 1;
+  int bad = 0;
+  for (int lt = 0; lt < TT; ++lt)
+    for (int m = 0; m * TT < N / 2; ++m) {
+      if (lt + m * TT == 0) continue;
+      const SlotPair f = item_lds<LOGN, TT>(pair_lds<LOGN>(lt), lt, m);
+      const PairSlot r = pair_slot(LOGN, lt + m * TT);
+      if (f.a != lpad(r.pj) || f.b != lpad(r.pm)) ++bad;
+    }
+  return bad != 0;
+}
+
 int main() {
   int pbad = 0;
   for (int logn = 2; logn <= 16; ++logn) pbad |= check_pairs(logn);
+  pbad |= check_pair_base<8>() | check_pair_base<9>() | check_pair_base<10>() | check_pair_base<11>() |
+          check_pair_base<12>() | check_pair_base<13>() | check_pair_base<14>() | check_pair_base<15>() |
+          check_pair_base<16>();
+  pbad |= check_small_items<2>() | check_small_items<3>() | check_small_items<4>() | check_small_items<5>() |
+          check_small_items<6>() | check_small_items<7>();
   double r[13] = { run<2>(15), run<3>(15), run<4>(15), run<5>(15), run<6>(15), run<7>(15), run<8>(15), run<9>(15), run<10>(15), run<11>(15), run<12>(15), run<13>(15), run<14>(15) };
   int bad = 0;
   for (int i = 0; i < 13; ++i) { printf("LOGN=%d rel err %.3e\n", i + 2, r[i]); if (!(r[i] < 1e-5)) bad = 1; }

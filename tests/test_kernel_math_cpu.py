@@ -21,7 +21,8 @@ def test_fft_tile_arithmetic_matches_direct_sums(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert r.stdout.count("rel err") == 24
-    assert r.stdout.count(" ok") == 15
+    assert r.stdout.count(" ok") == 15 + 9
+    assert r.stdout.count("pair base") == 9
     assert r.stdout.count("two halves") == 11
 
 
