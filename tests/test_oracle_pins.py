@@ -234,6 +234,20 @@ def test_schedule_covers_every_pair_exactly_once(P):
     assert np.array_equal(cover[1:, 1:], want)
 
 
+@pytest.mark.parametrize("logL", [4, 8, 11])
+def test_prompt_inputs_dead_after_prefill_only_for_top_runs(logL):
+    """After a prefill of P positions has run every gray block after n <= P, a later
+    block (n > P) still reads an input at or before P unless P = L - L/2^k: the prompt's
+    activations can be dropped on this schedule exactly for P = L/2, 3L/4, ... (the
+    relative schedule the rebuttal describes would allow it for every P)."""
+    L = 2 ** logL
+    tiles = list(schedule.gray_tiles(L))
+    top_runs = {L - L // 2 ** k for k in range(1, logL + 1)}
+    for P in range(1, L):
+        reaches_back = any(i > P and lo <= P for i, U, (lo, hi), _ in tiles)
+        assert reaches_back == (P not in top_runs), P
+
+
 @pytest.mark.parametrize("P", [1, 4, 10, 16])
 def test_schedule_counts_match_proposition_1(P):
     facts = json.load(open(os.path.join(GOLDEN, "schedule_facts.json")))
