@@ -688,6 +688,29 @@ def main():
                        "per position (chunks off), one warm generation")}
         log(f"bench: data-dependent filters L={Ld}: {dd['tokens_per_s']:,.0f} tokens/s; fixed filters per "
             f"position {dd['fixed_filter_per_position_tokens_per_s']:,.0f}")
+        # the workload's whole stack with data-dependent taps (fi_dd_stack_*): every layer's taps
+        # per position, tanh between layers, over Ls positions
+        Ls = min(4096, w.L)
+        hs = torch.from_numpy((rng.standard_normal((Ls, w.M, w.B, w.D)) / np.sqrt(64.0) *
+                               np.exp(-np.arange(Ls) / 2048.0)[:, None, None, None]).astype(np.float32)).cuda()
+        ys = torch.empty_like(hs)
+        sdc = fi.DDContext(w.B, w.D, Ls, layers=w.M)
+        sms = []
+        for _ in range(2):
+            sdc.reset()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            sdc.run(xd[:Ls], hs, ys)
+            b.record()
+            torch.cuda.synchronize()
+            sms.append(a.elapsed_time(b))
+        sdc.close()
+        del sdc, hs, ys
+        dd["stack"] = {"M": w.M, "L": Ls, "ms": round(sms[-1], 3),
+                       "tokens_per_s": round(Ls * w.B / (sms[-1] * 1e-3), 1),
+                       "note": "fi_dd_stack_* over L positions of all the workload's layers (layer 0's input and "
+                               "every layer's taps given per position, tanh between layers), warm, HIP events"}
+        log(f"bench: data-dependent stack M={w.M} L={Ls}: {dd['stack']['tokens_per_s']:,.0f} tokens/s")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, h)
 

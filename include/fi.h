@@ -390,7 +390,8 @@ typedef struct fi_dd fi_dd; /* opaque, owned by the library */
 
 /* Device bytes the workspace of a data-dependent context needs: three
  * [B*D][L] fp32 arrays (inputs, taps, pending sums) plus the fixed-block
- * spectra (16 L bytes per row) and twiddles.  0 if the shape is unsupported:
+ * spectra (16 L bytes per row), twiddles and one [B*D] array (the layer
+ * inputs of a position, used by stacks).  0 if the shape is unsupported:
  * B, D >= 1, B*D <= 2^24, L a power of two up to 32768 (the widest product,
  * L/2 points, must fit one workgroup's transform); fft_min_log2 in [2, 15], or
  * -1 for the default 8.  Products of p < 2^fft_min_log2 run directly: up to
@@ -406,12 +407,29 @@ size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log
 fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
                      void *stream);
 
-/* One position: x_t and h_t ([B][D], device) arrive, y_t ([B][D], device) is
- * written.  FI_ERANGE after L positions, FI_EINVAL for null pointers,
- * FI_ESTATE after a device failure. */
+/* A stack of `layers` data-dependent layers in one context (the summary page's
+ * layer stacks, "Schicht-uebergreifende Parallelisierung (Algorithmus 3)",
+ * with the filters of "Datenabhaengige Filter-Erweiterung (Appendix B)"):
+ * at each position layer l's taps h^l_t arrive with the data, layer 0's input
+ * x^0_t too, and layer l+1's input is tanh(y^l_t).  The red cells run layer
+ * after layer (one thread per (b, c) chain); every product of the position
+ * then runs once for the rows of all layers.  Sizes and limits as
+ * fi_dd_workspace_bytes, with 1 <= layers <= 64 and layers * batch * channels
+ * rows; 0 for an unsupported shape. */
+size_t fi_dd_stack_workspace_bytes(int layers, int batch, int channels, int64_t L, int fft_min_log2);
+
+/* Create a stack context (as fi_dd_init; layers = 1 is the single layer). */
+fi_status fi_dd_stack_init(fi_dd **out, int layers, int batch, int channels, int64_t L, int fft_min_log2,
+                           void *workspace, void *stream);
+
+/* One position: x_t ([B][D], device: layer 0's input) and h_t ([M][B][D],
+ * device: every layer's tap, M the context's layers, 1 for fi_dd_init) arrive,
+ * y_t ([M][B][D], device: every layer's output) is written.  FI_ERANGE after
+ * L positions, FI_EINVAL for null pointers, FI_ESTATE after a device failure. */
 fi_status fi_dd_step(fi_dd *ctx, const float *x_t, const float *h_t, float *y_t);
 
-/* `steps` positions in a row: x, h, y are [steps][B][D] (device). */
+/* `steps` positions in a row: x is [steps][B][D], h and y [steps][M][B][D]
+ * (device). */
 fi_status fi_dd_run(fi_dd *ctx, const float *x, const float *h, int64_t steps, float *y);
 
 /* Back to position 0 (inputs, taps and pending sums cleared). */

@@ -1888,6 +1888,9 @@ fi_status fi_lazy_generate(fi_ctx *c, int64_t steps, float *y) {
 // Data-dependent filters: the taps arrive with the data (fi_dd_*).
 // ---------------------------------------------------------------------------
 struct fi_dd {
+    int M = 1;                       // layers (a stack: rows r = l * B * D + b * D + c)
+    bool stack = false;              // made by fi_dd_stack_init: red cells through the layers first
+    float *xs = nullptr;             // a stack's layer inputs of the current position [M][B][D]
     int B = 0, D = 0, R = 0, kmin = 0, kmax = -1;
     int64_t L = 0, pos = 0;
     hipStream_t stream = nullptr;
@@ -1905,7 +1908,7 @@ constexpr int kDDMaxLog = 15;      // L <= 2^15: the widest product (L/2) is one
 constexpr int kDDFftMinDefault = 8;    // products of p <= 128 run in the per-position launch
 
 struct DDLayout {
-    size_t xh = 0, hh = 0, acc = 0, twid = 0, total = 0;
+    size_t xh = 0, hh = 0, acc = 0, twid = 0, xs = 0, total = 0;
     size_t spx[kMaxP] = {0}, sph[kMaxP] = {0};
     int kmin = 0, kmax = -1, logNT = 2;
 };
@@ -1934,8 +1937,15 @@ bool dd_layout(int B, int D, int64_t L, int fft_min, DDLayout &ly) {
     }
     ly.logNT = std::max(2, ly.kmax + 1);
     ly.twid = take((size_t(2) << ly.logNT) * sizeof(float2));
+    ly.xs = take(R * sizeof(float));
     ly.total = off;
     return true;
+}
+
+// A stack of M layers: the rows of every layer in one context (R = M B D).
+bool dd_stack_layout(int M, int B, int D, int64_t L, int fft_min, DDLayout &ly) {
+    if (M < 1 || M > kMaxLayers || (int64_t)M * B > (int64_t(1) << 24)) return false;
+    return dd_layout(M * B, D, L, fft_min, ly);
 }
 
 fi_status dd_fail(fi_dd *c, fi_status s, const std::string &msg) {
@@ -1971,6 +1981,13 @@ void dd_near_launch(fi_dd *c, int pm, int64_t n, const float *x, const float *h,
 
 fi_status dd_step(fi_dd *c, const float *x, const float *h, float *y) {
     const int64_t n = c->pos;
+    if (c->stack) {
+        // a stack: the red cells layer after layer, then every layer's products from the staged inputs
+        const int BD = c->B * c->D;
+        hipLaunchKernelGGL(fi::k_dd_chain, dim3((unsigned)((BD + 255) / 256)), dim3(256), 0, c->stream, c->q, c->M,
+                           BD, (long long)n, x, h, y, c->xs);
+        x = c->xs;
+    }
     // largest direct product of this position up to the one-launch limit (0: none)
     int64_t pm = 0;
     for (int64_t p = 1; p <= fi::kDDNearMax && p < c->q.pd && 2 * p <= n + 1 && (n + 1) % p == 0; p *= 2) pm = p;
@@ -1995,22 +2012,30 @@ size_t fi_dd_workspace_bytes(int batch, int channels, int64_t L, int fft_min_log
     return dd_layout(batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly) ? ly.total : 0;
 }
 
-fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
-                     void *stream_) {
+}  // extern "C"
+
+namespace {
+
+fi_status dd_init(fi_dd **out, bool stack, int layers, int batch, int channels, int64_t L, int fft_min_log2,
+                  void *workspace, void *stream_) {
     hipStream_t stream = (hipStream_t)stream_;
     if (!out || !workspace) return FI_EINVAL;
     *out = nullptr;
     DDLayout ly;
-    if (!dd_layout(batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly)) return FI_EINVAL;
+    if (!dd_stack_layout(layers, batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly))
+        return FI_EINVAL;
     fi_dd *c = new fi_dd();
+    c->M = layers;
+    c->stack = stack;
     c->B = batch;
     c->D = channels;
-    c->R = batch * channels;
+    c->R = layers * batch * channels;
     c->L = L;
     c->stream = stream;
     c->ws = (char *)workspace;
     c->kmin = ly.kmin;
     c->kmax = ly.kmax;
+    c->xs = (float *)(c->ws + ly.xs);
     c->q.xh = (float *)(c->ws + ly.xh);
     c->q.hh = (float *)(c->ws + ly.hh);
     c->q.acc = (float *)(c->ws + ly.acc);
@@ -2040,6 +2065,27 @@ fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_mi
     return FI_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fi_status fi_dd_init(fi_dd **out, int batch, int channels, int64_t L, int fft_min_log2, void *workspace,
+                     void *stream) {
+    return dd_init(out, false, 1, batch, channels, L, fft_min_log2, workspace, stream);
+}
+
+size_t fi_dd_stack_workspace_bytes(int layers, int batch, int channels, int64_t L, int fft_min_log2) {
+    DDLayout ly;
+    return dd_stack_layout(layers, batch, channels, L, fft_min_log2 < 0 ? kDDFftMinDefault : fft_min_log2, ly)
+               ? ly.total
+               : 0;
+}
+
+fi_status fi_dd_stack_init(fi_dd **out, int layers, int batch, int channels, int64_t L, int fft_min_log2,
+                           void *workspace, void *stream) {
+    return dd_init(out, true, layers, batch, channels, L, fft_min_log2, workspace, stream);
+}
+
 fi_status fi_dd_step(fi_dd *c, const float *x_t, const float *h_t, float *y_t) {
     if (!c || !x_t || !h_t || !y_t) return FI_EINVAL;
     if (c->poisoned) return FI_ESTATE;
@@ -2051,9 +2097,9 @@ fi_status fi_dd_run(fi_dd *c, const float *x, const float *h, int64_t steps, flo
     if (!c || steps < 0 || (steps > 0 && (!x || !h || !y))) return FI_EINVAL;
     if (c->poisoned) return FI_ESTATE;
     if (c->pos + steps > c->L) return dd_fail(c, FI_ERANGE, "run past L");
-    const size_t R = (size_t)c->R;
+    const size_t R = (size_t)c->R, BD = (size_t)c->B * c->D;
     for (int64_t i = 0; i < steps; ++i) {
-        const fi_status s = dd_step(c, x + i * R, h + i * R, y + i * R);
+        const fi_status s = dd_step(c, x + i * BD, h + i * R, y + i * R);
         if (s != FI_OK) return s;
     }
     return FI_OK;

@@ -103,6 +103,30 @@ __global__ void __launch_bounds__(256) k_dd_near(DDev q, long long n, const floa
     q.acc[base + n + 1 + j] += s;
 }
 
+// Red cells of position n for a stack of M data-dependent layers, one thread
+// per (b, c) chain through every layer (rows r = l * BD + b * D + c): layer
+// l's input x (layer 0: x0, the arriving input; layer l+1: tanh of layer l's
+// output), its arriving tap h[r], its pending sum and first input and tap.
+// Each layer's input goes to xs[r] for the position's product kernels, which
+// store x_n, h_n and form the same red cell again (the same operations on the
+// same values, so y is written twice with one value).
+static __global__ void __launch_bounds__(256) k_dd_chain(DDev q, int M, int BD, long long n,
+                                                         const float *__restrict__ x0, const float *__restrict__ h,
+                                                         float *__restrict__ y, float *__restrict__ xs) {
+    const int bc = blockIdx.x * 256 + threadIdx.x;
+    if (bc >= BD) return;
+    float x = x0[bc];
+    for (int l = 0; l < M; ++l) {
+        const int r = l * BD + bc;
+        const size_t base = (size_t)r * q.L;
+        const float hn = h[r];
+        xs[r] = x;
+        const float yl = n == 0 ? x * hn : fmaf(q.xh[base], hn, fmaf(x, q.hh[base], q.acc[base + n]));
+        y[r] = yl;
+        x = tanhf(yl);
+    }
+}
+
 // Direct products of kDDNearMax < p < pd at position n, one thread per row,
 // after k_dd_near (which stored x_n, h_n).  Both products of a band block go
 // to the same targets.

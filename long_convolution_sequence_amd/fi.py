@@ -92,6 +92,8 @@ def load_library():
         "fi_time_hyena_block": (I, [P, I, ctypes.POINTER(ctypes.c_double)]),
         "fi_dd_workspace_bytes": (S, [I, I, I64, I]),
         "fi_dd_init": (I, [ctypes.POINTER(P), I, I, I64, I, P, P]),
+        "fi_dd_stack_workspace_bytes": (S, [I, I, I, I64, I]),
+        "fi_dd_stack_init": (I, [ctypes.POINTER(P), I, I, I, I64, I, P, P]),
         "fi_dd_step": (I, [P, P, P, P]),
         "fi_dd_run": (I, [P, P, P, I64, P]),
         "fi_dd_reset": (I, [P]),
@@ -412,9 +414,11 @@ class Context:
 class DDContext:
     """Data-dependent filters: per position both the input x_t and the filter tap h_t arrive
     ([B][D] each, one layer, taps per (b, c)) and y_t = sum_{i+j=t} x_i h_j is produced.
-    Wraps the fi_dd_* calls (see include/fi.h); no CPU path."""
+    layers=M makes a stack (fi_dd_stack_*): x_t [B][D] is layer 0's input, h_t and y_t are
+    [M][B][D], and layer l+1's input is tanh(y^l_t).  Wraps the fi_dd_* calls (see
+    include/fi.h); no CPU path."""
 
-    def __init__(self, batch, channels, L, *, fft_min_log2=-1, device=None):
+    def __init__(self, batch, channels, L, *, fft_min_log2=-1, layers=None, device=None):
         import torch
         if not torch.cuda.is_available():
             raise FiError(FI_EDEVICE, "no GPU visible; the library has no CPU path")
@@ -422,14 +426,21 @@ class DDContext:
         self._torch = torch
         self.device = torch.device(device or "cuda")
         self.B, self.D, self.L = int(batch), int(channels), int(L)
-        nbytes = lib.fi_dd_workspace_bytes(self.B, self.D, self.L, int(fft_min_log2))
+        self.M = None if layers is None else int(layers)
+        if self.M is None:
+            nbytes = lib.fi_dd_workspace_bytes(self.B, self.D, self.L, int(fft_min_log2))
+        else:
+            nbytes = lib.fi_dd_stack_workspace_bytes(self.M, self.B, self.D, self.L, int(fft_min_log2))
         if nbytes == 0:
-            raise FiError(FI_EINVAL, f"unsupported shape B={batch} D={channels} L={L}")
+            raise FiError(FI_EINVAL, f"unsupported shape M={layers} B={batch} D={channels} L={L}")
         self.workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
         self.stream = torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
-        st = lib.fi_dd_init(ctypes.byref(h), self.B, self.D, self.L, int(fft_min_log2),
-                            ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_void_p(self.stream.cuda_stream))
+        ws, strm = ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_void_p(self.stream.cuda_stream)
+        if self.M is None:
+            st = lib.fi_dd_init(ctypes.byref(h), self.B, self.D, self.L, int(fft_min_log2), ws, strm)
+        else:
+            st = lib.fi_dd_stack_init(ctypes.byref(h), self.M, self.B, self.D, self.L, int(fft_min_log2), ws, strm)
         if st != FI_OK:
             raise FiError(st, "fi_dd_init failed")
         self._h = h
@@ -451,25 +462,30 @@ class DDContext:
     def position(self) -> int:
         return int(self._lib.fi_dd_position(self._h))
 
+    def _layer_shape(self):
+        return (self.B, self.D) if self.M is None else (self.M, self.B, self.D)
+
     def step(self, x, h, y=None):
-        """One position: x, h [B][D] device tensors; returns y [B][D]."""
-        y = self._torch.empty((self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
-        shp = (self.B, self.D)
+        """One position: x [B][D], h [B][D] (a stack: [M][B][D]) device tensors; returns y
+        shaped like h."""
+        ls = self._layer_shape()
+        y = self._torch.empty(ls, dtype=self._torch.float32, device=self.device) if y is None else y
         if x is None or h is None:
             raise FiError(FI_EINVAL, "x and h are required")
-        self._check(self._lib.fi_dd_step(self._h, self._p(x, shp, "x"), self._p(h, shp, "h"),
-                                         self._p(y, shp, "y")))
+        self._check(self._lib.fi_dd_step(self._h, self._p(x, (self.B, self.D), "x"), self._p(h, ls, "h"),
+                                         self._p(y, ls, "y")))
         return y
 
     def run(self, x, h, y=None):
-        """len(x) positions: x, h [T][B][D] device tensors; returns y [T][B][D]."""
+        """len(x) positions: x [T][B][D], h [T][B][D] (a stack: [T][M][B][D]) device tensors;
+        returns y shaped like h."""
         if x is None or h is None or getattr(x, "ndim", 0) != 3:
-            raise FiError(FI_EINVAL, "x and h: expected [T][B][D] device tensors")
+            raise FiError(FI_EINVAL, "x and h: expected [T][B][D] (h of a stack [T][M][B][D]) device tensors")
         T = int(x.shape[0])
-        y = self._torch.empty((T, self.B, self.D), dtype=self._torch.float32, device=self.device) if y is None else y
-        shp = (T, self.B, self.D)
-        self._check(self._lib.fi_dd_run(self._h, self._p(x, shp, "x"), self._p(h, shp, "h"), T,
-                                        self._p(y, shp, "y")))
+        hs = (T,) + self._layer_shape()
+        y = self._torch.empty(hs, dtype=self._torch.float32, device=self.device) if y is None else y
+        self._check(self._lib.fi_dd_run(self._h, self._p(x, (T, self.B, self.D), "x"), self._p(h, hs, "h"), T,
+                                        self._p(y, hs, "y")))
         return y
 
     def reset(self):

@@ -114,8 +114,8 @@ def test_null_context_calls_are_rejected(lib):
 def _dd_expected_bytes(B, D, L, kmin):
     """Workspace of a data-dependent context as the header states it: three
     [B*D][L] fp32 arrays, the two fixed-block spectra (8p bytes per row each) of
-    every FFT product size p = 2^k with k >= kmin and 2p <= L, and the twiddles
-    of the widest transform; every part 256-byte aligned."""
+    every FFT product size p = 2^k with k >= kmin and 2p <= L, the twiddles
+    of the widest transform and one [B*D] fp32 array; every part 256-byte aligned."""
     al = lambda v: (v + 255) // 256 * 256
     R = B * D
     total = 3 * al(R * L * 4)
@@ -125,7 +125,16 @@ def _dd_expected_bytes(B, D, L, kmin):
         kmax = k
         k += 1
     total += al((2 << max(2, kmax + 1)) * 8)
+    total += al(R * 4)
     return total
+
+
+@pytest.mark.parametrize("M,B,D,L,kmin", [(1, 2, 5, 1024, 3), (3, 2, 5, 4096, 8), (18, 1, 864, 16384, 8)])
+def test_dd_stack_workspace_bytes(lib, M, B, D, L, kmin):
+    """A stack of M layers holds every layer's rows: the workspace of M*B rows."""
+    assert lib.fi_dd_stack_workspace_bytes(M, B, D, L, kmin) == _dd_expected_bytes(M * B, D, L, kmin)
+    assert lib.fi_dd_stack_workspace_bytes(0, B, D, L, kmin) == 0
+    assert lib.fi_dd_stack_workspace_bytes(65, B, D, L, kmin) == 0
 
 
 @pytest.mark.parametrize("B,D,L,kmin", [(1, 1, 1, 2), (1, 4, 2, 2), (2, 5, 1024, 3), (1, 864, 16384, 2),

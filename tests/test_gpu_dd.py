@@ -126,3 +126,51 @@ def test_dd_many_rows_ragged():
     worst = _rows_worst(x, h, y)
     say(f"  worst error/tolerance {worst:.3e}")
     assert worst <= 1.0
+
+
+@pytest.mark.parametrize("fft_min", [3, 8])
+def test_dd_stack_layers_replayed_against_definition(fft_min):
+    """A stack of data-dependent layers (fi_dd_stack_*): layer 0's input and every
+    layer's taps arrive per position, layer l+1's input is tanh(y^l_t).  Each layer
+    is replayed against the definition from its realised input (layer 0: the given
+    one; layer l+1: tanh of the GPU's layer-l output, in fp32), so every layer meets
+    the teacher-forced bar; steps and run agree bit for bit, reset repeats."""
+    M, B, D, L = 3, 2, 5, 4096
+    say(f"case data-dependent stack M={M} B={B} D={D} L={L} fft_min_log2={fft_min}")
+    rng = np.random.default_rng(43)
+    x0 = rng.standard_normal((L, B, D)).astype(np.float32)
+    h = (rng.standard_normal((L, M, B, D)) * np.exp(-np.arange(L) / 600.0)[:, None, None, None]
+         / np.sqrt(60.0)).astype(np.float32)
+    xd, hd = torch.from_numpy(x0).cuda(), torch.from_numpy(h).cuda()
+    with fi.DDContext(B, D, L, fft_min_log2=fft_min, layers=M) as ctx:
+        y = ctx.run(xd, hd).cpu().numpy()                       # [L][M][B][D]
+        assert ctx.position == L
+        ctx.reset()
+        half = L // 2
+        ya = torch.stack([ctx.step(xd[t], hd[t]) for t in range(100)])
+        yb = ctx.run(xd[100:half], hd[100:half])
+        yc = ctx.run(xd[half:], hd[half:])
+        assert np.array_equal(torch.cat([ya, yb, yc]).cpu().numpy(), y)
+    worst = 0.0
+    xl = x0
+    for l in range(M):
+        w = _rows_worst(xl, np.ascontiguousarray(h[:, l]), np.ascontiguousarray(y[:, l]))
+        say(f"  layer {l}: worst error/tolerance {w:.3e}, max|y| {np.abs(y[:, l]).max():.3f}")
+        worst = max(worst, w)
+        xl = np.tanh(y[:, l]).astype(np.float32)
+    assert worst <= 1.0
+    assert np.abs(y[:, M - 1]).max() > 1e-3
+
+
+def test_dd_stack_of_one_layer_equals_single_layer():
+    """layers=1 runs the stack path (the red-cell kernel, then the products); it must
+    give the single-layer context's outputs bit for bit."""
+    B, D, L = 2, 3, 1024
+    say(f"case data-dependent stack of one layer B={B} D={D} L={L}")
+    x, h = _seq(L, B, D, 44, 200.0)
+    xd, hd = torch.from_numpy(x).cuda(), torch.from_numpy(h).cuda()
+    with fi.DDContext(B, D, L, fft_min_log2=5) as one:
+        y1 = one.run(xd, hd).cpu().numpy()
+    with fi.DDContext(B, D, L, fft_min_log2=5, layers=1) as st:
+        ys = st.run(xd, hd[:, None]).cpu().numpy()
+    assert np.array_equal(ys[:, 0], y1)
