@@ -971,8 +971,13 @@ fi_status resume_ring(fi_ctx *c) {
     return FI_OK;
 }
 
-// Before launching positions up to `upto`: join the side stream if deferred
-// sub-blocks it still computes are due by then (upto < 0: join in any case).
+// Before launching positions up to `upto` (the last position whose kernels,
+// its gray block included, the launch issues: for a chunk of positions
+// pos+1 .. pos+G that is pos+G, whose FFT block run_chunk launches too): join
+// the side stream if deferred sub-blocks it still computes are due by then
+// (upto < 0: join in any case).  The block of position side_until writes into
+// the first deferred sub-block, so it must not start before the side stream
+// is done.
 fi_status join_side(fi_ctx *c, int64_t upto) {
     if (c->side_until && (upto < 0 || upto >= c->side_until)) {
         HIPCK(c, hipStreamWaitEvent(c->stream, c->ev_side, 0));
@@ -1477,7 +1482,7 @@ fi_status fi_prefill(fi_ctx *c, const float *x, int64_t P, float *y) {
         const int64_t i = c->pos - pos0;
         if (chunk_fits(c, c->pos, end)) {
             const int64_t G = int64_t(1) << c->chunk_log;
-            if ((s = join_side(c, c->pos + G - 1)) != FI_OK) return s;
+            if ((s = join_side(c, c->pos + G)) != FI_OK) return s;
             if ((s = run_chunk(c, c->pos, x + i * BD)) != FI_OK) return s;
             if (y)
                 HIPCK(c, hipMemcpyAsync(y + i * BD, c->dev.ylast + c->pos * BD, G * BD * sizeof(float),
@@ -1513,7 +1518,7 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
                 const int64_t run = G << kb;
                 const bool split_in_run = defers(c, c->chunk_log + kb - 1);
                 if (kb && !split_in_run && (c->pos & (run - 1)) == 0 && c->pos + run <= end) {
-                    if ((s = join_side(c, c->pos + run - G - 1)) != FI_OK) return s;
+                    if ((s = join_side(c, c->pos + run - G)) != FI_OK) return s;
                     HIPCK(c, hipGraphLaunch(c->gchunks, c->stream));
                     c->pos += run - G;
                     c->ring_stale = true;
@@ -1521,14 +1526,14 @@ fi_status fi_generate(fi_ctx *c, int64_t steps, float *y) {
                 const int64_t n = c->pos + G;
                 const int q = class_of(c, n);
                 if (!defers(c, q)) {
-                    if ((s = join_side(c, n - 1)) != FI_OK) return s;
+                    if ((s = join_side(c, n)) != FI_OK) return s;
                     HIPCK(c, hipGraphLaunch(c->gchunk[q], c->stream));
                     c->pos = n;
                     c->ring_stale = true;
                     continue;
                 }
             }
-            if ((s = join_side(c, c->pos + G - 1)) != FI_OK) return s;
+            if ((s = join_side(c, c->pos + G)) != FI_OK) return s;
             if ((s = run_chunk(c, c->pos, nullptr)) != FI_OK) return s;
             c->pos += G;
             continue;
