@@ -44,9 +44,10 @@ constexpr int kChunkBlockLog = 4; // a chunk block graph spans 2^4 - 1 chunks
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Launch shape of the transform kernels of 2^logn points (FftShape on the host).
+// threads per block of the transform kernels of 2^logn points (FftShape::TPB)
 int fft_tpb(int logn) {
     const int tt = logn >= 4 ? (1 << logn) / 16 : 1;
-    return tt >= 256 ? tt : 256;
+    return tt >= 256 ? tt : (logn == 8 ? 512 : 256);
 }
 int fft_per_block(int logn) { return fft_tpb(logn) / (logn >= 4 ? (1 << logn) / 16 : 1); }
 

@@ -208,7 +208,9 @@ template <int LOGN>
 struct FftShape {
     static constexpr int N = 1 << LOGN;
     static constexpr int TT = N >= 16 ? N / 16 : 1;          // threads per transform
-    static constexpr int TPB = TT >= 256 ? TT : 256;         // threads per block
+    // threads per block: 512 for 2^8 points (32 transforms; measured 5% faster
+    // than 256 there, slower for 2^7, 2^9 and 2^10), else 256 or one transform
+    static constexpr int TPB = TT >= 256 ? TT : (LOGN == 8 ? 512 : 256);
     static constexpr int PER_BLOCK = TPB / TT;               // transforms per block
     static constexpr int R0 = LOGN < 4 ? LOGN : 4;           // stages of the outer group
     static constexpr int QLOG0 = LOGN - R0;
