@@ -47,7 +47,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // threads per block of the transform kernels of 2^logn points (FftShape::TPB)
 int fft_tpb(int logn) {
     const int tt = logn >= 4 ? (1 << logn) / 16 : 1;
-    return logn <= 7 ? 256 : logn == 8 ? 512 : (tt > 64 ? tt : 64);
+    return tt > 64 ? tt : 64;
 }
 int fft_per_block(int logn) { return fft_tpb(logn) / (logn >= 4 ? (1 << logn) / 16 : 1); }
 

@@ -208,11 +208,11 @@ template <int LOGN>
 struct FftShape {
     static constexpr int N = 1 << LOGN;
     static constexpr int TT = N >= 16 ? N / 16 : 1;          // threads per transform
-    // threads per block, as measured in the pipeline: 256 up to 2^7 points,
-    // 512 for 2^8 (32 transforms; 5% faster than 256), one transform of at
-    // least one wave from 2^9 on (2^9: 32.0 against 34.5 us with 256 threads,
-    // 2^10: 61.7 against 65.6 us)
-    static constexpr int TPB = LOGN <= 7 ? 256 : LOGN == 8 ? 512 : (TT > 64 ? TT : 64);
+    // threads per block: one wave, or one transform when that is wider.
+    // Measured in the pipeline against 256 threads: 2^7 points 10.2 against
+    // 10.7 us, 2^8 16.6 against 17.4, 2^9 32.0 against 34.5, 2^10 61.7
+    // against 65.6 us.
+    static constexpr int TPB = TT > 64 ? TT : 64;
     static constexpr int PER_BLOCK = TPB / TT;               // transforms per block
     static constexpr int R0 = LOGN < 4 ? LOGN : 4;           // stages of the outer group
     static constexpr int QLOG0 = LOGN - R0;
