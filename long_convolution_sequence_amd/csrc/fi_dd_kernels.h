@@ -213,11 +213,11 @@ k_dd_fft(Dev p, DDev q, const float4 *__restrict__ spx, const float4 *__restrict
     const float *xr = q.xh + (size_t)rr * q.L, *hr = q.hh + (size_t)rr * q.L;
     float2 va[1 << R0], vb[1 << R0];
     // x[lo, n] against the spectrum of h[p, 2p)
-    fft_block<LOGN>(p, X, lt, active, reinterpret_cast<const float2 *>(xr + lo), sph + (size_t)rr * (N / 2), va,
+    fft_block<LOGN, false>(p, X, lt, active, reinterpret_cast<const float2 *>(xr + lo), sph + (size_t)rr * (N / 2), va,
                     []() {});
     if (!square) {
         __syncthreads();  // the second transform reuses the LDS
-        fft_block<LOGN>(p, X, lt, active, reinterpret_cast<const float2 *>(hr + lo), spx + (size_t)rr * (N / 2),
+        fft_block<LOGN, false>(p, X, lt, active, reinterpret_cast<const float2 *>(hr + lo), spx + (size_t)rr * (N / 2),
                         vb, []() {});
     }
     if (!active) return;

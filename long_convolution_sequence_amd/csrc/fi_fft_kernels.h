@@ -27,7 +27,7 @@ namespace fi {
 // on zeros.  X: the team's LDS.  before_last() runs just before the last
 // inverse stage group (a caller issues its loads of the targets there, so
 // that the group's arithmetic covers their latency).
-template <int LOGN, typename BeforeLast>
+template <int LOGN, bool SPEC2 = (LOGN == 13), typename BeforeLast>
 __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool active, const float2 *xsrc,
                                           const float4 *sp, float2 (&v)[1 << FftShape<LOGN>::R0],
                                           BeforeLast &&before_last) {
@@ -44,10 +44,14 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
     // this thread's spectrum pairs, loaded late: held across the whole forward
     // transform they would cost the registers of a fourth wave per SIMD.  When
     // the last stage group is short (fewer than four stages), they are issued
-    // before it, so that it covers part of their latency.
+    // before it, so that it covers part of their latency; with SPEC2 (the
+    // gray blocks of 2^13 points, whose last group has one stage) one group
+    // earlier still, which their registers allow (569 -> 547 us for that
+    // class; slower for 2^14, and a caller that runs two blocks spills).
     constexpr int NP = S::NPASS;
     constexpr bool EARLY = NP >= 2 && LOGN - 4 * (NP - 1) < 4;
-    forward_groups<LOGN, 1, EARLY ? NP - 1 : NP>(X, lt, p.twid, p.logNT);
+    constexpr int SPL = SPEC2 && NP >= 3 ? NP - 2 : NP - 1;   // group before which they are issued
+    forward_groups<LOGN, 1, EARLY ? SPL : NP>(X, lt, p.twid, p.logNT);
     constexpr int PAIRS = (N / 2 + TT - 1) / TT;
     float4 gs[PAIRS];
 #pragma unroll
@@ -55,7 +59,7 @@ __device__ __forceinline__ void fft_block(const Dev &p, float2 *X, int lt, bool 
         const int e = lt + m * TT;
         gs[m] = (active && e < N / 2) ? sp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if constexpr (EARLY) forward_groups<LOGN, NP - 1, NP>(X, lt, p.twid, p.logNT);
+    if constexpr (EARLY) forward_groups<LOGN, SPL, NP>(X, lt, p.twid, p.logNT);
     __syncthreads();
 
     // bins of the real transform times the filter spectrum, re-packed for the
